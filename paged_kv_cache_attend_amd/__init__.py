@@ -1,0 +1,19 @@
+"""Paged KV-cache attention for AMD MI355X (gfx950).
+
+The compute lives in ``libpa.so`` (hand-written HIP kernels behind a C ABI,
+declared in ``include/pa.h``).  This package is a thin ctypes binding over
+that library (``_lib``) plus the seeded input generator used by tests and
+benchmarks (``inputs``).  The library is loaded on first use; if it has not
+been built, every entry point raises instead of falling back to any other
+implementation.
+"""
+
+_BINDING = ("PaError", "Shape", "attend", "combine", "gather_kv", "lib_path", "load",
+            "plan", "status_string", "workspace_size", "Status")
+
+
+def __getattr__(name):
+    if name in _BINDING:
+        from . import _lib
+        return getattr(_lib, name)
+    raise AttributeError(name)
