@@ -1,0 +1,170 @@
+/*
+ * pa.h -- paged KV-cache attention on AMD MI355X (gfx950), C ABI.
+ *
+ * The operation
+ * -------------
+ * New query tokens attend to their own request's keys and values, which live
+ * in a block-paged cache.  The inference-optimisation chapter ("Chapter 8:
+ * Inference optimisation", section 8.3.1, Fig. 8-10) describes the layout
+ * this follows: a sequence is cut into fixed-size logical blocks, each request
+ * keeps a block table mapping logical block i to a physical block anywhere in
+ * a shared pool, and attention recovers logical order through that table.
+ * Several tables may reference the same physical block (shared prefixes,
+ * section 8.3.2, Fig. 8-13).  Two workloads use it:
+ *   - decode: one new token per request (same chapter, sections 8.1.1 and
+ *     8.2.1), grouped-query heads, bound by HBM bandwidth;
+ *   - chunked denoising: a chunk of latent tokens attends to the KV that
+ *     earlier chunks left at the same noise level (PhysisServe teardown page,
+ *     section "why autoregressive denoising can be pipelined", the update
+ *     z_c^(d-1) = Phi_d(z_c^(d), K_<c^(d), cond_c)).
+ *
+ * For every slot r with n = ctx_lens[r] > 0 and m = q_lens[r] > 0, every new
+ * row i < m (global row q_off[r] + i, q_off = exclusive running sum of q_lens)
+ * and every query head h (KV head g = h / (num_q_heads / num_kv_heads)):
+ *     K_r[j] = k_cache[block_table[r][j / 16]][g][j % 16][:]   (j < n)
+ *     s_j    = scale * <q[row][h], K_r[j]>        over visible keys j
+ *     out[row][h] = sum_j softmax(s)_j V_r[j]      (bf16, round to nearest even)
+ *     lse[row][h] = ln sum_j exp(s_j)               (fp32, natural log)
+ * Visible keys are all j < n (full mask), or j <= n - m + i with
+ * PA_FLAG_CAUSAL.  n counts every key, including the new tokens' own K/V,
+ * which the caller has already written into their pages.
+ *
+ * Finished ("zombie") slots ride along in an in-flight batch without a result
+ * anyone reads (Photon pipelined-decoding page, section 5): a slot with
+ * ctx_lens[r] == 0 or q_lens[r] == 0 writes nothing -- its out/lse bytes are
+ * left exactly as they were.
+ *
+ * Data layout (all device memory, owned by the caller)
+ *   q, out       bf16  [total_q][num_q_heads][head_dim], rows packed by slot
+ *   k_cache,
+ *   v_cache      bf16  [num_blocks][num_kv_heads][block_size][head_dim]
+ *                      (one (block, KV head) tile = 16 x 128 x 2 B = 4 KiB)
+ *   block_table  int32 [num_seqs][max_blocks_per_seq]
+ *   ctx_lens,
+ *   q_lens       int32 [num_seqs]
+ *   lse          fp32  [total_q][num_q_heads]  (may be NULL)
+ *
+ * Conventions
+ *   - Every call only enqueues work on `stream` (a hipStream_t; NULL is the
+ *     null stream) and returns; results are ordered on that stream.  No call
+ *     allocates memory, synchronises, or reads device memory on the host, so
+ *     calls may be captured in a HIP graph (cf. the Photon page, section 3:
+ *     fixed buffers, no runtime allocation).
+ *   - The library keeps no state and is re-entrant.  The caller keeps every
+ *     buffer alive and unmodified (and does not reuse `workspace`) until the
+ *     stream has passed the call -- the "free only after the accelerator has
+ *     stopped reading" rule of section 8.3.2.
+ *   - Host-detectable errors return a status before anything is launched.
+ *     Device-side contents (table entries < num_blocks, n <= 16 *
+ *     max_blocks_per_seq, m <= n, n <= max_ctx_len, m <= max_q_len, the sum
+ *     of q_lens <= total_q) are preconditions; pa_validate checks them on the
+ *     device.  There is no retry and no fallback path.
+ */
+#ifndef PA_H_
+#define PA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pa_status {
+  PA_OK = 0,
+  PA_ERR_NULL_ARG = 1,            /* a required pointer is NULL */
+  PA_ERR_BAD_SHAPE = 2,           /* inconsistent or out-of-range sizes */
+  PA_ERR_UNSUPPORTED = 3,         /* valid but not implemented (e.g. head_dim != 128) */
+  PA_ERR_WORKSPACE_TOO_SMALL = 4, /* workspace_bytes < pa_workspace_size() */
+  PA_ERR_LAUNCH = 5               /* the HIP runtime rejected a kernel launch */
+} pa_status;
+
+/* Request rows may only see keys up to their own position (chunked prefill,
+ * speculative verification).  Without it every row sees all n keys. */
+#define PA_FLAG_CAUSAL 0x1u
+
+/* Host-known sizes of one call.  The maxima are upper bounds the caller's
+ * scheduler already knows; they size the launch grid without a device read. */
+typedef struct pa_shape {
+  int32_t num_seqs;           /* slots (rows of block_table, ctx_lens, q_lens) */
+  int32_t total_q;            /* rows of q / out / lse */
+  int32_t num_q_heads;        /* Hq, a multiple of num_kv_heads */
+  int32_t num_kv_heads;       /* Hkv */
+  int32_t head_dim;           /* must be 128 */
+  int32_t block_size;         /* tokens per block; must be 16 */
+  int32_t max_blocks_per_seq; /* columns of block_table */
+  int32_t max_q_len;          /* >= every q_lens[r]; 1 selects the decode path */
+  int32_t max_ctx_len;        /* >= every ctx_lens[r] */
+  int32_t partition_size;     /* split-KV partition in tokens: 0 = automatic,
+                                 otherwise a positive multiple of block_size */
+  int64_t num_blocks;         /* physical blocks in each of k_cache / v_cache */
+  uint32_t flags;             /* PA_FLAG_* */
+  uint32_t reserved;          /* must be 0 */
+} pa_shape;
+
+/* Bytes of scratch pa_attend needs for this shape: split-KV partials
+ * (normalised fp32 output and fp32 LSE per partition and row).  0 when the
+ * call needs none.  Returns 0 for a shape pa_attend would reject. */
+size_t pa_workspace_size(const pa_shape* shape);
+
+/* Number of split-KV partitions pa_attend will use for this shape (1 = no
+ * split, or the path that does not split); 0 for an invalid shape. */
+int32_t pa_num_partitions(const pa_shape* shape);
+
+/* Attention of the new rows against the paged cache, as defined above.
+ * `workspace` may be NULL when pa_workspace_size() is 0.  `lse` may be NULL.
+ * q and out must not overlap.  Errors: PA_ERR_NULL_ARG, PA_ERR_BAD_SHAPE,
+ * PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE_TOO_SMALL (nothing launched), or
+ * PA_ERR_LAUNCH. */
+pa_status pa_attend(const pa_shape* shape, const void* q, const void* k_cache,
+                    const void* v_cache, const int32_t* block_table,
+                    const int32_t* ctx_lens, const int32_t* q_lens, float scale,
+                    void* out, float* lse, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
+/* Merge split-KV partials by their log-sum-exp weights.  For each row:
+ *   M = max_p lse_p,  w_p = exp(lse_p - M),
+ *   lse = M + ln sum_p w_p,  out = sum_p w_p o_p / sum_p w_p  (bf16, RNE).
+ * Partials with lse_p = -inf weigh zero and their outputs are never read; a
+ * row whose partials are all -inf is left untouched (out and lse unchanged).
+ *   partial_out  fp32 [num_partials][rows][head_dim] (each o_p normalised)
+ *   partial_lse  fp32 [num_partials][rows]
+ *   out          bf16 [rows][head_dim]
+ *   lse          fp32 [rows] (may be NULL)
+ * head_dim must be a positive multiple of 4, at most 1024.  Exported for
+ * callers that produce partials themselves (context-parallel shards, or a
+ * shared-prefix pass merged with per-request suffixes). */
+pa_status pa_combine(int32_t num_partials, int32_t rows, int32_t head_dim,
+                     const float* partial_out, const float* partial_lse,
+                     void* out, float* lse, void* stream);
+
+/* Copy every active slot's cached K (or V) rows into a dense buffer through
+ * the same page addressing the attention kernels use:
+ *   dst[r][j][g][:] = cache[block_table[r][j / 16]][g][j % 16][:]  for j < n
+ * dst is bf16 [num_seqs][max_ctx_len][num_kv_heads][head_dim]; rows j >= n
+ * (and all rows of slots with n == 0) are left untouched.  For checking the
+ * gather bit for bit. */
+pa_status pa_gather_kv(const pa_shape* shape, const void* cache,
+                       const int32_t* block_table, const int32_t* ctx_lens,
+                       void* dst, void* stream);
+
+/* Check the device-side preconditions of pa_attend for this shape and data.
+ * Writes a bit mask to *error_word (device int32, caller-owned): 0 if all
+ * hold, else PA_BAD_* bits below.  Enqueued on `stream`; read the word after
+ * the stream passes. */
+#define PA_BAD_BLOCK_ID 0x1   /* a table entry in [0, ceil(n/16)) outside [0, num_blocks) */
+#define PA_BAD_CTX_LEN 0x2    /* n < 0, n > max_ctx_len or n > 16 * max_blocks_per_seq */
+#define PA_BAD_Q_LEN 0x4      /* m < 0, m > max_q_len, or m > n while n > 0 */
+#define PA_BAD_TOTAL_Q 0x8    /* sum of q_lens exceeds total_q */
+pa_status pa_validate(const pa_shape* shape, const int32_t* block_table,
+                      const int32_t* ctx_lens, const int32_t* q_lens,
+                      int32_t* error_word, void* stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char* pa_status_string(pa_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H_ */

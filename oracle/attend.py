@@ -59,7 +59,8 @@ def bf16_bits_to_f64(bits) -> np.ndarray:
     which float64 then represents exactly.
     """
     b = np.asarray(bits, dtype=np.uint16)
-    return (b.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    with np.errstate(invalid="ignore"):  # NaN payloads widen to NaN
+        return (b.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
 
 
 def gather_request_kv(cache_bits, table_row, n: int, kv_head: int, block_size: int = 16) -> np.ndarray:

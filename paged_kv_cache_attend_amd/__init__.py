@@ -8,8 +8,9 @@ been built, every entry point raises instead of falling back to any other
 implementation.
 """
 
-_BINDING = ("PaError", "Shape", "attend", "combine", "gather_kv", "lib_path", "load",
-            "plan", "status_string", "workspace_size", "Status")
+_BINDING = ("PaError", "Shape", "Status", "attend", "combine", "gather_kv", "validate",
+            "lib_path", "load", "make_shape", "plan", "status_string", "workspace_size",
+            "EXPORTS")
 
 
 def __getattr__(name):

@@ -1,0 +1,253 @@
+"""ctypes binding over libpa.so, with the names of the C ABI in include/pa.h.
+
+Argument marshalling only: tensors are checked for dtype, device, layout and
+size, then their device pointers and the current HIP stream are passed to the
+library.  Every step of the computation runs in the library's HIP kernels.
+If libpa.so has not been built, loading raises -- there is no other path.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import enum
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(PKG, "libpa.so")
+_lib = None
+
+PA_FLAG_CAUSAL = 0x1
+PA_BAD_BLOCK_ID = 0x1
+PA_BAD_CTX_LEN = 0x2
+PA_BAD_Q_LEN = 0x4
+PA_BAD_TOTAL_Q = 0x8
+
+EXPORTS = ("pa_workspace_size", "pa_num_partitions", "pa_attend", "pa_combine",
+           "pa_gather_kv", "pa_validate", "pa_status_string")
+
+
+class Status(enum.IntEnum):
+    OK = 0
+    ERR_NULL_ARG = 1
+    ERR_BAD_SHAPE = 2
+    ERR_UNSUPPORTED = 3
+    ERR_WORKSPACE_TOO_SMALL = 4
+    ERR_LAUNCH = 5
+
+
+class PaError(RuntimeError):
+    def __init__(self, status, where: str = ""):
+        self.status = Status(status) if status in Status._value2member_map_ else status
+        msg = status_string(status) if _lib is not None else str(status)
+        super().__init__(f"{where}: {msg} ({self.status!r})" if where else msg)
+
+
+class Shape(ctypes.Structure):
+    """Mirror of ``pa_shape``."""
+
+    _fields_ = [
+        ("num_seqs", ctypes.c_int32),
+        ("total_q", ctypes.c_int32),
+        ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("max_blocks_per_seq", ctypes.c_int32),
+        ("max_q_len", ctypes.c_int32),
+        ("max_ctx_len", ctypes.c_int32),
+        ("partition_size", ctypes.c_int32),
+        ("num_blocks", ctypes.c_int64),
+        ("flags", ctypes.c_uint32),
+        ("reserved", ctypes.c_uint32),
+    ]
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def load():
+    """Load libpa.so (once).  Raises PaError-compatible RuntimeError if absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"libpa.so not built at {_LIB_PATH}; run paged_kv_cache_attend_amd.build")
+    lib = ctypes.CDLL(_LIB_PATH)
+    P = ctypes.c_void_p
+    shp = ctypes.POINTER(Shape)
+    lib.pa_workspace_size.argtypes = [shp]
+    lib.pa_workspace_size.restype = ctypes.c_size_t
+    lib.pa_num_partitions.argtypes = [shp]
+    lib.pa_num_partitions.restype = ctypes.c_int32
+    lib.pa_attend.argtypes = [shp, P, P, P, P, P, P, ctypes.c_float, P, P, P, ctypes.c_size_t, P]
+    lib.pa_attend.restype = ctypes.c_int
+    lib.pa_combine.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P, P, P, P, P]
+    lib.pa_combine.restype = ctypes.c_int
+    lib.pa_gather_kv.argtypes = [shp, P, P, P, P, P]
+    lib.pa_gather_kv.restype = ctypes.c_int
+    lib.pa_validate.argtypes = [shp, P, P, P, P, P]
+    lib.pa_validate.restype = ctypes.c_int
+    lib.pa_status_string.argtypes = [ctypes.c_int]
+    lib.pa_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().pa_status_string(int(status)).decode()
+
+
+def _check(status: int, where: str):
+    if status != Status.OK:
+        raise PaError(status, where)
+
+
+def make_shape(num_seqs, total_q, num_q_heads, num_kv_heads, max_blocks_per_seq, max_q_len,
+               max_ctx_len, num_blocks, partition_size=0, causal=False, head_dim=128,
+               block_size=16, flags=None) -> Shape:
+    f = (PA_FLAG_CAUSAL if causal else 0) if flags is None else flags
+    return Shape(int(num_seqs), int(total_q), int(num_q_heads), int(num_kv_heads), int(head_dim),
+                 int(block_size), int(max_blocks_per_seq), int(max_q_len), int(max_ctx_len),
+                 int(partition_size), int(num_blocks), int(f), 0)
+
+
+def workspace_size(shape: Shape) -> int:
+    return int(load().pa_workspace_size(ctypes.byref(shape)))
+
+
+def plan(shape: Shape):
+    """(workspace bytes, number of split-KV partitions) for a shape."""
+    lib = load()
+    return int(lib.pa_workspace_size(ctypes.byref(shape))), int(lib.pa_num_partitions(ctypes.byref(shape)))
+
+
+# ---------------------------------------------------------------------------
+# torch-tensor wrappers
+# ---------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream_handle(device, stream):
+    torch = _torch()
+    s = torch.cuda.current_stream(device) if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _need(t, name, dtype, device, ndim=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+
+
+def attend(q, k_cache, v_cache, block_table, ctx_lens, q_lens, scale, out, lse=None, *,
+           max_q_len: int, max_ctx_len: int, partition_size: int = 0, causal: bool = False,
+           workspace=None, stream=None):
+    """``pa_attend`` on torch tensors (all on one GPU).
+
+    q, out: bf16 [total_q, Hq, 128]; k_cache, v_cache: bf16 [num_blocks, Hkv, 16, 128];
+    block_table: int32 [num_seqs, max_blocks]; ctx_lens, q_lens: int32 [num_seqs];
+    lse: fp32 [total_q, Hq] or None.  ``max_q_len`` / ``max_ctx_len`` are the
+    caller's known upper bounds (no device read happens here).  If the shape
+    needs a workspace and none is given, one is allocated with torch.
+    """
+    torch = _torch()
+    dev = q.device
+    _need(q, "q", torch.bfloat16, dev, 3)
+    _need(out, "out", torch.bfloat16, dev, 3)
+    _need(k_cache, "k_cache", torch.bfloat16, dev, 4)
+    _need(v_cache, "v_cache", torch.bfloat16, dev, 4)
+    _need(block_table, "block_table", torch.int32, dev, 2)
+    _need(ctx_lens, "ctx_lens", torch.int32, dev, 1)
+    _need(q_lens, "q_lens", torch.int32, dev, 1)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, dev, 2)
+    total_q, hq, d = q.shape
+    nb, hkv, bs, d2 = k_cache.shape
+    if tuple(out.shape) != tuple(q.shape) or tuple(v_cache.shape) != tuple(k_cache.shape) or d2 != d:
+        raise ValueError("shape mismatch between q/out or k_cache/v_cache")
+    if lse is not None and tuple(lse.shape) != (total_q, hq):
+        raise ValueError("lse must be [total_q, Hq]")
+    num_seqs = block_table.shape[0]
+    if ctx_lens.shape[0] != num_seqs or q_lens.shape[0] != num_seqs:
+        raise ValueError("ctx_lens / q_lens must have one entry per block-table row")
+    shape = make_shape(num_seqs, total_q, hq, hkv, block_table.shape[1], max_q_len, max_ctx_len,
+                       nb, partition_size, causal, head_dim=d, block_size=bs)
+    need = workspace_size(shape)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = load().pa_attend(ctypes.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+                          _ptr(ctx_lens), _ptr(q_lens), ctypes.c_float(float(scale)), _ptr(out), _ptr(lse),
+                          _ptr(workspace), ctypes.c_size_t(ws_bytes), _stream_handle(dev, stream))
+    _check(st, "pa_attend")
+    return out, lse
+
+
+def combine(partial_out, partial_lse, out, lse=None, *, stream=None):
+    """``pa_combine``: partial_out fp32 [P, rows, D], partial_lse fp32 [P, rows],
+    out bf16 [rows, D], lse fp32 [rows] or None."""
+    torch = _torch()
+    dev = partial_out.device
+    _need(partial_out, "partial_out", torch.float32, dev, 3)
+    _need(partial_lse, "partial_lse", torch.float32, dev, 2)
+    _need(out, "out", torch.bfloat16, dev, 2)
+    P, rows, D = partial_out.shape
+    if tuple(partial_lse.shape) != (P, rows) or tuple(out.shape) != (rows, D):
+        raise ValueError("shape mismatch")
+    if lse is not None:
+        _need(lse, "lse", torch.float32, dev, 1)
+    st = load().pa_combine(P, rows, D, _ptr(partial_out), _ptr(partial_lse), _ptr(out), _ptr(lse),
+                           _stream_handle(dev, stream))
+    _check(st, "pa_combine")
+    return out, lse
+
+
+def gather_kv(cache, block_table, ctx_lens, dst, *, max_ctx_len: int, stream=None):
+    """``pa_gather_kv``: dst bf16 [num_seqs, max_ctx_len, Hkv, 128]."""
+    torch = _torch()
+    dev = cache.device
+    _need(cache, "cache", torch.bfloat16, dev, 4)
+    _need(block_table, "block_table", torch.int32, dev, 2)
+    _need(ctx_lens, "ctx_lens", torch.int32, dev, 1)
+    _need(dst, "dst", torch.bfloat16, dev, 4)
+    nb, hkv, bs, d = cache.shape
+    num_seqs = block_table.shape[0]
+    if tuple(dst.shape) != (num_seqs, max_ctx_len, hkv, d):
+        raise ValueError("dst must be [num_seqs, max_ctx_len, Hkv, D]")
+    shape = make_shape(num_seqs, 1, hkv, hkv, block_table.shape[1], 1, max_ctx_len, nb,
+                       head_dim=d, block_size=bs)
+    st = load().pa_gather_kv(ctypes.byref(shape), _ptr(cache), _ptr(block_table), _ptr(ctx_lens),
+                             _ptr(dst), _stream_handle(dev, stream))
+    _check(st, "pa_gather_kv")
+    return dst
+
+
+def validate(block_table, ctx_lens, q_lens, error_word, *, num_blocks: int, total_q: int,
+             max_q_len: int, max_ctx_len: int, num_q_heads: int = 1, num_kv_heads: int = 1,
+             stream=None):
+    """``pa_validate``: writes the PA_BAD_* mask into error_word (int32 [1])."""
+    torch = _torch()
+    dev = block_table.device
+    _need(error_word, "error_word", torch.int32, dev, 1)
+    shape = make_shape(block_table.shape[0], total_q, num_q_heads, num_kv_heads, block_table.shape[1],
+                       max_q_len, max_ctx_len, num_blocks)
+    st = load().pa_validate(ctypes.byref(shape), _ptr(block_table), _ptr(ctx_lens), _ptr(q_lens),
+                            _ptr(error_word), _stream_handle(dev, stream))
+    _check(st, "pa_validate")
+    return error_word

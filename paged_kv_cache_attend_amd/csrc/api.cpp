@@ -1,0 +1,270 @@
+// api.cpp -- the C ABI of libpa.so: argument checks, launch planning, launches.
+//
+// Host-side only.  Nothing here reads device memory, allocates, or waits on
+// the stream, so every entry point can be captured in a HIP graph (fixed
+// buffers and no runtime allocation, as the Photon pipelined-decoding page
+// requires of its decode slots, section 3).  Errors that the host can detect
+// are returned before anything is launched; there is no fallback path.
+
+#include <hip/hip_runtime_api.h>
+
+#include <climits>
+#include <cmath>
+
+#include "launch.h"
+#include "pa.h"
+
+namespace {
+
+using namespace pa;
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+struct Plan {
+  bool empty = true;      // nothing to launch
+  bool decode = false;    // split-KV decode path, else chunk path
+  int group = 1;          // query heads per KV head
+  int part_pages = 0;     // pages per partition (decode)
+  int num_parts = 1;      // partitions (decode)
+  size_t rows = 0;        // total_q * num_q_heads
+  size_t ws_bytes = 0;    // workspace bytes
+  size_t part_out_bytes = 0;
+  unsigned grid = 0;
+};
+
+int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+pa_status check_shape(const pa_shape* s) {
+  if (!s) return PA_ERR_NULL_ARG;
+  if (s->reserved != 0) return PA_ERR_BAD_SHAPE;
+  if (s->num_seqs < 0 || s->total_q < 0 || s->num_q_heads <= 0 || s->num_kv_heads <= 0 ||
+      s->head_dim <= 0 || s->block_size <= 0 || s->max_blocks_per_seq <= 0 ||
+      s->max_q_len < 0 || s->max_ctx_len < 0 || s->partition_size < 0 || s->num_blocks < 0)
+    return PA_ERR_BAD_SHAPE;
+  if (s->num_q_heads % s->num_kv_heads != 0) return PA_ERR_BAD_SHAPE;
+  if (s->head_dim != kHeadDim || s->block_size != kBlockSize) return PA_ERR_UNSUPPORTED;
+  if (s->partition_size % kBlockSize != 0) return PA_ERR_BAD_SHAPE;
+  if ((long long)s->max_ctx_len > (long long)kBlockSize * s->max_blocks_per_seq) return PA_ERR_BAD_SHAPE;
+  if (s->max_q_len > s->total_q && s->num_seqs > 0) return PA_ERR_BAD_SHAPE;
+  if (s->num_blocks == 0 && s->max_ctx_len > 0) return PA_ERR_BAD_SHAPE;
+  if (s->flags & ~PA_FLAG_CAUSAL) return PA_ERR_UNSUPPORTED;
+  // Index arithmetic limits: rows and grid sizes must fit 32-bit counters.
+  const long long rows = (long long)s->total_q * s->num_q_heads;
+  if (rows > INT_MAX / 2) return PA_ERR_UNSUPPORTED;
+  if ((long long)s->num_seqs * s->max_blocks_per_seq > (long long)INT_MAX) return PA_ERR_UNSUPPORTED;
+  return PA_OK;
+}
+
+// Partition size when the caller leaves it to the library.  Decode moves
+// 8 KiB per page and KV head; a partition must be long enough to amortise its
+// prologue and epilogue (at least two pages per wave) and short enough that
+// the grid covers the 256 CUs with a few resident workgroups each.
+int auto_part_pages(const pa_shape* s, int max_pages) {
+  const long long pairs = (long long)s->num_seqs * s->num_kv_heads;
+  const long long target_wgs = 4LL * kNumCUs;
+  long long parts = (target_wgs + pairs - 1) / pairs;
+  if (parts < 1) parts = 1;
+  int pp = ceil_div(max_pages, (int)(parts > max_pages ? max_pages : parts));
+  if (pp < 8) pp = 8;
+  return pp;
+}
+
+pa_status make_plan(const pa_shape* s, Plan* plan) {
+  const pa_status st = check_shape(s);
+  if (st != PA_OK) return st;
+  Plan p;
+  p.group = s->num_q_heads / s->num_kv_heads;
+  p.rows = (size_t)s->total_q * (size_t)s->num_q_heads;
+  if (s->num_seqs == 0 || s->total_q == 0 || s->max_q_len == 0 || s->max_ctx_len == 0) {
+    *plan = p;  // nothing can be written
+    return PA_OK;
+  }
+  p.empty = false;
+  p.decode = (s->max_q_len == 1) && decode_supports_group(p.group);
+  if (p.decode) {
+    const int max_pages = ceil_div(s->max_ctx_len, kBlockSize);
+    p.part_pages = s->partition_size > 0 ? s->partition_size / kBlockSize : auto_part_pages(s, max_pages);
+    p.num_parts = ceil_div(max_pages, p.part_pages);
+    const long long grid = (long long)s->num_kv_heads * s->num_seqs * p.num_parts;
+    if (grid > INT_MAX) return PA_ERR_UNSUPPORTED;
+    p.grid = (unsigned)grid;
+    if (p.num_parts > 1) {
+      p.part_out_bytes = (size_t)p.num_parts * p.rows * kHeadDim * sizeof(float);
+      p.ws_bytes = p.part_out_bytes + (size_t)p.num_parts * p.rows * sizeof(float);
+    }
+  } else {
+    const int q_tiles = ceil_div(s->max_q_len, kChunkRows);
+    const long long grid = (long long)s->num_seqs * s->num_q_heads * q_tiles;
+    if (grid > INT_MAX) return PA_ERR_UNSUPPORTED;
+    p.grid = (unsigned)grid;
+  }
+  *plan = p;
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t pa_workspace_size(const pa_shape* shape) {
+  Plan p;
+  if (make_plan(shape, &p) != PA_OK) return 0;
+  return p.ws_bytes;
+}
+
+int32_t pa_num_partitions(const pa_shape* shape) {
+  Plan p;
+  if (make_plan(shape, &p) != PA_OK) return 0;
+  return p.decode ? p.num_parts : 1;
+}
+
+pa_status pa_attend(const pa_shape* shape, const void* q, const void* k_cache,
+                    const void* v_cache, const int32_t* block_table,
+                    const int32_t* ctx_lens, const int32_t* q_lens, float scale,
+                    void* out, float* lse, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+  Plan plan;
+  const pa_status st = make_plan(shape, &plan);
+  if (st != PA_OK) return st;
+  if (!std::isfinite(scale)) return PA_ERR_BAD_SHAPE;
+  if (plan.empty) return PA_OK;
+  if (!q || !k_cache || !v_cache || !block_table || !ctx_lens || !q_lens || !out)
+    return PA_ERR_NULL_ARG;
+  if (plan.ws_bytes > 0) {
+    if (!workspace) return PA_ERR_NULL_ARG;
+    if (workspace_bytes < plan.ws_bytes) return PA_ERR_WORKSPACE_TOO_SMALL;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const float scale_log2 = scale * kLog2e;
+
+  if (plan.decode) {
+    DecodeParams d;
+    d.q = static_cast<const uint16_t*>(q);
+    d.k = static_cast<const uint16_t*>(k_cache);
+    d.v = static_cast<const uint16_t*>(v_cache);
+    d.block_table = block_table;
+    d.ctx_lens = ctx_lens;
+    d.q_lens = q_lens;
+    d.out = static_cast<uint16_t*>(out);
+    d.lse = lse;
+    d.part_out = plan.num_parts > 1 ? static_cast<float*>(workspace) : nullptr;
+    d.part_lse = plan.num_parts > 1
+                     ? reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.part_out_bytes)
+                     : nullptr;
+    d.scale_log2 = scale_log2;
+    d.num_seqs = shape->num_seqs;
+    d.num_q_heads = shape->num_q_heads;
+    d.num_kv_heads = shape->num_kv_heads;
+    d.max_blocks = shape->max_blocks_per_seq;
+    d.total_q = shape->total_q;
+    d.part_pages = plan.part_pages;
+    d.num_parts = plan.num_parts;
+    if (launch_decode(d, plan.group, plan.grid, s) != hipSuccess) return PA_ERR_LAUNCH;
+    if (plan.num_parts > 1) {
+      CombineParams c;
+      c.part_out = d.part_out;
+      c.part_lse = d.part_lse;
+      c.out = d.out;
+      c.lse = lse;
+      c.num_parts = plan.num_parts;
+      c.rows = (int32_t)plan.rows;
+      c.head_dim = kHeadDim;
+      if (launch_combine(c, s) != hipSuccess) return PA_ERR_LAUNCH;
+    }
+    return PA_OK;
+  }
+
+  ChunkParams c;
+  c.q = static_cast<const uint16_t*>(q);
+  c.k = static_cast<const uint16_t*>(k_cache);
+  c.v = static_cast<const uint16_t*>(v_cache);
+  c.block_table = block_table;
+  c.ctx_lens = ctx_lens;
+  c.q_lens = q_lens;
+  c.out = static_cast<uint16_t*>(out);
+  c.lse = lse;
+  c.scale_log2 = scale_log2;
+  c.num_seqs = shape->num_seqs;
+  c.num_q_heads = shape->num_q_heads;
+  c.num_kv_heads = shape->num_kv_heads;
+  c.max_blocks = shape->max_blocks_per_seq;
+  c.q_tiles = ceil_div(shape->max_q_len, kChunkRows);
+  c.causal = (shape->flags & PA_FLAG_CAUSAL) ? 1 : 0;
+  if (launch_chunk(c, plan.grid, s) != hipSuccess) return PA_ERR_LAUNCH;
+  return PA_OK;
+}
+
+pa_status pa_combine(int32_t num_partials, int32_t rows, int32_t head_dim,
+                     const float* partial_out, const float* partial_lse, void* out,
+                     float* lse, void* stream) {
+  if (num_partials <= 0 || rows < 0 || head_dim <= 0 || head_dim % 4 != 0 || head_dim > 1024)
+    return PA_ERR_BAD_SHAPE;
+  if ((long long)rows * head_dim * num_partials > (long long)1 << 40) return PA_ERR_UNSUPPORTED;
+  if (rows == 0) return PA_OK;
+  if (!partial_out || !partial_lse || !out) return PA_ERR_NULL_ARG;
+  CombineParams c;
+  c.part_out = partial_out;
+  c.part_lse = partial_lse;
+  c.out = static_cast<uint16_t*>(out);
+  c.lse = lse;
+  c.num_parts = num_partials;
+  c.rows = rows;
+  c.head_dim = head_dim;
+  if (launch_combine(c, static_cast<hipStream_t>(stream)) != hipSuccess) return PA_ERR_LAUNCH;
+  return PA_OK;
+}
+
+pa_status pa_gather_kv(const pa_shape* shape, const void* cache, const int32_t* block_table,
+                       const int32_t* ctx_lens, void* dst, void* stream) {
+  const pa_status st = check_shape(shape);
+  if (st != PA_OK) return st;
+  if (shape->num_seqs == 0 || shape->max_ctx_len == 0) return PA_OK;
+  if (!cache || !block_table || !ctx_lens || !dst) return PA_ERR_NULL_ARG;
+  GatherParams g;
+  g.cache = static_cast<const uint16_t*>(cache);
+  g.block_table = block_table;
+  g.ctx_lens = ctx_lens;
+  g.dst = static_cast<uint16_t*>(dst);
+  g.num_seqs = shape->num_seqs;
+  g.num_kv_heads = shape->num_kv_heads;
+  g.max_blocks = shape->max_blocks_per_seq;
+  g.max_ctx = shape->max_ctx_len;
+  g.max_pages = ceil_div(shape->max_ctx_len, kBlockSize);
+  if (launch_gather(g, static_cast<hipStream_t>(stream)) != hipSuccess) return PA_ERR_LAUNCH;
+  return PA_OK;
+}
+
+pa_status pa_validate(const pa_shape* shape, const int32_t* block_table, const int32_t* ctx_lens,
+                      const int32_t* q_lens, int32_t* error_word, void* stream) {
+  const pa_status st = check_shape(shape);
+  if (st != PA_OK) return st;
+  if (!error_word) return PA_ERR_NULL_ARG;
+  if (shape->num_seqs > 0 && (!block_table || !ctx_lens || !q_lens)) return PA_ERR_NULL_ARG;
+  ValidateParams v;
+  v.block_table = block_table;
+  v.ctx_lens = ctx_lens;
+  v.q_lens = q_lens;
+  v.error_word = error_word;
+  v.num_blocks = shape->num_blocks;
+  v.num_seqs = shape->num_seqs;
+  v.max_blocks = shape->max_blocks_per_seq;
+  v.max_ctx = shape->max_ctx_len;
+  v.max_q = shape->max_q_len;
+  v.total_q = shape->total_q;
+  if (launch_validate(v, static_cast<hipStream_t>(stream)) != hipSuccess) return PA_ERR_LAUNCH;
+  return PA_OK;
+}
+
+const char* pa_status_string(pa_status status) {
+  switch (status) {
+    case PA_OK: return "ok";
+    case PA_ERR_NULL_ARG: return "a required pointer is NULL";
+    case PA_ERR_BAD_SHAPE: return "inconsistent or out-of-range sizes";
+    case PA_ERR_UNSUPPORTED: return "valid but unsupported configuration";
+    case PA_ERR_WORKSPACE_TOO_SMALL: return "workspace smaller than pa_workspace_size()";
+    case PA_ERR_LAUNCH: return "kernel launch failed";
+  }
+  return "unknown status";
+}
+
+}  // extern "C"

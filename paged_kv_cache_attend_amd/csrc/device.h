@@ -1,0 +1,123 @@
+// device.h -- small device helpers shared by the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "launch.h"
+
+namespace pa {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+// ---------------------------------------------------------------------------
+// Page addressing.  Logical key j of a slot lives in logical block j / 16 at
+// slot j % 16; the block table names the physical block.  One (physical
+// block, KV head) tile is 16 x 128 bf16 = 4 KiB, contiguous.  Every kernel
+// that touches the cache goes through these two functions.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ size_t tile_index(int32_t phys, int g, int num_kv_heads) {
+  return (size_t)phys * (size_t)num_kv_heads + (size_t)g;
+}
+// Element offset of (phys, g, slot, dim) in a cache pool.
+__device__ __forceinline__ size_t cache_offset(int32_t phys, int g, int slot, int dim,
+                                               int num_kv_heads) {
+  return (tile_index(phys, g, num_kv_heads) * kBlockSize + (size_t)slot) * kHeadDim + (size_t)dim;
+}
+
+// ---------------------------------------------------------------------------
+// Work distribution over the 8 XCDs.  Workgroups are handed to XCDs round
+// robin (id % 8); this maps hardware id -> logical id so that each XCD gets a
+// contiguous range of logical ids, i.e. neighbouring work (same KV head,
+// same shared pages) runs under one L2.  A bijection for any grid size.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
+  const int q = nblocks / kNumXCDs;
+  const int r = nblocks % kNumXCDs;
+  const int x = bid % kNumXCDs;
+  const int k = bid / kNumXCDs;
+  return x * q + (x < r ? x : r) + k;
+}
+
+// ---------------------------------------------------------------------------
+// bf16 <-> fp32.  Widening is exact (bf16 is the top half of binary32);
+// narrowing uses the hardware convert, round to nearest even.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  bf16x2_t v;
+  v[0] = (__bf16)a;
+  v[1] = (__bf16)b;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// fp32 += two bf16 products (v_dot2c_f32_bf16): products of bf16 are exact
+// in fp32, accumulation is fp32.
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+__device__ __forceinline__ float dot8_bf16(const uint4& a, const uint4& b, float c) {
+  c = dot2_bf16(a.x, b.x, c);
+  c = dot2_bf16(a.y, b.y, c);
+  c = dot2_bf16(a.z, b.z, c);
+  c = dot2_bf16(a.w, b.w, c);
+  return c;
+}
+
+// ---------------------------------------------------------------------------
+// Cross-lane reductions inside one 16-lane DPP row.  row_ror:n rotates the
+// row by n lanes, so after rotations by 8, 4, 2, 1 every lane of the row
+// holds the reduction of all 16.
+// ---------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float row16_max(float x) {
+  x = fmaxf(x, dpp_f32<0x128>(x));
+  x = fmaxf(x, dpp_f32<0x124>(x));
+  x = fmaxf(x, dpp_f32<0x122>(x));
+  x = fmaxf(x, dpp_f32<0x121>(x));
+  return x;
+}
+__device__ __forceinline__ float row16_sum(float x) {
+  x += dpp_f32<0x128>(x);
+  x += dpp_f32<0x124>(x);
+  x += dpp_f32<0x122>(x);
+  x += dpp_f32<0x121>(x);
+  return x;
+}
+
+// Sum over the whole 64-lane wave (result in every lane).
+__device__ __forceinline__ int wave_sum_i32(int x) {
+  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
+  return x;
+}
+
+// Row of slot `seq`'s first new token: sum of q_lens[0 .. seq).
+__device__ __forceinline__ int q_row_offset(const int32_t* q_lens, int seq, int lane) {
+  int s = 0;
+  for (int i = lane; i < seq; i += 64) s += q_lens[i];
+  return wave_sum_i32(s);
+}
+
+// Orders LDS traffic between the lanes of one wave: LDS operations of a wave
+// execute in program order, this keeps the compiler from moving them.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+constexpr float kLn2 = 0.69314718055994530942f;
+
+}  // namespace pa

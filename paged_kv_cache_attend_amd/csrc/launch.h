@@ -1,0 +1,104 @@
+// launch.h -- internal interface between the C-ABI front end (api.cpp) and the
+// HIP kernels.  Host-only types: nothing here is visible outside libpa.so.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pa {
+
+constexpr int kHeadDim = 128;    // only head size built
+constexpr int kBlockSize = 16;   // tokens per KV block
+constexpr int kNumCUs = 256;     // MI355X compute units (8 XCDs x 32)
+constexpr int kNumXCDs = 8;
+
+// Split-KV decode: one workgroup per (KV head, slot, partition).
+struct DecodeParams {
+  const uint16_t* q;          // bf16 [total_q][Hq][128]
+  const uint16_t* k;          // bf16 [num_blocks][Hkv][16][128]
+  const uint16_t* v;
+  const int32_t* block_table; // [num_seqs][max_blocks]
+  const int32_t* ctx_lens;
+  const int32_t* q_lens;
+  uint16_t* out;              // bf16 [total_q][Hq][128]      (num_parts == 1)
+  float* lse;                 // fp32 [total_q][Hq] or null   (num_parts == 1)
+  float* part_out;            // fp32 [num_parts][total_q*Hq][128] (num_parts > 1)
+  float* part_lse;            // fp32 [num_parts][total_q*Hq]
+  float scale_log2;           // softmax scale * log2(e)
+  int32_t num_seqs;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t max_blocks;
+  int32_t total_q;
+  int32_t part_pages;         // 16-token pages per partition
+  int32_t num_parts;
+};
+
+// Chunk path (several new rows per slot): bf16 MFMA for S = QK^T and O = PV.
+struct ChunkParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const int32_t* block_table;
+  const int32_t* ctx_lens;
+  const int32_t* q_lens;
+  uint16_t* out;
+  float* lse;
+  float scale_log2;
+  int32_t num_seqs;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t max_blocks;
+  int32_t q_tiles;            // ceil(max_q_len / rows per workgroup)
+  int32_t causal;
+};
+
+struct CombineParams {
+  const float* part_out;      // [P][rows][D]
+  const float* part_lse;      // [P][rows]
+  uint16_t* out;              // bf16 [rows][D]
+  float* lse;                 // [rows] or null
+  int32_t num_parts;
+  int32_t rows;
+  int32_t head_dim;
+};
+
+struct GatherParams {
+  const uint16_t* cache;
+  const int32_t* block_table;
+  const int32_t* ctx_lens;
+  uint16_t* dst;              // [num_seqs][max_ctx][Hkv][128]
+  int32_t num_seqs;
+  int32_t num_kv_heads;
+  int32_t max_blocks;
+  int32_t max_ctx;
+  int32_t max_pages;
+};
+
+struct ValidateParams {
+  const int32_t* block_table;
+  const int32_t* ctx_lens;
+  const int32_t* q_lens;
+  int32_t* error_word;
+  int64_t num_blocks;
+  int32_t num_seqs;
+  int32_t max_blocks;
+  int32_t max_ctx;
+  int32_t max_q;
+  int32_t total_q;
+};
+
+// Decode kernels exist for these query-per-KV head group sizes.
+bool decode_supports_group(int group);
+constexpr int kDecodeThreads = 256;
+hipError_t launch_decode(const DecodeParams& p, int group, unsigned grid, hipStream_t s);
+
+constexpr int kChunkRows = 128;  // query rows per chunk workgroup
+hipError_t launch_chunk(const ChunkParams& p, unsigned grid, hipStream_t s);
+
+hipError_t launch_combine(const CombineParams& p, hipStream_t s);
+hipError_t launch_gather(const GatherParams& p, hipStream_t s);
+hipError_t launch_validate(const ValidateParams& p, hipStream_t s);
+
+}  // namespace pa

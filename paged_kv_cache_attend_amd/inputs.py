@@ -341,3 +341,47 @@ def relocate(problem: PagedProblem, layer: int, seed: int):
     v2[perm] = v
     table2 = perm[problem.block_table]
     return q, table2, k2, v2
+
+
+# ---------------------------------------------------------------------------
+# Host-side precondition check and upload (harness plumbing).
+# ---------------------------------------------------------------------------
+
+def check_preconditions(problem: PagedProblem, table=None) -> None:
+    """Raise if the problem breaks a device-side precondition of pa_attend
+    (so that no kernel is ever launched on out-of-range data)."""
+    t = problem.block_table if table is None else np.asarray(table)
+    bs = problem.block_size
+    if (problem.ctx_lens < 0).any() or (problem.q_lens < 0).any():
+        raise ValueError("negative length")
+    if int(problem.ctx_lens.max(initial=0)) > bs * t.shape[1]:
+        raise ValueError("ctx_len beyond the block table")
+    if int(problem.q_lens.sum()) != problem.total_q:
+        raise ValueError("q_lens do not sum to total_q")
+    live = (problem.ctx_lens > 0)
+    if ((problem.q_lens > problem.ctx_lens) & live).any():
+        raise ValueError("more new rows than keys")
+    for r in np.nonzero(live)[0]:
+        ids = t[r, :_blocks(int(problem.ctx_lens[r]), bs)]
+        if (ids < 0).any() or (ids >= problem.num_blocks).any():
+            raise ValueError(f"slot {r}: block id outside the pool")
+
+
+def bits_to_torch_bf16(bits: np.ndarray, device):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(device)
+
+
+def to_device(problem: PagedProblem, q, k, v, device, table=None):
+    """Upload one layer's arrays plus the shared index arrays as torch tensors."""
+    import torch
+    check_preconditions(problem, table)
+    t = problem.block_table if table is None else table
+    return dict(
+        q=bits_to_torch_bf16(q, device),
+        k=bits_to_torch_bf16(k, device),
+        v=bits_to_torch_bf16(v, device),
+        block_table=torch.from_numpy(np.ascontiguousarray(t, dtype=np.int32)).to(device),
+        ctx_lens=torch.from_numpy(problem.ctx_lens.astype(np.int32)).to(device),
+        q_lens=torch.from_numpy(problem.q_lens.astype(np.int32)).to(device),
+    )

@@ -1,0 +1,177 @@
+"""C-ABI checks that need no GPU: the library loads, exports what include/pa.h
+declares, and rejects bad arguments on the host before launching anything."""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import re
+import subprocess
+
+import pytest
+
+import paged_kv_cache_attend_amd as pk
+from paged_kv_cache_attend_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pa.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.lib_path()):
+        from paged_kv_cache_attend_amd import build
+        build.build()
+    return pk.load()
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pa_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_names():
+    assert _declared() == sorted(_lib.EXPORTS)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.lib_path()], capture_output=True, text=True,
+                         check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for name in _declared():
+        assert name in exported, name
+        assert getattr(lib, name) is not None
+
+
+def test_shape_struct_layout():
+    # int32 x 10, int64, uint32 x 2 -> 10*4 + 8 + 8 = 56 bytes, int64 at offset 40
+    assert ctypes.sizeof(pk.Shape) == 56
+    assert pk.Shape.num_blocks.offset == 40
+
+
+def _shape(**kw):
+    base = dict(num_seqs=4, total_q=4, num_q_heads=32, num_kv_heads=8, max_blocks_per_seq=10,
+                max_q_len=1, max_ctx_len=160, num_blocks=64)
+    base.update(kw)
+    return pk.make_shape(**base)
+
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every case below fails on the host
+
+
+def _attend(lib, shape, scale=0.088, ws=None, ws_bytes=0, q=FAKE, out=FAKE, null_shape=False):
+    sp = None if null_shape else ctypes.byref(shape)
+    return lib.pa_attend(sp, q, FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.c_float(scale), out, None, ws,
+                         ctypes.c_size_t(ws_bytes), None)
+
+
+def test_status_strings(lib):
+    for s in pk.Status:
+        assert pk.status_string(s)
+    assert pk.status_string(99) == "unknown status"
+
+
+@pytest.mark.parametrize("kw,expected", [
+    (dict(num_q_heads=30), pk.Status.ERR_BAD_SHAPE),       # not a multiple of Hkv
+    (dict(head_dim=64), pk.Status.ERR_UNSUPPORTED),
+    (dict(block_size=32), pk.Status.ERR_UNSUPPORTED),
+    (dict(partition_size=24), pk.Status.ERR_BAD_SHAPE),    # not whole blocks
+    (dict(partition_size=-16), pk.Status.ERR_BAD_SHAPE),
+    (dict(max_ctx_len=161), pk.Status.ERR_BAD_SHAPE),      # beyond 16 * max_blocks
+    (dict(num_seqs=-1), pk.Status.ERR_BAD_SHAPE),
+    (dict(num_kv_heads=0), pk.Status.ERR_BAD_SHAPE),
+    (dict(max_q_len=5), pk.Status.ERR_BAD_SHAPE),          # above total_q
+    (dict(num_blocks=0), pk.Status.ERR_BAD_SHAPE),
+    (dict(flags=0x100), pk.Status.ERR_UNSUPPORTED),
+])
+def test_bad_shapes_rejected(lib, kw, expected):
+    s = _shape(**kw)
+    assert _attend(lib, s) == expected
+    assert lib.pa_workspace_size(ctypes.byref(s)) == 0
+    assert lib.pa_num_partitions(ctypes.byref(s)) == 0
+
+
+def test_reserved_field_must_be_zero(lib):
+    s = _shape()
+    s.reserved = 1
+    assert _attend(lib, s) == pk.Status.ERR_BAD_SHAPE
+
+
+def test_null_arguments(lib):
+    s = _shape()
+    assert _attend(lib, s, null_shape=True) == pk.Status.ERR_NULL_ARG
+    assert _attend(lib, s, q=None) == pk.Status.ERR_NULL_ARG
+    assert _attend(lib, s, out=None) == pk.Status.ERR_NULL_ARG
+
+
+def test_non_finite_scale(lib):
+    s = _shape()
+    assert _attend(lib, s, scale=math.nan) == pk.Status.ERR_BAD_SHAPE
+    assert _attend(lib, s, scale=math.inf) == pk.Status.ERR_BAD_SHAPE
+
+
+def test_workspace_checks(lib):
+    s = _shape(num_seqs=68, total_q=68, max_blocks_per_seq=528, max_ctx_len=8447, num_blocks=20000,
+               partition_size=512)
+    need, parts = pk.plan(s)
+    assert parts == 17
+    rows = 68 * 32
+    assert need == parts * rows * (128 + 1) * 4 == 19_087_872
+    assert _attend(lib, s, ws=None, ws_bytes=0) == pk.Status.ERR_NULL_ARG
+    assert _attend(lib, s, ws=FAKE, ws_bytes=need - 1) == pk.Status.ERR_WORKSPACE_TOO_SMALL
+
+
+def test_single_partition_needs_no_workspace(lib):
+    s = _shape(partition_size=160)
+    assert pk.plan(s) == (0, 1)
+
+
+def test_auto_partitions_cover_the_chip(lib):
+    # 16 slots x 8 KV heads x 2303 keys: the automatic split must give the
+    # decode grid several workgroups per CU.
+    s = _shape(num_seqs=16, total_q=16, max_blocks_per_seq=144, max_ctx_len=2303, num_blocks=2592)
+    ws, parts = pk.plan(s)
+    assert parts > 1 and 16 * 8 * parts >= 512
+    assert ws == parts * 16 * 32 * 129 * 4
+
+
+def test_chunk_path_needs_no_workspace(lib):
+    s = _shape(num_seqs=4, total_q=1024, num_q_heads=24, num_kv_heads=24, max_blocks_per_seq=64,
+               max_q_len=256, max_ctx_len=1024, num_blocks=288)
+    assert pk.plan(s) == (0, 1)
+
+
+def test_empty_batches_launch_nothing(lib):
+    # nothing to write: returns OK without touching the (fake) pointers
+    for kw in (dict(num_seqs=0), dict(total_q=0, max_q_len=0), dict(max_ctx_len=0), dict(max_q_len=0)):
+        s = _shape(**kw)
+        assert _attend(lib, s) == pk.Status.OK, kw
+
+
+def test_combine_argument_checks(lib):
+    f = lib.pa_combine
+    assert f(0, 4, 128, FAKE, FAKE, FAKE, None, None) == pk.Status.ERR_BAD_SHAPE
+    assert f(2, -1, 128, FAKE, FAKE, FAKE, None, None) == pk.Status.ERR_BAD_SHAPE
+    assert f(2, 4, 126, FAKE, FAKE, FAKE, None, None) == pk.Status.ERR_BAD_SHAPE
+    assert f(2, 4, 2048, FAKE, FAKE, FAKE, None, None) == pk.Status.ERR_BAD_SHAPE
+    assert f(2, 4, 128, None, FAKE, FAKE, None, None) == pk.Status.ERR_NULL_ARG
+    assert f(2, 4, 128, FAKE, FAKE, None, None, None) == pk.Status.ERR_NULL_ARG
+    assert f(2, 0, 128, None, None, None, None, None) == pk.Status.OK
+
+
+def test_gather_and_validate_argument_checks(lib):
+    s = _shape()
+    assert lib.pa_gather_kv(ctypes.byref(s), None, FAKE, FAKE, FAKE, None) == pk.Status.ERR_NULL_ARG
+    assert lib.pa_gather_kv(None, FAKE, FAKE, FAKE, FAKE, None) == pk.Status.ERR_NULL_ARG
+    assert lib.pa_validate(ctypes.byref(s), FAKE, FAKE, FAKE, None, None) == pk.Status.ERR_NULL_ARG
+    bad = _shape(head_dim=96)
+    assert lib.pa_gather_kv(ctypes.byref(bad), FAKE, FAKE, FAKE, FAKE, None) == pk.Status.ERR_UNSUPPORTED
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(_lib, "_lib", None)
+    monkeypatch.setattr(_lib, "_LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        _lib.load()

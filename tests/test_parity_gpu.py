@@ -1,0 +1,248 @@
+"""GPU parity: the HIP path (through the C ABI) against the FP64 oracle.
+
+Tolerances: output max |d| <= 1e-2, mean |d| <= 1e-3, LSE max |d| <= 1e-3 on
+every written row; rows of inactive slots keep their sentinel bytes exactly.
+Bit-exact checks: page gather, page placement, shared-versus-copied prefix,
+single-key output, repeat determinism.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_attend_amd as pk
+from paged_kv_cache_attend_amd import inputs
+
+from gpu_util import DEV, LSE_SENTINEL, OUT_SENTINEL, bf16_to_f64, compare, run_gpu, run_oracle, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(ctx, ql=None, hq=8, hkv=2, seed=3, **kw):
+    ql = [1] * len(ctx) if ql is None else ql
+    return inputs.make_problem("case", seed, ctx, ql, hq, hkv, **kw)
+
+
+# ---------------------------------------------------------------------------
+# decode path
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("ps", [0, 16, 32, 64, 112])
+def test_tiny_decode(ps):
+    p = inputs.tiny_decode()
+    say(f"tiny_decode partition_size={ps}")
+    compare(p, run_gpu(p, partition_size=ps), run_oracle(p), label=f"tiny ps={ps}")
+
+
+def test_fig_8_10_and_worked_example():
+    for p in (inputs.fig_8_10_case(), inputs.worked_example_9_13_5_15()):
+        say(p.name)
+        compare(p, run_gpu(p), run_oracle(p), label=p.name)
+
+
+@pytest.mark.parametrize("hq,hkv", [(8, 2), (32, 8), (4, 4), (8, 4), (2, 1)])
+@pytest.mark.parametrize("ps", [0, 16, 64, 4096])
+def test_decode_ragged_lengths(hq, hkv, ps):
+    ctx = [1, 2, 15, 16, 17, 31, 32, 33, 100, 257, 1000, 1023, 1024, 1025, 3001]
+    p = _case(ctx, hq=hq, hkv=hkv, seed=hq * 31 + hkv)
+    say(f"decode ragged hq={hq} hkv={hkv} ps={ps}")
+    compare(p, run_gpu(p, partition_size=ps), run_oracle(p), label=f"ragged {hq}/{hkv} ps={ps}")
+
+
+@pytest.mark.parametrize("ps", [0, 32, 4096])
+def test_zombies_and_empty_slots_untouched(ps):
+    # zombies keep a query row (q_len 1, ctx_len 0); q_len 0 slots own no row
+    p = _case([0, 37, 0, 100, 5, 0, 64], ql=[1, 1, 1, 1, 0, 0, 1], seed=17)
+    say(f"zombies ps={ps}")
+    ref = run_oracle(p)
+    assert ref[2].tolist() == [False, True, False, True, True]
+    compare(p, run_gpu(p, partition_size=ps), ref, label=f"zombies ps={ps}")
+
+
+def test_all_zombies_write_nothing():
+    p = _case([0, 0, 0], seed=19)
+    p.ctx_lens[:] = 0
+    ob, lb = run_gpu(p, partition_size=32)
+    assert (ob == OUT_SENTINEL).all() and (lb.view(np.uint32) == LSE_SENTINEL).all()
+
+
+def test_single_key_is_bit_exact():
+    p = _case([1, 1, 1], hq=32, hkv=8, seed=23)
+    q, k, v = p.layer(0)
+    ob, lb = run_gpu(p, q=q, k=k, v=v)
+    for r in range(3):
+        phys = p.block_table[r, 0]
+        for h in range(32):
+            assert np.array_equal(ob[r, h], v[phys, h // 4, 0]), (r, h)
+
+
+def test_page_placement_is_bit_exact():
+    p = _case([37, 100, 300, 1000, 5], hq=32, hkv=8, seed=29)
+    base = run_gpu(p, partition_size=64)
+    for seed in (1, 2):
+        q, table2, k2, v2 = inputs.relocate(p, 0, seed)
+        other = run_gpu(p, q=q, k=k2, v=v2, table=table2, partition_size=64)
+        assert np.array_equal(base[0], other[0])
+        assert np.array_equal(base[1].view(np.uint32), other[1].view(np.uint32))
+
+
+def test_shared_prefix_equals_private_copies_bit_exact():
+    p = _case([600, 700, 512, 800], hq=32, hkv=8, seed=31, shared_prefix_tokens=512)
+    q, k, v = p.layer(0)
+    a = run_gpu(p, q=q, k=k, v=v, partition_size=128)
+    # give slots 1..3 their own copies of the 32 shared blocks
+    extra = 3 * 32
+    k2 = np.concatenate([k, np.zeros((extra,) + k.shape[1:], k.dtype)])
+    v2 = np.concatenate([v, np.zeros((extra,) + v.shape[1:], v.dtype)])
+    table = p.block_table.copy()
+    nxt = p.num_blocks
+    for r in (1, 2, 3):
+        for j in range(32):
+            k2[nxt] = k[table[r, j]]
+            v2[nxt] = v[table[r, j]]
+            table[r, j] = nxt
+            nxt += 1
+    p2 = inputs.with_block_table(p, table, np.zeros(nxt, np.int32), num_blocks=nxt)
+    b = run_gpu(p2, q=q, k=k2, v=v2, table=table, partition_size=128)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1].view(np.uint32), b[1].view(np.uint32))
+
+
+def test_repeat_calls_are_deterministic():
+    p = _case([2303] * 4, hq=32, hkv=8, seed=37)
+    q, k, v = p.layer(0)
+    a = run_gpu(p, q=q, k=k, v=v)
+    b = run_gpu(p, q=q, k=k, v=v, repeats=3)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1].view(np.uint32), b[1].view(np.uint32))
+
+
+def test_lse_optional():
+    p = _case([37, 100], seed=41)
+    ob, lb = run_gpu(p, with_lse=False, partition_size=32)
+    assert lb is None
+    compare(p, (ob, None), run_oracle(p), label="no lse")
+
+
+# ---------------------------------------------------------------------------
+# the reference workloads at full size (sampled layers)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("layer", [0, 35])
+def test_qwen3_short_decode_full_size(layer):
+    p = inputs.qwen3_short_decode(num_layers=36)
+    say(f"qwen3 short decode layer {layer}")
+    compare(p, run_gpu(p, layer), run_oracle(p, layer), label=f"cfg2 layer {layer}")
+
+
+def test_qwen3_shared_prefix_decode_full_size():
+    p = inputs.qwen3_shared_prefix_decode(num_layers=36)
+    say("qwen3 shared-prefix decode layer 7")
+    compare(p, run_gpu(p, 7), run_oracle(p, 7), label="cfg3 layer 7")
+
+
+def test_ragged_mixed_decode_full_size():
+    p = inputs.ragged_mixed_decode()
+    say("ragged mixed decode")
+    assert pk.plan(pk.make_shape(p.num_seqs, p.total_q, 32, 8, 528, 1, p.max_ctx_len, p.num_blocks,
+                                 partition_size=512))[1] == -(-p.max_ctx_len // 512)
+    compare(p, run_gpu(p), run_oracle(p), label="cfg4")
+
+
+def test_chunked_denoise_full_size():
+    p = inputs.chunked_denoise()
+    say("chunked denoise")
+    compare(p, run_gpu(p), run_oracle(p), label="cfg5")
+
+
+# ---------------------------------------------------------------------------
+# chunk (MFMA) path
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("ctx,ql,hq,hkv", [
+    ([64, 40], [8, 3], 4, 4),
+    ([20, 50, 31], [20, 7, 1], 6, 2),
+    ([300, 1024, 17], [129, 256, 17], 24, 24),
+    ([1000, 77], [200, 2], 32, 8),
+    ([33, 0, 65], [2, 1, 65], 8, 8),
+])
+@pytest.mark.parametrize("causal", [False, True])
+def test_chunk_path(ctx, ql, hq, hkv, causal):
+    p = _case(ctx, ql, hq=hq, hkv=hkv, seed=sum(ctx) + hq, causal=causal)
+    say(f"chunk ctx={ctx} ql={ql} {hq}/{hkv} causal={causal}")
+    compare(p, run_gpu(p), run_oracle(p), label=f"chunk {ctx} {ql} causal={causal}")
+
+
+def test_chunk_path_handles_group_sizes_without_decode_kernel():
+    # 8 query heads per KV head with one row each takes the MFMA path
+    p = _case([37, 100, 1000], hq=64, hkv=8, seed=43)
+    compare(p, run_gpu(p), run_oracle(p), label="G=8 decode via chunk path")
+
+
+# ---------------------------------------------------------------------------
+# gather, combine, validate
+# ---------------------------------------------------------------------------
+
+def test_gather_is_bit_exact():
+    p = _case([37, 100, 0, 16, 1000], hq=8, hkv=2, seed=47)
+    q, k, v = p.layer(0)
+    t = inputs.to_device(p, q, k, v, DEV)
+    dst = torch.full((p.num_seqs, p.max_ctx_len, 2, 128), 0x1234, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+    pk.gather_kv(t["k"], t["block_table"], t["ctx_lens"], dst, max_ctx_len=p.max_ctx_len)
+    torch.cuda.synchronize()
+    got = dst.view(torch.int16).cpu().numpy().view(np.uint16)
+    for r in range(p.num_seqs):
+        n = int(p.ctx_lens[r])
+        j = np.arange(n)
+        expect = k[p.block_table[r][j // 16], :, j % 16, :]  # [n][Hkv][D]
+        assert np.array_equal(got[r, :n], expect)
+        assert (got[r, n:] == 0x1234).all()
+
+
+def test_combine_matches_oracle_merge():
+    rng = np.random.default_rng(53)
+    P, rows, D = 7, 300, 128
+    po = rng.standard_normal((P, rows, D)).astype(np.float32)
+    pl = (rng.standard_normal((P, rows)) * 4).astype(np.float32)
+    dead = rng.random((P, rows)) < 0.3
+    pl[dead] = -np.inf
+    po[dead] = np.nan
+    pl[:, 5] = -np.inf   # a row with no live partial stays untouched
+    po[:, 5] = np.nan
+    out = torch.full((rows, D), OUT_SENTINEL, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+    lse = torch.full((rows,), LSE_SENTINEL, dtype=torch.int32, device=DEV).view(torch.float32)
+    pk.combine(torch.from_numpy(po).to(DEV), torch.from_numpy(pl).to(DEV), out, lse)
+    torch.cuda.synchronize()
+    ref_o, ref_l, touched = oracle.combine_fp64(po, pl)
+    ob = out.view(torch.int16).cpu().numpy().view(np.uint16)
+    lb = lse.cpu().numpy()
+    o = bf16_to_f64(ob)
+    assert not touched[5] and (ob[5] == OUT_SENTINEL).all() and lb[5:6].view(np.uint32)[0] == LSE_SENTINEL
+    assert np.abs(o[touched] - ref_o[touched]).max() <= 2e-2
+    assert np.abs(lb[touched] - ref_l[touched]).max() <= 1e-4
+
+
+def test_validate_flags_bad_data():
+    p = _case([37, 100, 0], ql=[1, 1, 1], seed=59)
+    bt = torch.from_numpy(p.block_table).to(DEV)
+    cl = torch.from_numpy(p.ctx_lens).to(DEV)
+    ql = torch.from_numpy(p.q_lens).to(DEV)
+    word = torch.full((1,), -1, dtype=torch.int32, device=DEV)
+
+    def check(bt_, cl_, ql_, **kw):
+        args = dict(num_blocks=p.num_blocks, total_q=3, max_q_len=1, max_ctx_len=100)
+        args.update(kw)
+        pk.validate(bt_, cl_, ql_, word, **args)
+        torch.cuda.synchronize()
+        return int(word.item())
+
+    assert check(bt, cl, ql) == 0
+    bad = bt.clone()
+    bad[1, 3] = p.num_blocks
+    assert check(bad, cl, ql) == pk._lib.PA_BAD_BLOCK_ID
+    assert check(bt, cl, ql, max_ctx_len=99) == pk._lib.PA_BAD_CTX_LEN
+    assert check(bt, cl, ql, total_q=2) == pk._lib.PA_BAD_TOTAL_Q
+    ql2 = ql.clone()
+    ql2[0] = 40
+    assert check(bt, cl, ql2, max_q_len=64, total_q=64) == pk._lib.PA_BAD_Q_LEN
