@@ -1,0 +1,310 @@
+#!/usr/bin/env python3
+"""Paged KV-cache attention benchmark on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME]
+
+A step is one pass of the hot path over one batch: for the decode workloads,
+``pa_attend`` on every layer in turn (each layer has its own K/V pool, so the
+pass streams all layers' KV from HBM; a single layer would fit the 256 MB
+Infinity Cache), for the chunk workload one ``pa_attend`` call.  Inputs are
+seeded synthetic N(0, 1) bf16 values with the shapes of the named workload,
+uploaded before timing.  Prints ONE JSON line.
+
+Default workload: 36 layers x 16 slots x 2303 keys, 32 query / 8 KV heads of
+128 (the Qwen3-8B-shaped decode batch), split-KV with an automatic partition.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
+METRIC = "paged decode attention KV-read GB/s (% of HBM peak) + chunk-attn TFLOP/s"
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="qwen3_8b_short_decode")
+    ap.add_argument("--partition-size", type=int, default=None,
+                    help="split-KV partition in tokens (default: the workload's own, 0 = automatic)")
+    ap.add_argument("--launch", choices=["graph", "eager"], default="graph")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-chunk", action="store_true", help="skip the secondary chunk-path measurement")
+    ap.add_argument("--cpu-budget-s", type=float, default=25.0)
+    return ap.parse_args()
+
+
+def build_decode(problem, dev, want_oracle: bool, cpu_budget_s: float):
+    """Upload every layer; run the oracle on layers while the CPU budget lasts."""
+    import torch
+    from paged_kv_cache_attend_amd import inputs
+    layers = []
+    ref = {}
+    cpu_time = 0.0
+    cpu_bytes = 0
+    if want_oracle:
+        import oracle
+        from threadpoolctl import threadpool_limits
+    for l in range(problem.num_layers):
+        q, k, v = problem.layer(l)
+        t = inputs.to_device(problem, q, k, v, dev)
+        layers.append(t)
+        if want_oracle and cpu_time < cpu_budget_s:
+            with threadpool_limits(1):
+                t0 = time.perf_counter()
+                ref[l] = oracle.attend_fp64(q, k, v, problem.block_table, problem.ctx_lens, problem.q_lens,
+                                            problem.scale, problem.num_kv_heads, problem.block_size,
+                                            causal=problem.causal)
+                cpu_time += time.perf_counter() - t0
+            cpu_bytes += problem.kv_bytes_read()
+        del q, k, v
+        if l % 6 == 5 or l == problem.num_layers - 1:
+            log(f"uploaded {l + 1}/{problem.num_layers} layers; oracle {len(ref)} layers in {cpu_time:.1f}s")
+    torch.cuda.synchronize()
+    return layers, ref, cpu_time, cpu_bytes
+
+
+def prepare_calls(problem, layers, partition_size):
+    import torch
+    import paged_kv_cache_attend_amd as pk
+    calls, outs, lses = [], [], []
+    workspace = None
+    for t in layers:
+        out = torch.empty_like(t["q"])
+        lse = torch.empty(t["q"].shape[:2], dtype=torch.float32, device=t["q"].device)
+        c = pk.PreparedAttend(t["q"], t["k"], t["v"], t["block_table"], t["ctx_lens"], t["q_lens"],
+                              float(problem.scale), out, lse, max_q_len=problem.max_q_len,
+                              max_ctx_len=problem.max_ctx_len, partition_size=partition_size,
+                              causal=problem.causal, workspace=workspace)
+        workspace = c.workspace  # one workspace serves every layer (stream-ordered)
+        calls.append(c)
+        outs.append(out)
+        lses.append(lse)
+    return calls, outs, lses
+
+
+def time_pass(calls, steps, warmup, launch):
+    """Time `steps` passes; returns (ms per pass from events, wall ms per pass)."""
+    import torch
+    stream = torch.cuda.current_stream()
+
+    def one_pass():
+        for c in calls:
+            c.launch(stream)
+
+    graph = None
+    if launch == "graph":
+        one_pass()  # make sure everything is loaded before capture
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            one_pass()
+        run = graph.replay
+    else:
+        run = one_pass
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(steps):
+        run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    return e0.elapsed_time(e1) / steps, wall, graph
+
+
+def time_kernel_launches(calls, reps):
+    """Average duration of one pa_attend call (all of its launches), measured
+    with HIP events on the launch stream around `reps` back-to-back passes."""
+    import torch
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps):
+        for c in calls:
+            c.launch(stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / (reps * len(calls))
+
+
+def parity(problem, outs, lses, ref):
+    import torch
+    import oracle
+    emax = emean = lmax = 0.0
+    n = 0
+    for l, (o_ref, l_ref, written) in ref.items():
+        ob = outs[l].view(torch.int16).cpu().numpy().view(np.uint16)
+        lb = lses[l].cpu().numpy().astype(np.float64)
+        o = oracle.bf16_bits_to_f64(ob)
+        err = np.abs(o[written] - o_ref[written])
+        emax = max(emax, float(err.max()))
+        emean = max(emean, float(err.mean()))
+        lmax = max(lmax, float(np.abs(lb[written] - l_ref[written]).max()))
+        n += 1
+    return {"layers_checked": n, "max_abs_out": emax, "mean_abs_out": emean, "max_abs_lse": lmax,
+            "pass": bool(emax <= 1e-2 and emean <= 1e-3 and lmax <= 1e-3)}
+
+
+def chunk_secondary(dev, steps):
+    """TFLOP/s of the chunked-denoising workload (4 x 24 heads x 256 rows x 1024 keys)."""
+    import torch
+    import paged_kv_cache_attend_amd as pk
+    from paged_kv_cache_attend_amd import inputs
+    p = inputs.chunked_denoise()
+    q, k, v = p.layer(0)
+    sets = []
+    for _ in range(16):  # 16 resident copies (~1 GB) so a rotation misses the Infinity Cache
+        t = inputs.to_device(p, q, k, v, dev)
+        out = torch.empty_like(t["q"])
+        lse = torch.empty(t["q"].shape[:2], dtype=torch.float32, device=dev)
+        sets.append(pk.PreparedAttend(t["q"], t["k"], t["v"], t["block_table"], t["ctx_lens"], t["q_lens"],
+                                      float(p.scale), out, lse, max_q_len=p.max_q_len,
+                                      max_ctx_len=p.max_ctx_len))
+    flops = 4 * int((p.q_lens.astype(np.int64) * p.ctx_lens).sum()) * p.num_q_heads * p.head_dim
+    reps = max(steps, 50)
+    cold_ms, _, _ = time_pass(sets, reps // 16 + 1, 2, "graph")
+    cold_ms /= len(sets)
+    warm_ms, _, _ = time_pass(sets[:1] * 16, reps // 16 + 1, 2, "graph")
+    warm_ms /= 16
+    return {"workload": "chunked_denoise", "flop_per_call": flops,
+            "tflops_cold": flops / (cold_ms * 1e-3) / 1e12, "tflops_warm": flops / (warm_ms * 1e-3) / 1e12,
+            "ms_cold": cold_ms, "ms_warm": warm_ms,
+            "frac_of_bf16_peak_warm": flops / (warm_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU (asked for {args.gpus}); multi-GPU runs are not part "
+              "of this build", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from paged_kv_cache_attend_amd import inputs
+    import paged_kv_cache_attend_amd as pk
+    pk.load()  # fail loudly if the HIP library is missing
+    dev = torch.device("cuda:0")
+    # All work runs on one non-default stream (graph capture needs one).
+    torch.cuda.set_stream(torch.cuda.Stream(device=dev))
+    if args.config not in inputs.CONFIGS or args.config in ("tiny_decode",):
+        raise SystemExit(f"unknown or untimeable config {args.config}")
+    problem = inputs.CONFIGS[args.config]()
+    ps = problem.partition_size if args.partition_size is None else args.partition_size
+    log(f"config {problem.name}: {problem.num_layers} layers, {problem.num_seqs} slots, "
+        f"Hq {problem.num_q_heads} / Hkv {problem.num_kv_heads}, max ctx {problem.max_ctx_len}")
+
+    t_setup = time.perf_counter()
+    layers, ref, cpu_s, cpu_bytes = build_decode(problem, dev, not args.no_cpu_baseline, args.cpu_budget_s)
+    calls, outs, lses = prepare_calls(problem, layers, ps)
+    log(f"setup {time.perf_counter() - t_setup:.1f}s; partitions per slot {calls[0].num_partitions}")
+
+    decode = problem.max_q_len == 1
+    ms, wall_ms, _ = time_pass(calls, args.steps, args.warmup, args.launch)
+    eager_ms = None
+    if args.launch == "graph":
+        eager_ms, _, _ = time_pass(calls, max(10, args.steps // 4), 2, "eager")
+    per_call_ms = time_kernel_launches(calls, max(5, args.steps // 10))
+
+    kv_read = problem.kv_bytes_read() * problem.num_layers
+    kv_unique = problem.kv_bytes_unique() * problem.num_layers
+    flops = 4 * int((problem.q_lens.astype(np.int64) * problem.ctx_lens).sum()) * problem.num_q_heads \
+        * problem.head_dim * problem.num_layers
+    if decode:
+        headline_bytes = kv_unique  # each distinct byte read once (equals kv_read without sharing)
+        value = headline_bytes / (ms * 1e-3) / 1e9
+        unit = "GB/s"
+        per_launch_bytes = headline_bytes / len(calls)
+        achieved = per_launch_bytes / (per_call_ms * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                    "kernel": "pa_attend (split-KV decode + LSE combine) per layer",
+                    "avg_launch_us": per_call_ms * 1e3}
+    else:
+        value = flops / (ms * 1e-3) / 1e12
+        unit = "TFLOP/s"
+        achieved = (flops / len(calls)) / (per_call_ms * 1e-3) / 1e12
+        roofline = {"bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": achieved / BF16_PEAK_TFLOPS, "traffic": None, "kernel": "chunk_kernel",
+                    "avg_launch_us": per_call_ms * 1e3}
+
+    par = parity(problem, outs, lses, ref) if ref else None
+    cpu = None
+    if ref and cpu_s > 0:
+        ncores = 1
+        if decode:
+            cpu = {"value": cpu_bytes / cpu_s / 1e9, "unit": "GB/s", "cores": ncores, "kind": "oracle",
+                   "sample": f"{len(ref)} of {problem.num_layers} layers, all {problem.num_seqs} slots, "
+                             f"FP64 NumPy oracle, 1 BLAS thread, {cpu_s:.1f}s"}
+        else:
+            cpu = {"value": flops / problem.num_layers * len(ref) / cpu_s / 1e12, "unit": "TFLOP/s",
+                   "cores": ncores, "kind": "oracle", "sample": f"{len(ref)} call(s), 1 BLAS thread, {cpu_s:.1f}s"}
+        cpu["cpu_model"] = platform.processor() or platform.machine()
+
+    secondary = None
+    if decode and not args.no_chunk:
+        secondary = chunk_secondary(dev, args.steps)
+
+    line = {
+        "metric": METRIC,
+        "value": value,
+        "unit": unit,
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": problem.name,
+            "layers": problem.num_layers,
+            "batch": problem.num_seqs,
+            "ctx_len_max": problem.max_ctx_len,
+            "q_heads": problem.num_q_heads,
+            "kv_heads": problem.num_kv_heads,
+            "head_dim": problem.head_dim,
+            "block_size": problem.block_size,
+            "partition_size": ps,
+            "partitions": calls[0].num_partitions,
+            "launch": args.launch,
+            "accumulate": "fp32",
+        },
+        "frac_of_hbm_peak": (value / HBM_PEAK_GBS) if decode else None,
+        "kv_bytes_per_step": kv_read if decode else None,
+        "kv_unique_bytes_per_step": kv_unique if decode else None,
+        "effective_gbs": (kv_read / (ms * 1e-3) / 1e9) if decode else None,
+        "eager_ms_per_step": eager_ms,
+        "wall_ms_per_step": wall_ms,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "parity": par,
+        "chunk": secondary,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -102,17 +102,29 @@ typedef struct pa_shape {
   uint32_t reserved;          /* must be 0 */
 } pa_shape;
 
-/* Bytes of scratch pa_attend needs for this shape: split-KV partials
- * (normalised fp32 output and fp32 LSE per partition and row).  0 when the
- * call needs none.  Returns 0 for a shape pa_attend would reject. */
+/* Bytes of scratch pa_attend needs for this shape: one int32 counter per
+ * (slot, KV head), then the split-KV partials (fp32 LSE and normalised fp32
+ * output per partition and row).  0 when the call needs none.  Returns 0 for
+ * a shape pa_attend would reject. */
 size_t pa_workspace_size(const pa_shape* shape);
+
+/* Prepare a workspace for this shape: zero its counter region (enqueued on
+ * `stream` as a kernel, so it may be captured in a graph).  Required once
+ * before a workspace is first used with a shape, and again before it is
+ * reused with a different shape.  Every pa_attend call that completes leaves
+ * the counters at zero again, so repeated calls (and graph replays) with the
+ * same shape need no further initialisation.  Errors as for pa_attend. */
+pa_status pa_workspace_init(const pa_shape* shape, void* workspace, size_t workspace_bytes,
+                            void* stream);
 
 /* Number of split-KV partitions pa_attend will use for this shape (1 = no
  * split, or the path that does not split); 0 for an invalid shape. */
 int32_t pa_num_partitions(const pa_shape* shape);
 
 /* Attention of the new rows against the paged cache, as defined above.
- * `workspace` may be NULL when pa_workspace_size() is 0.  `lse` may be NULL.
+ * `workspace` (initialised with pa_workspace_init for this shape) may be
+ * NULL when pa_workspace_size() is 0.  One workspace must not be used by two
+ * calls that can run at the same time.  `lse` may be NULL.
  * q and out must not overlap.  Errors: PA_ERR_NULL_ARG, PA_ERR_BAD_SHAPE,
  * PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE_TOO_SMALL (nothing launched), or
  * PA_ERR_LAUNCH. */

@@ -10,7 +10,7 @@ implementation.
 
 _BINDING = ("PaError", "Shape", "Status", "attend", "combine", "gather_kv", "validate",
             "lib_path", "load", "make_shape", "plan", "status_string", "workspace_size",
-            "EXPORTS")
+            "EXPORTS", "PreparedAttend", "workspace_init")
 
 
 def __getattr__(name):

@@ -22,7 +22,7 @@ PA_BAD_CTX_LEN = 0x2
 PA_BAD_Q_LEN = 0x4
 PA_BAD_TOTAL_Q = 0x8
 
-EXPORTS = ("pa_workspace_size", "pa_num_partitions", "pa_attend", "pa_combine",
+EXPORTS = ("pa_workspace_size", "pa_workspace_init", "pa_num_partitions", "pa_attend", "pa_combine",
            "pa_gather_kv", "pa_validate", "pa_status_string")
 
 
@@ -73,11 +73,18 @@ def load():
         return _lib
     if not os.path.exists(_LIB_PATH):
         raise RuntimeError(f"libpa.so not built at {_LIB_PATH}; run paged_kv_cache_attend_amd.build")
+    # torch carries its own copy of the HIP runtime.  Loading torch first lets
+    # libpa.so bind to that same copy (same SONAME), so device pointers and
+    # stream handles from torch are valid in the library; loading libpa.so
+    # first would put two HIP runtimes in the process.
+    import torch  # noqa: F401
     lib = ctypes.CDLL(_LIB_PATH)
     P = ctypes.c_void_p
     shp = ctypes.POINTER(Shape)
     lib.pa_workspace_size.argtypes = [shp]
     lib.pa_workspace_size.restype = ctypes.c_size_t
+    lib.pa_workspace_init.argtypes = [shp, P, ctypes.c_size_t, P]
+    lib.pa_workspace_init.restype = ctypes.c_int
     lib.pa_num_partitions.argtypes = [shp]
     lib.pa_num_partitions.restype = ctypes.c_int32
     lib.pa_attend.argtypes = [shp, P, P, P, P, P, P, ctypes.c_float, P, P, P, ctypes.c_size_t, P]
@@ -114,6 +121,14 @@ def make_shape(num_seqs, total_q, num_q_heads, num_kv_heads, max_blocks_per_seq,
 
 def workspace_size(shape: Shape) -> int:
     return int(load().pa_workspace_size(ctypes.byref(shape)))
+
+
+def workspace_init(shape: Shape, workspace, *, stream=None):
+    """``pa_workspace_init``: zero the workspace's counters for this shape."""
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = load().pa_workspace_init(ctypes.byref(shape), _ptr(workspace), ctypes.c_size_t(ws_bytes),
+                                  _stream_handle(workspace.device, stream))
+    _check(st, "pa_workspace_init")
 
 
 def plan(shape: Shape):
@@ -191,6 +206,7 @@ def attend(q, k_cache, v_cache, block_table, ctx_lens, q_lens, scale, out, lse=N
     need = workspace_size(shape)
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        workspace_init(shape, workspace, stream=stream)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = load().pa_attend(ctypes.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
                           _ptr(ctx_lens), _ptr(q_lens), ctypes.c_float(float(scale)), _ptr(out), _ptr(lse),
@@ -251,3 +267,49 @@ def validate(block_table, ctx_lens, q_lens, error_word, *, num_blocks: int, tota
                             _ptr(error_word), _stream_handle(dev, stream))
     _check(st, "pa_validate")
     return error_word
+
+
+class PreparedAttend:
+    """A ``pa_attend`` call with its arguments marshalled once.
+
+    For launch loops (benchmarks, graph capture): ``launch()`` makes the bare
+    C call on the given stream and checks the status.  The tensors must stay
+    alive and in place for as long as the object is used.
+    """
+
+    def __init__(self, q, k_cache, v_cache, block_table, ctx_lens, q_lens, scale, out, lse=None, *,
+                 max_q_len: int, max_ctx_len: int, partition_size: int = 0, causal: bool = False,
+                 workspace=None):
+        torch = _torch()
+        dev = q.device
+        for t, name, dt, nd in ((q, "q", torch.bfloat16, 3), (out, "out", torch.bfloat16, 3),
+                                (k_cache, "k_cache", torch.bfloat16, 4), (v_cache, "v_cache", torch.bfloat16, 4),
+                                (block_table, "block_table", torch.int32, 2), (ctx_lens, "ctx_lens", torch.int32, 1),
+                                (q_lens, "q_lens", torch.int32, 1)):
+            _need(t, name, dt, dev, nd)
+        if lse is not None:
+            _need(lse, "lse", torch.float32, dev, 2)
+        total_q, hq, d = q.shape
+        nb, hkv, bs, _ = k_cache.shape
+        self.shape = make_shape(block_table.shape[0], total_q, hq, hkv, block_table.shape[1], max_q_len,
+                                max_ctx_len, nb, partition_size, causal, head_dim=d, block_size=bs)
+        need, self.num_partitions = plan(self.shape)
+        if need and workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        self.workspace = workspace
+        ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        if ws_bytes < need:
+            raise PaError(Status.ERR_WORKSPACE_TOO_SMALL, "PreparedAttend")
+        if need:
+            workspace_init(self.shape, workspace)
+        self._keep = (q, k_cache, v_cache, block_table, ctx_lens, q_lens, out, lse, workspace)
+        self._fn = load().pa_attend
+        self._args = [ctypes.byref(self.shape), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+                      _ptr(ctx_lens), _ptr(q_lens), ctypes.c_float(float(scale)), _ptr(out), _ptr(lse),
+                      _ptr(workspace), ctypes.c_size_t(ws_bytes)]
+        self.device = dev
+
+    def launch(self, stream=None):
+        st = self._fn(*self._args, _stream_handle(self.device, stream))
+        if st:
+            raise PaError(st, "pa_attend")

@@ -28,9 +28,14 @@ struct Plan {
   int num_parts = 1;      // partitions (decode)
   size_t rows = 0;        // total_q * num_q_heads
   size_t ws_bytes = 0;    // workspace bytes
-  size_t part_out_bytes = 0;
+  // Workspace layout (split decode): counters | partial LSE | partial out.
+  size_t counters_bytes = 0;
+  size_t lse_offset = 0;
+  size_t out_offset = 0;
   unsigned grid = 0;
 };
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
@@ -55,16 +60,18 @@ pa_status check_shape(const pa_shape* s) {
   return PA_OK;
 }
 
-// Partition size when the caller leaves it to the library.  Decode moves
-// 8 KiB per page and KV head; a partition must be long enough to amortise its
-// prologue and epilogue (at least two pages per wave) and short enough that
-// the grid covers the 256 CUs with a few resident workgroups each.
+// Partition size when the caller leaves it to the library.  The decode grid
+// should fill the chip in one round of resident workgroups (kDecodeWGsPerCU
+// per CU): every (slot, KV head) pair is split into as many equal partitions
+// as fit, so all workgroups start together and finish together.  A partition
+// keeps at least two pages per wave to amortise its prologue and merge.
 int auto_part_pages(const pa_shape* s, int max_pages) {
   const long long pairs = (long long)s->num_seqs * s->num_kv_heads;
-  const long long target_wgs = 4LL * kNumCUs;
-  long long parts = (target_wgs + pairs - 1) / pairs;
+  const long long resident = (long long)kDecodeWGsPerCU * kNumCUs;
+  long long parts = resident / (pairs > 0 ? pairs : 1);
   if (parts < 1) parts = 1;
-  int pp = ceil_div(max_pages, (int)(parts > max_pages ? max_pages : parts));
+  if (parts > max_pages) parts = max_pages;
+  int pp = ceil_div(max_pages, (int)parts);
   if (pp < 8) pp = 8;
   return pp;
 }
@@ -89,8 +96,10 @@ pa_status make_plan(const pa_shape* s, Plan* plan) {
     if (grid > INT_MAX) return PA_ERR_UNSUPPORTED;
     p.grid = (unsigned)grid;
     if (p.num_parts > 1) {
-      p.part_out_bytes = (size_t)p.num_parts * p.rows * kHeadDim * sizeof(float);
-      p.ws_bytes = p.part_out_bytes + (size_t)p.num_parts * p.rows * sizeof(float);
+      p.counters_bytes = align256((size_t)s->num_seqs * s->num_kv_heads * sizeof(int32_t));
+      p.lse_offset = p.counters_bytes;
+      p.out_offset = p.lse_offset + align256((size_t)p.num_parts * p.rows * sizeof(float));
+      p.ws_bytes = p.out_offset + (size_t)p.num_parts * p.rows * kHeadDim * sizeof(float);
     }
   } else {
     const int q_tiles = ceil_div(s->max_q_len, kChunkRows);
@@ -147,10 +156,11 @@ pa_status pa_attend(const pa_shape* shape, const void* q, const void* k_cache,
     d.q_lens = q_lens;
     d.out = static_cast<uint16_t*>(out);
     d.lse = lse;
-    d.part_out = plan.num_parts > 1 ? static_cast<float*>(workspace) : nullptr;
-    d.part_lse = plan.num_parts > 1
-                     ? reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.part_out_bytes)
-                     : nullptr;
+    char* ws = static_cast<char*>(workspace);
+    const bool split = plan.num_parts > 1;
+    d.counters = split ? reinterpret_cast<int32_t*>(ws) : nullptr;
+    d.part_lse = split ? reinterpret_cast<float*>(ws + plan.lse_offset) : nullptr;
+    d.part_out = split ? reinterpret_cast<float*>(ws + plan.out_offset) : nullptr;
     d.scale_log2 = scale_log2;
     d.num_seqs = shape->num_seqs;
     d.num_q_heads = shape->num_q_heads;
@@ -160,17 +170,6 @@ pa_status pa_attend(const pa_shape* shape, const void* q, const void* k_cache,
     d.part_pages = plan.part_pages;
     d.num_parts = plan.num_parts;
     if (launch_decode(d, plan.group, plan.grid, s) != hipSuccess) return PA_ERR_LAUNCH;
-    if (plan.num_parts > 1) {
-      CombineParams c;
-      c.part_out = d.part_out;
-      c.part_lse = d.part_lse;
-      c.out = d.out;
-      c.lse = lse;
-      c.num_parts = plan.num_parts;
-      c.rows = (int32_t)plan.rows;
-      c.head_dim = kHeadDim;
-      if (launch_combine(c, s) != hipSuccess) return PA_ERR_LAUNCH;
-    }
     return PA_OK;
   }
 
@@ -191,6 +190,20 @@ pa_status pa_attend(const pa_shape* shape, const void* q, const void* k_cache,
   c.q_tiles = ceil_div(shape->max_q_len, kChunkRows);
   c.causal = (shape->flags & PA_FLAG_CAUSAL) ? 1 : 0;
   if (launch_chunk(c, plan.grid, s) != hipSuccess) return PA_ERR_LAUNCH;
+  return PA_OK;
+}
+
+pa_status pa_workspace_init(const pa_shape* shape, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  Plan plan;
+  const pa_status st = make_plan(shape, &plan);
+  if (st != PA_OK) return st;
+  if (plan.ws_bytes == 0) return PA_OK;
+  if (!workspace) return PA_ERR_NULL_ARG;
+  if (workspace_bytes < plan.ws_bytes) return PA_ERR_WORKSPACE_TOO_SMALL;
+  if (launch_zero_i32(static_cast<int32_t*>(workspace), plan.counters_bytes / sizeof(int32_t),
+                      static_cast<hipStream_t>(stream)) != hipSuccess)
+    return PA_ERR_LAUNCH;
   return PA_OK;
 }
 

@@ -239,8 +239,9 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_kernel(ChunkParams p) {
 }  // namespace
 
 hipError_t launch_chunk(const ChunkParams& p, unsigned grid, hipStream_t s) {
-  hipLaunchKernelGGL(chunk_kernel, dim3(grid), dim3(kThreads), 0, s, p);
-  return hipGetLastError();
+  ChunkParams arg = p;
+  void* args[] = {&arg};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&chunk_kernel), dim3(grid), dim3(kThreads), args, 0, s);
 }
 
 }  // namespace pa

@@ -77,8 +77,9 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineParams c) {
 
 hipError_t launch_combine(const CombineParams& c, hipStream_t s) {
   const unsigned grid = (unsigned)((c.rows + kRowsPerBlock - 1) / kRowsPerBlock);
-  hipLaunchKernelGGL(combine_kernel, dim3(grid), dim3(kThreads), 0, s, c);
-  return hipGetLastError();
+  CombineParams arg = c;
+  void* args[] = {&arg};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&combine_kernel), dim3(grid), dim3(kThreads), args, 0, s);
 }
 
 }  // namespace pa

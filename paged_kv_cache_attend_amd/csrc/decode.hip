@@ -1,4 +1,5 @@
-// decode.hip -- paged decode attention, one new token per slot, split-KV.
+// decode.hip -- paged decode attention, one new token per slot, split-KV with
+// the log-sum-exp merge fused into the same launch.
 //
 // What it computes: for each active slot and query head, softmax attention of
 // the one new query row over the slot's n cached keys, gathered through the
@@ -7,36 +8,43 @@
 // kernel is bound by HBM bandwidth (same chapter, section 8.2.1): per key and
 // KV head it moves 512 bytes (K and V, 128 bf16 each) and does 4 FLOP per
 // byte for a group of four query heads.  Everything is arranged around
-// streaming those bytes:
+// keeping enough of those bytes in flight:
 //
 // * Grid: one 256-thread workgroup per (KV head, slot, partition), where a
 //   partition is a run of `part_pages` 16-token pages (split-KV, "flash
 //   decoding"): short batches still put enough workgroups on 256 CUs.  The
 //   hardware id is remapped so each XCD owns a contiguous range of
-//   (KV head, slot) pairs -- slots that share prefix pages read them under
-//   one L2.
+//   (KV head, slot, partition) work -- the partitions of one slot, and slots
+//   that share prefix pages, read under one L2.
 // * Each of the 4 waves takes every 4th page of the partition.  A page of one
 //   KV head is a contiguous 4 KiB K tile and a 4 KiB V tile; a wave loads
-//   each with four 128-bit loads per lane (fully coalesced 1 KiB per
-//   instruction) and issues the next page's loads before working on the
-//   current one.  The block table entries of the partition are read once into
-//   lanes and broadcast with readlane.
+//   each with four 128-bit loads per lane (fully coalesced, 1 KiB per
+//   instruction) into a three-page register ring: two pages are in flight
+//   while one is consumed, and a page's loads are issued as soon as its
+//   buffer is free.  Page ids come from scalar loads one issue ahead.  The partition's block-table entries
+//   are read once into lanes and broadcast with readlane.
 // * Scores: the K tile goes to LDS (XOR-swizzled 16-byte chunks, conflict
-//   free); lane (token t = lane % 16, head h = lane / 16) forms the full
-//   128-long dot product of its query head with key t using bf16 dot2
-//   instructions against the query held in registers.  The whole group of
-//   query heads thus shares one read of each key.
-// * Online softmax in the log2 domain (scale * log2 e folded in): running max
-//   per head, row max over the 16 tokens with DPP row rotations, per-lane
-//   running sums reduced once at the end.
-// * PV: the V tile stays in registers in its load layout (lane holds 8 dims of
-//   tokens 4k + lane/16); the probabilities reach that layout through a tiny
-//   LDS buffer; fp32 FMA accumulation.
+//   free); lane (token t = lane % 16, head h = lane / 16) forms the 128-long
+//   dot product of its query head with key t using v_dot2c_f32_bf16 against
+//   the query staged in LDS, so the group of query heads shares one read of
+//   each key.
+// * Online softmax in the log2 domain (scale * log2 e folded in): per-head
+//   row max over the 16 tokens with DPP row rotations; the reference max is
+//   only raised (and the accumulators rescaled) when a score exceeds it by
+//   more than 2^8, which keeps every weight <= 256 and skips the rescale on
+//   almost every page.
+// * PV: the V tile stays in registers in its load layout (lane holds 8 dims
+//   of tokens 4k + lane/16).  Weights reach that layout through a small LDS
+//   buffer, are rounded to bf16 and paired by token; v_perm pairs the V
+//   values the same way, and v_dot2c_f32_bf16 accumulates two tokens per
+//   instruction in fp32.
 // * Epilogue: the four waves' (max, sum, acc) merge through LDS.  With one
-//   partition the workgroup writes bf16 out and the LSE; otherwise it writes
-//   the normalised fp32 partial and its LSE for the combine kernel.  Empty
-//   partitions (and slots with no keys) write LSE = -inf partials so the merge
-//   gives them zero weight; with one partition they write nothing at all.
+//   partition the workgroup writes bf16 out and the LSE.  Otherwise it writes
+//   its normalised fp32 partial and LSE to the workspace, and the last of the
+//   slot's partitions to finish (an atomic counter per (slot, KV head),
+//   reset to zero by that same workgroup) merges all partials by their LSE
+//   and writes the result, all in the same launch.  Empty partitions and slots with no keys take part
+//   with LSE = -inf; a slot whose partials are all -inf writes nothing.
 
 #include "device.h"
 
@@ -46,19 +54,158 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kTileBytes = kBlockSize * kHeadDim * 2;  // 4 KiB
+constexpr int kTileVec = kTileBytes / 16;              // uint4 per tile
+constexpr float kRescaleSlack = 8.0f;                  // log2 units
+
+struct Page {
+  u32x4_t k[4];
+  u32x4_t v[4];
+};
+
+// Issue the loads of one page (K and V tiles of KV head g) into `b`.
+__device__ __forceinline__ void issue_page(Page& b, const u32x4_t* __restrict__ kpool,
+                                           const u32x4_t* __restrict__ vpool, int32_t phys, int g,
+                                           int num_kv_heads, int lane) {
+  const size_t base = tile_index(phys, g, num_kv_heads) * kTileVec + lane;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) b.k[k] = kpool[base + k * 64];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) b.v[k] = vpool[base + k * 64];
+}
+
+template <int G>
+struct WaveState {
+  float m_ref;      // reference max (log2 domain) of head hq, uniform over its row
+  float l_lane;     // this lane's running sum of weights
+  float acc[G][8];  // PV layout accumulators
+};
+
+// One page: scores, online softmax, PV.  `sk` is this wave's 4 KiB LDS tile,
+// `sp` its 16 x 4 weight buffer, `salpha` its 4 rescale factors.
+template <int G>
+__device__ __forceinline__ void consume_page(WaveState<G>& st, Page& b, const uint8_t* sq,
+                                             uint8_t* sk, float* sp, float* salpha, int valid,
+                                             float scale_log2, int lane) {
+  const int tq = lane & 15;
+  const int hq = (lane >> 4) % G;
+  const int pr = lane >> 4;
+  const int pc = lane & 15;
+
+  // K tile -> LDS.  Row t (256 B) keeps its 16-byte chunk c at slot c ^ t.
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int t = 4 * k + pr;
+    *reinterpret_cast<u32x4_t*>(sk + t * 256 + ((pc ^ t) << 4)) = b.k[k];
+  }
+  wave_lds_sync();
+
+  // Score of (token tq, head hq).  The query of head h keeps its 16-byte chunk
+  // c at slot c ^ h, so the four heads' broadcast reads use different banks.
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const u32x4_t kk = *reinterpret_cast<const u32x4_t*>(sk + tq * 256 + ((i ^ tq) << 4));
+    const u32x4_t qq = *reinterpret_cast<const u32x4_t*>(sq + hq * 256 + ((i ^ hq) << 4));
+    s = dot8_bf16(qq, kk, s);
+  }
+  const float sl = (tq < valid) ? s * scale_log2 : -INFINITY;
+  const float tmax = row16_max(sl);
+  const bool raise = tmax > st.m_ref + kRescaleSlack;
+  const bool any_raise = __builtin_amdgcn_ballot_w64(raise) != 0;
+  float alpha = 1.f;
+  if (any_raise) {
+    const float m_new = fmaxf(st.m_ref, tmax);
+    alpha = fast_exp2(st.m_ref - m_new);  // 0 on the first page (m_ref = -inf)
+    st.m_ref = m_new;
+    st.l_lane *= alpha;
+  }
+  const float w = fast_exp2(sl - st.m_ref);
+  st.l_lane += w;
+  if ((lane >> 4) < G) {
+    sp[tq * 4 + hq] = w;
+    if (tq == 0) salpha[hq] = alpha;
+  }
+  wave_lds_sync();
+
+  if (any_raise) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float a = salpha[h];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) st.acc[h][j] *= a;
+    }
+  }
+
+  // Weights of this lane's tokens t_k = 4k + pr, all heads, as bf16 pairs
+  // (t0, t1) and (t2, t3).
+  uint32_t w01[G], w23[G];
+  {
+    const float4 p0 = *reinterpret_cast<const float4*>(sp + (0 + pr) * 4);
+    const float4 p1 = *reinterpret_cast<const float4*>(sp + (4 + pr) * 4);
+    const float4 p2 = *reinterpret_cast<const float4*>(sp + (8 + pr) * 4);
+    const float4 p3 = *reinterpret_cast<const float4*>(sp + (12 + pr) * 4);
+    const float a0[4] = {p0.x, p0.y, p0.z, p0.w};
+    const float a1[4] = {p1.x, p1.y, p1.z, p1.w};
+    const float a2[4] = {p2.x, p2.y, p2.z, p2.w};
+    const float a3[4] = {p3.x, p3.y, p3.z, p3.w};
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      w01[h] = pack_bf16x2(a0[h], a1[h]);
+      w23[h] = pack_bf16x2(a2[h], a3[h]);
+    }
+  }
+
+  // V of tokens past the end holds anything (NaN included): zero it.
+  if (valid < kBlockSize) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      if (4 * k + pr >= valid) b.v[k] = u32x4_t{0u, 0u, 0u, 0u};
+  }
+  // V pairs: dims (2w, 2w+1) of tokens (t0, t1) and (t2, t3).
+#pragma unroll
+  for (int wd = 0; wd < 4; ++wd) {
+    const uint32_t lo01 = __builtin_amdgcn_perm(b.v[1][wd], b.v[0][wd], 0x05040100u);
+    const uint32_t hi01 = __builtin_amdgcn_perm(b.v[1][wd], b.v[0][wd], 0x07060302u);
+    const uint32_t lo23 = __builtin_amdgcn_perm(b.v[3][wd], b.v[2][wd], 0x05040100u);
+    const uint32_t hi23 = __builtin_amdgcn_perm(b.v[3][wd], b.v[2][wd], 0x07060302u);
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      st.acc[h][2 * wd] = dot2_bf16(w01[h], lo01, st.acc[h][2 * wd]);
+      st.acc[h][2 * wd] = dot2_bf16(w23[h], lo23, st.acc[h][2 * wd]);
+      st.acc[h][2 * wd + 1] = dot2_bf16(w01[h], hi01, st.acc[h][2 * wd + 1]);
+      st.acc[h][2 * wd + 1] = dot2_bf16(w23[h], hi23, st.acc[h][2 * wd + 1]);
+    }
+  }
+}
+
+// Scalar prefix sum of q_lens[0 .. seq): the row of slot `seq`'s new token.
+__device__ __forceinline__ int q_row_scalar(const int32_t* q_lens, int seq) {
+  int s = 0;
+  int i = 0;
+  for (; i + 16 <= seq; i += 16) {
+    int t = 0;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) t += scalar_load_i32(q_lens, i + j);
+    s += t;
+  }
+  for (; i < seq; ++i) s += scalar_load_i32(q_lens, i);
+  return s;
+}
 
 template <int G>
 __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeParams p) {
   static_assert(G == 1 || G == 2 || G == 4, "group size");
   __shared__ __attribute__((aligned(16))) uint8_t s_k[kWaves][kTileBytes];
-  __shared__ __attribute__((aligned(16))) float s_p[kWaves][kBlockSize][4];
+  __shared__ __attribute__((aligned(16))) uint8_t s_q[G][kHeadDim * 2];
+  __shared__ __attribute__((aligned(16))) float s_p[kWaves][kBlockSize * 4];
   __shared__ __attribute__((aligned(16))) float s_alpha[kWaves][4];
   __shared__ __attribute__((aligned(16))) float s_acc[kWaves][4][G][kHeadDim];
   __shared__ float s_m[kWaves][G];
   __shared__ float s_l[kWaves][G];
+  __shared__ int s_last;
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
   const int wg = xcd_remap(blockIdx.x, gridDim.x);
   const int P = p.num_parts;
@@ -67,186 +214,229 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeParams 
   const int seq = rest % p.num_seqs;
   const int g = rest / p.num_seqs;
 
-  const int m = p.q_lens[seq];
-  if (m <= 0) return;  // no row: nothing to write
-  const int n = p.ctx_lens[seq];
-  const int q_row = q_row_offset(p.q_lens, seq, lane);
-  const int h0 = g * G;
+  // Lengths, row offset and page ids are wave-uniform: scalar loads, which
+  // do not share the (in-order) vector load counter with the page stream.
+  const int m = scalar_load_i32(p.q_lens, seq);
+  if (m <= 0) return;  // no row: nothing to write, no partial to count
+  const int n = scalar_load_i32(p.ctx_lens, seq);
   const int npages = (n + kBlockSize - 1) / kBlockSize;
   const int pstart = part * p.part_pages;
   const int pend = min(npages, pstart + p.part_pages);
-  const size_t rows = (size_t)p.total_q * p.num_q_heads;
+  const bool has_work = n > 0 && pstart < pend;
 
-  if (n <= 0 || pstart >= pend) {
-    // zombie slot or empty partition
-    if (P > 1 && threadIdx.x < G) {
-      p.part_lse[(size_t)part * rows + (size_t)q_row * p.num_q_heads + h0 + threadIdx.x] = -INFINITY;
+  const int32_t* bt = p.block_table + (size_t)seq * p.max_blocks;
+  const u32x4_t* kpool = reinterpret_cast<const u32x4_t*>(p.k);
+  const u32x4_t* vpool = reinterpret_cast<const u32x4_t*>(p.v);
+  const int last_page = pend - 1;
+  auto page_id = [&](int page) -> int32_t { return scalar_load_i32(bt, min(page, last_page)); };
+
+  const int h0 = g * G;
+  const size_t rows = (size_t)p.total_q * p.num_q_heads;
+  const int my_h = (threadIdx.x * 2) / kHeadDim;  // epilogue role: 2 dims of one head
+  const int my_d = (threadIdx.x * 2) % kHeadDim;
+  const bool my_out = threadIdx.x * 2 < G * kHeadDim;
+  float my_o0 = 0.f, my_o1 = 0.f, my_lse = -INFINITY;  // this workgroup's partial
+
+  // Prologue, in issue order: the wave's first page, the query (so that its
+  // wait only covers that first page, needed next anyway), the second and
+  // third pages.  Every load here is unconditional within the workgroup-
+  // uniform has_work branch -- a wave with fewer than three pages re-reads a
+  // valid page -- so the load counter's waits stay exact.
+  Page ring0, ring1, ring2;
+  const int page0 = pstart + wave;
+  const int cnt = (has_work && page0 < pend) ? (pend - page0 + kWaves - 1) / kWaves : 0;
+  int q_row = 0;
+  int32_t next_id = 0;
+  if (has_work) {
+    issue_page(ring0, kpool, vpool, page_id(page0), g, p.num_kv_heads, lane);
+    issue_order_barrier();
+    q_row = q_row_scalar(p.q_lens, seq);
+    const int qh = (threadIdx.x >> 4) % G, qc = threadIdx.x & 15;
+    const u32x4_t qchunk =
+        reinterpret_cast<const u32x4_t*>(p.q)[((size_t)q_row * p.num_q_heads + h0 + qh) * 16 + qc];
+    issue_order_barrier();
+    issue_page(ring1, kpool, vpool, page_id(page0 + kWaves), g, p.num_kv_heads, lane);
+    issue_page(ring2, kpool, vpool, page_id(page0 + 2 * kWaves), g, p.num_kv_heads, lane);
+    next_id = page_id(page0 + 3 * kWaves);
+    // Query of heads h0 .. h0+G-1 -> LDS, 16-byte chunk c of head h at slot c ^ h.
+    if (threadIdx.x < G * 16) *reinterpret_cast<u32x4_t*>(&s_q[qh][(qc ^ qh) << 4]) = qchunk;
+    __syncthreads();
+  } else {
+    q_row = q_row_scalar(p.q_lens, seq);
+  }
+
+  if (has_work) {
+    WaveState<G> st;
+    st.m_ref = -INFINITY;
+    st.l_lane = 0.f;
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) st.acc[h][j] = 0.f;
+
+    uint8_t* sk = s_k[wave];
+    float* sp = s_p[wave];
+    float* sa = s_alpha[wave];
+    const uint8_t* sq = &s_q[0][0];
+    // This wave's pages are page0 + 4k for k < cnt; page k lives in ring k % 3.
+    // The main loop reissues unconditionally, so the (in-order) load counter
+    // sees the same pattern on every trip and each wait leaves the other two
+    // pages in flight; the last pages are peeled off.
+    auto valid_of = [&](int k) { return min(kBlockSize, n - (page0 + kWaves * k) * kBlockSize); };
+#define PA_CONSUME(RING, K) consume_page<G>(st, RING, sq, sk, sp, sa, valid_of(K), p.scale_log2, lane)
+#define PA_REISSUE(RING, K)                                          \
+  {                                                                  \
+    issue_page(RING, kpool, vpool, next_id, g, p.num_kv_heads, lane); \
+    next_id = page_id(page0 + kWaves * ((K) + 1));                   \
+  }
+    int k = 0;
+    for (; k + 5 < cnt; k += 3) {
+      PA_CONSUME(ring0, k);
+      PA_REISSUE(ring0, k + 3);
+      PA_CONSUME(ring1, k + 1);
+      PA_REISSUE(ring1, k + 4);
+      PA_CONSUME(ring2, k + 2);
+      PA_REISSUE(ring2, k + 5);
+    }
+    // At most five pages left: k, k+1, k+2 in rings 0, 1, 2 (if they exist);
+    // k+3 and k+4 still to be issued into rings 0 and 1.
+    if (k < cnt) {
+      PA_CONSUME(ring0, k);
+      if (k + 3 < cnt) PA_REISSUE(ring0, k + 3);
+      if (k + 1 < cnt) {
+        PA_CONSUME(ring1, k + 1);
+        if (k + 4 < cnt) PA_REISSUE(ring1, k + 4);
+      }
+      if (k + 2 < cnt) PA_CONSUME(ring2, k + 2);
+      if (k + 3 < cnt) PA_CONSUME(ring0, k + 3);
+      if (k + 4 < cnt) PA_CONSUME(ring1, k + 4);
+    }
+#undef PA_CONSUME
+#undef PA_REISSUE
+
+    // Per-wave state -> LDS.
+    const int tq = lane & 15;
+    const int hq = (lane >> 4) % G;
+    const int pr = lane >> 4;
+    const int pc = lane & 15;
+    const float l_sum = row16_sum(st.l_lane);
+    if ((lane >> 4) < G && tq == 0) {
+      s_m[wave][hq] = st.m_ref;
+      s_l[wave][hq] = l_sum;
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float4* dst = reinterpret_cast<float4*>(&s_acc[wave][pr][h][pc * 8]);
+      dst[0] = make_float4(st.acc[h][0], st.acc[h][1], st.acc[h][2], st.acc[h][3]);
+      dst[1] = make_float4(st.acc[h][4], st.acc[h][5], st.acc[h][6], st.acc[h][7]);
+    }
+    __syncthreads();
+
+    // Merge the waves: two adjacent dims of one head per thread.
+    if (my_out) {
+      const int h = my_h, d = my_d;
+      float M = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_m[w][h]);
+      float L = 0.f, a0 = 0.f, a1 = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float sc = fast_exp2(s_m[w][h] - M);  // 0 for a wave with no page
+        L = fmaf(sc, s_l[w][h], L);
+        float x0 = 0.f, x1 = 0.f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float2 v = *reinterpret_cast<const float2*>(&s_acc[w][r][h][d]);
+          x0 += v.x;
+          x1 += v.y;
+        }
+        a0 = fmaf(sc, x0, a0);
+        a1 = fmaf(sc, x1, a1);
+      }
+      const float inv = 1.f / L;
+      my_o0 = a0 * inv;
+      my_o1 = a1 * inv;
+      my_lse = (M + fast_log2(L)) * kLn2;  // natural log
+    }
+  }
+
+  if (P == 1) {
+    if (has_work && my_out) {
+      const size_t row = (size_t)q_row * p.num_q_heads + h0 + my_h;
+      reinterpret_cast<uint32_t*>(p.out)[(row * kHeadDim + my_d) / 2] = pack_bf16x2(my_o0, my_o1);
+      if (my_d == 0 && p.lse) p.lse[row] = my_lse;
     }
     return;
   }
 
-  // Lane roles.  Score layout: token tq, head hq.  Load / PV layout: tokens
-  // 4k + pr (k = 0..3), dims 8*pc .. 8*pc + 7.
-  const int tq = lane & 15;
-  const int hq = (lane >> 4) % G;
-  const int pr = lane >> 4;
-  const int pc = lane & 15;
-
-  // Query of head h0 + hq, 128 bf16 = 16 x 16 bytes, held in registers.
-  uint4 qv[16];
-  {
-    const uint4* qp = reinterpret_cast<const uint4*>(p.q) +
-                      ((size_t)q_row * p.num_q_heads + h0 + hq) * (kHeadDim / 8);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) qv[i] = qp[i];
+  // Split: publish this partition's partial, count it, and let the last
+  // partition of the (slot, KV head) to finish merge them all.  The partials
+  // and the counter are exchanged with relaxed device-scope atomics, which
+  // the compiler emits as cache-coherent (sc1) loads and stores; each thread
+  // waits for its partial stores to complete before the workgroup bumps the
+  // counter.  This avoids device-scope fences, which on this chip write back
+  // and invalidate the whole L2 of the XCD.
+  uint64_t* part_out64 = reinterpret_cast<uint64_t*>(p.part_out);
+  if (my_out) {
+    const size_t prow = (size_t)part * rows + (size_t)q_row * p.num_q_heads + h0 + my_h;
+    if (has_work) {
+      const uint64_t bits = (uint64_t)__float_as_uint(my_o0) | ((uint64_t)__float_as_uint(my_o1) << 32);
+      __hip_atomic_store(part_out64 + (prow * kHeadDim + my_d) / 2, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (my_d == 0) __hip_atomic_store(p.part_lse + prow, my_lse, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-
-  // Block table entries of this partition, one per lane, 64 at a time.
-  const int32_t* bt = p.block_table + (size_t)seq * p.max_blocks;
-  int bt_base = pstart;
-  int bt_lane = (pstart + lane < pend) ? bt[pstart + lane] : 0;
-
-  const uint4* kpool = reinterpret_cast<const uint4*>(p.k);
-  const uint4* vpool = reinterpret_cast<const uint4*>(p.v);
-
-  uint4 kn[4], vn[4];
-  auto load_page = [&](int page) {
-    if (page - bt_base >= 64) {
-      bt_base += 64;
-      bt_lane = (bt_base + lane < pend) ? bt[bt_base + lane] : 0;
-    }
-    const int phys = __builtin_amdgcn_readlane(bt_lane, page - bt_base);
-    const size_t base = tile_index(phys, g, p.num_kv_heads) * (kTileBytes / 16);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) kn[k] = kpool[base + k * 64 + lane];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) vn[k] = vpool[base + k * 64 + lane];
-  };
-
-  float m_run = -INFINITY;  // running max (log2 domain) of head hq
-  float l_lane = 0.f;       // running sum of this lane's probabilities
-  float acc[G][8];
-#pragma unroll
-  for (int h = 0; h < G; ++h)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) acc[h][j] = 0.f;
-
-  uint8_t* sk = s_k[wave];
-  int page = pstart + wave;
-  if (page < pend) load_page(page);
-
-  for (; page < pend; page += kWaves) {
-    // K tile -> LDS.  Row t (256 B) keeps its 16-byte chunk c at slot c ^ t.
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int t = 4 * k + pr;
-      *reinterpret_cast<uint4*>(sk + t * 256 + ((pc ^ t) << 4)) = kn[k];
-    }
-    uint4 vc[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) vc[k] = vn[k];
-    const int valid = min(kBlockSize, n - page * kBlockSize);
-    if (page + kWaves < pend) load_page(page + kWaves);
-    wave_lds_sync();
-
-    // Score of (token tq, head hq).
-    float s = 0.f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const uint4 kk = *reinterpret_cast<const uint4*>(sk + tq * 256 + ((i ^ tq) << 4));
-      s = dot8_bf16(qv[i], kk, s);
-    }
-    const float sl = (tq < valid) ? s * p.scale_log2 : -INFINITY;
-    const float tmax = row16_max(sl);
-    const float m_new = fmaxf(m_run, tmax);
-    const float alpha = fast_exp2(m_run - m_new);
-    const float pw = fast_exp2(sl - m_new);
-    l_lane = l_lane * alpha + pw;
-    m_run = m_new;
-    if ((lane >> 4) < G) {
-      s_p[wave][tq][hq] = pw;
-      if (tq == 0) s_alpha[wave][hq] = alpha;
-    }
-    wave_lds_sync();
-
-    // PV in the load layout.
-    float al[G];
-#pragma unroll
-    for (int h = 0; h < G; ++h) al[h] = s_alpha[wave][h];
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) acc[h][j] *= al[h];
-    if (valid < kBlockSize) {
-#pragma unroll
-      for (int k = 0; k < 4; ++k)
-        if (4 * k + pr >= valid) vc[k] = make_uint4(0u, 0u, 0u, 0u);
-    }
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int t = 4 * k + pr;
-      const float4 pt = *reinterpret_cast<const float4*>(&s_p[wave][t][0]);
-      const float pk[4] = {pt.x, pt.y, pt.z, pt.w};
-      float vf[8];
-      vf[0] = bf16_lo(vc[k].x); vf[1] = bf16_hi(vc[k].x);
-      vf[2] = bf16_lo(vc[k].y); vf[3] = bf16_hi(vc[k].y);
-      vf[4] = bf16_lo(vc[k].z); vf[5] = bf16_hi(vc[k].z);
-      vf[6] = bf16_lo(vc[k].w); vf[7] = bf16_hi(vc[k].w);
-#pragma unroll
-      for (int h = 0; h < G; ++h)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) acc[h][j] = fmaf(pk[h], vf[j], acc[h][j]);
-    }
-  }
-
-  // Per-wave state -> LDS.
-  const float l_sum = row16_sum(l_lane);
-  if ((lane >> 4) < G && tq == 0) {
-    s_m[wave][hq] = m_run;
-    s_l[wave][hq] = l_sum;
-  }
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    float4* dst = reinterpret_cast<float4*>(&s_acc[wave][pr][h][pc * 8]);
-    dst[0] = make_float4(acc[h][0], acc[h][1], acc[h][2], acc[h][3]);
-    dst[1] = make_float4(acc[h][4], acc[h][5], acc[h][6], acc[h][7]);
-  }
+  wait_vm_stores();
   __syncthreads();
+  int32_t* counter = p.counters + (size_t)seq * p.num_kv_heads + g;
+  if (threadIdx.x == 0)
+    s_last = (__hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == P - 1);
+  __syncthreads();
+  if (!s_last) return;
 
-  // Merge the waves: two adjacent dims of one head per thread.
-  for (int o = threadIdx.x * 2; o < G * kHeadDim; o += kDecodeThreads * 2) {
-    const int h = o / kHeadDim;
-    const int d = o % kHeadDim;
-    float M = -INFINITY;
+  // Merge by log-sum-exp weights, online over batches of up to 8 partials:
+  // every load of a batch is issued before any is used, and a partial with
+  // LSE = -inf (empty) gets weight 0 without its output being read.
+  if (my_out) {
+    const size_t row = (size_t)q_row * p.num_q_heads + h0 + my_h;
+    const float* pl = p.part_lse + row;
+    const uint64_t* po = part_out64 + (row * kHeadDim + my_d) / 2;
+    const size_t ostride = rows * kHeadDim / 2;
+    float M = -INFINITY, W = 0.f, a0 = 0.f, a1 = 0.f;
+    for (int q0 = 0; q0 < P; q0 += 8) {
+      float lv[8];
+      uint64_t ov[8];
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_m[w][h]);
-    float L = 0.f, a0 = 0.f, a1 = 0.f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float sc = fast_exp2(s_m[w][h] - M);  // 0 for a wave with no page
-      L = fmaf(sc, s_l[w][h], L);
-      float x0 = 0.f, x1 = 0.f;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        x0 += s_acc[w][r][h][d];
-        x1 += s_acc[w][r][h][d + 1];
+      for (int i = 0; i < 8; ++i) {
+        const int q = min(q0 + i, P - 1);
+        lv[i] = __hip_atomic_load(pl + (size_t)q * rows, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        ov[i] = __hip_atomic_load(po + (size_t)q * ostride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
-      a0 = fmaf(sc, x0, a0);
-      a1 = fmaf(sc, x1, a1);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float l = (q0 + i < P) ? lv[i] : -INFINITY;
+        if (l == -INFINITY) continue;
+        const float M2 = fmaxf(M, l);
+        const float sc = fast_exp2((M - M2) * 1.4426950408889634f);  // 0 when M = -inf
+        const float w = fast_exp2((l - M2) * 1.4426950408889634f);
+        W = fmaf(W, sc, w);
+        a0 = fmaf(a0, sc, w * __uint_as_float((uint32_t)ov[i]));
+        a1 = fmaf(a1, sc, w * __uint_as_float((uint32_t)(ov[i] >> 32)));
+        M = M2;
+      }
     }
-    const float inv = 1.f / L;
-    const float o0 = a0 * inv, o1 = a1 * inv;
-    const float lse = (M + fast_log2(L)) * kLn2;
-    const size_t row = (size_t)q_row * p.num_q_heads + h0 + h;
-    if (P == 1) {
-      reinterpret_cast<uint32_t*>(p.out)[(row * kHeadDim + d) / 2] = pack_bf16x2(o0, o1);
-      if (d == 0 && p.lse) p.lse[row] = lse;
-    } else {
-      const size_t prow = (size_t)part * rows + row;
-      reinterpret_cast<float2*>(p.part_out)[(prow * kHeadDim + d) / 2] = make_float2(o0, o1);
-      if (d == 0) p.part_lse[prow] = lse;
+    if (M != -INFINITY) {
+      const float inv = 1.f / W;
+      reinterpret_cast<uint32_t*>(p.out)[(row * kHeadDim + my_d) / 2] = pack_bf16x2(a0 * inv, a1 * inv);
+      if (my_d == 0 && p.lse) p.lse[row] = M + fast_log2(W) * kLn2;
     }
   }
+  // Leave the counter at zero for the next call (the next launch sees it).
+  if (threadIdx.x == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__global__ __launch_bounds__(256) void zero_kernel(int32_t* __restrict__ x, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+    x[i] = 0;
 }
 
 }  // namespace
@@ -254,13 +444,26 @@ __global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeParams 
 bool decode_supports_group(int group) { return group == 1 || group == 2 || group == 4; }
 
 hipError_t launch_decode(const DecodeParams& p, int group, unsigned grid, hipStream_t s) {
+  const void* fn = nullptr;
   switch (group) {
-    case 1: hipLaunchKernelGGL(decode_kernel<1>, dim3(grid), dim3(kDecodeThreads), 0, s, p); break;
-    case 2: hipLaunchKernelGGL(decode_kernel<2>, dim3(grid), dim3(kDecodeThreads), 0, s, p); break;
-    case 4: hipLaunchKernelGGL(decode_kernel<4>, dim3(grid), dim3(kDecodeThreads), 0, s, p); break;
+    case 1: fn = reinterpret_cast<const void*>(&decode_kernel<1>); break;
+    case 2: fn = reinterpret_cast<const void*>(&decode_kernel<2>); break;
+    case 4: fn = reinterpret_cast<const void*>(&decode_kernel<4>); break;
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
+  DecodeParams arg = p;
+  void* args[] = {&arg};
+  return hipLaunchKernel(fn, dim3(grid), dim3(kDecodeThreads), args, 0, s);
+}
+
+hipError_t launch_zero_i32(int32_t* x, size_t n, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  size_t blocks = (n + 255) / 256;
+  if (blocks > 1024) blocks = 1024;
+  int32_t* xa = x;
+  size_t na = n;
+  void* args[] = {&xa, &na};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&zero_kernel), dim3((unsigned)blocks), dim3(256), args, 0, s);
 }
 
 }  // namespace pa

@@ -12,6 +12,10 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+// Native vectors for 16-byte data in registers (HIP's uint4 is a struct whose
+// copies can end up in scratch memory).
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 // ---------------------------------------------------------------------------
 // Page addressing.  Logical key j of a slot lives in logical block j / 16 at
@@ -62,7 +66,7 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
                                          __builtin_bit_cast(bf16x2_t, b), c, false);
 }
-__device__ __forceinline__ float dot8_bf16(const uint4& a, const uint4& b, float c) {
+__device__ __forceinline__ float dot8_bf16(const u32x4_t& a, const u32x4_t& b, float c) {
   c = dot2_bf16(a.x, b.x, c);
   c = dot2_bf16(a.y, b.y, c);
   c = dot2_bf16(a.z, b.z, c);
@@ -114,6 +118,26 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
+
+// Wave-uniform read of read-only data through the scalar cache (s_load).
+// The pointer is viewed in the constant address space, which is only valid
+// for memory no kernel writes while this one runs (e.g. the block table).
+// Scalar loads are counted apart from vector loads, so waiting for one does
+// not drain the vector loads in flight.
+__device__ __forceinline__ int32_t scalar_load_i32(const int32_t* p, int idx) {
+  const __attribute__((address_space(4))) int32_t* cp =
+      (const __attribute__((address_space(4))) int32_t*)(p);
+  return cp[__builtin_amdgcn_readfirstlane(idx)];
+}
+
+// Compiler-only barrier for memory operations: keeps the issue order of the
+// loads on either side (emits no instruction).
+__device__ __forceinline__ void issue_order_barrier() { asm volatile("" ::: "memory"); }
+
+// Wait until this thread's outstanding vector-memory operations (loads and
+// stores) have completed: s_waitcnt vmcnt(0), the other counters left
+// unconstrained (expcnt 7, lgkmcnt 15 in the gfx9 encoding).
+__device__ __forceinline__ void wait_vm_stores() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }

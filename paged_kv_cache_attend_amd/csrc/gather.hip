@@ -77,13 +77,15 @@ __global__ __launch_bounds__(256) void validate_kernel(ValidateParams p) {
 
 hipError_t launch_gather(const GatherParams& p, hipStream_t s) {
   const unsigned grid = (unsigned)p.num_seqs * (unsigned)p.max_pages;
-  hipLaunchKernelGGL(gather_kernel, dim3(grid), dim3(256), 0, s, p);
-  return hipGetLastError();
+  GatherParams arg = p;
+  void* args[] = {&arg};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&gather_kernel), dim3(grid), dim3(256), args, 0, s);
 }
 
 hipError_t launch_validate(const ValidateParams& p, hipStream_t s) {
-  hipLaunchKernelGGL(validate_kernel, dim3(1), dim3(256), 0, s, p);
-  return hipGetLastError();
+  ValidateParams arg = p;
+  void* args[] = {&arg};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&validate_kernel), dim3(1), dim3(256), args, 0, s);
 }
 
 }  // namespace pa

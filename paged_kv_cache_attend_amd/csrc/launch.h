@@ -12,6 +12,7 @@ constexpr int kHeadDim = 128;    // only head size built
 constexpr int kBlockSize = 16;   // tokens per KV block
 constexpr int kNumCUs = 256;     // MI355X compute units (8 XCDs x 32)
 constexpr int kNumXCDs = 8;
+constexpr int kDecodeWGsPerCU = 2;  // decode workgroups resident per CU (register bound)
 
 // Split-KV decode: one workgroup per (KV head, slot, partition).
 struct DecodeParams {
@@ -25,6 +26,7 @@ struct DecodeParams {
   float* lse;                 // fp32 [total_q][Hq] or null   (num_parts == 1)
   float* part_out;            // fp32 [num_parts][total_q*Hq][128] (num_parts > 1)
   float* part_lse;            // fp32 [num_parts][total_q*Hq]
+  int32_t* counters;          // [num_seqs][Hkv] finished partitions; zero between calls
   float scale_log2;           // softmax scale * log2(e)
   int32_t num_seqs;
   int32_t num_q_heads;
@@ -93,6 +95,7 @@ struct ValidateParams {
 bool decode_supports_group(int group);
 constexpr int kDecodeThreads = 256;
 hipError_t launch_decode(const DecodeParams& p, int group, unsigned grid, hipStream_t s);
+hipError_t launch_zero_i32(int32_t* x, size_t n, hipStream_t s);
 
 constexpr int kChunkRows = 128;  // query rows per chunk workgroup
 hipError_t launch_chunk(const ChunkParams& p, unsigned grid, hipStream_t s);

@@ -51,6 +51,15 @@ def test_shape_struct_layout():
     assert pk.Shape.num_blocks.offset == 40
 
 
+def _align(x):
+    return (x + 255) // 256 * 256
+
+
+def _ws_bytes(num_seqs, hkv, parts, rows):
+    """counters | partial LSE | partial out, each region 256-byte aligned."""
+    return _align(num_seqs * hkv * 4) + _align(parts * rows * 4) + parts * rows * 128 * 4
+
+
 def _shape(**kw):
     base = dict(num_seqs=4, total_q=4, num_q_heads=32, num_kv_heads=8, max_blocks_per_seq=10,
                 max_q_len=1, max_ctx_len=160, num_blocks=64)
@@ -118,7 +127,8 @@ def test_workspace_checks(lib):
     need, parts = pk.plan(s)
     assert parts == 17
     rows = 68 * 32
-    assert need == parts * rows * (128 + 1) * 4 == 19_087_872
+    assert need == _ws_bytes(68, 8, parts, rows)
+    assert need - _align(68 * 8 * 4) - (_align(parts * rows * 4) - parts * rows * 4) == 19_087_872
     assert _attend(lib, s, ws=None, ws_bytes=0) == pk.Status.ERR_NULL_ARG
     assert _attend(lib, s, ws=FAKE, ws_bytes=need - 1) == pk.Status.ERR_WORKSPACE_TOO_SMALL
 
@@ -134,7 +144,7 @@ def test_auto_partitions_cover_the_chip(lib):
     s = _shape(num_seqs=16, total_q=16, max_blocks_per_seq=144, max_ctx_len=2303, num_blocks=2592)
     ws, parts = pk.plan(s)
     assert parts > 1 and 16 * 8 * parts >= 512
-    assert ws == parts * 16 * 32 * 129 * 4
+    assert ws == _ws_bytes(16, 8, parts, 16 * 32)
 
 
 def test_chunk_path_needs_no_workspace(lib):
@@ -161,6 +171,18 @@ def test_combine_argument_checks(lib):
     assert f(2, 0, 128, None, None, None, None, None) == pk.Status.OK
 
 
+def test_workspace_init_argument_checks(lib):
+    s = _shape(partition_size=32)
+    need, parts = pk.plan(s)
+    assert parts == 5 and need > 0
+    assert lib.pa_workspace_init(ctypes.byref(s), None, need, None) == pk.Status.ERR_NULL_ARG
+    assert lib.pa_workspace_init(ctypes.byref(s), FAKE, need - 1, None) == pk.Status.ERR_WORKSPACE_TOO_SMALL
+    one = _shape(partition_size=160)
+    assert lib.pa_workspace_init(ctypes.byref(one), None, 0, None) == pk.Status.OK  # nothing to prepare
+    bad = _shape(head_dim=64)
+    assert lib.pa_workspace_init(ctypes.byref(bad), FAKE, need, None) == pk.Status.ERR_UNSUPPORTED
+
+
 def test_gather_and_validate_argument_checks(lib):
     s = _shape()
     assert lib.pa_gather_kv(ctypes.byref(s), None, FAKE, FAKE, FAKE, None) == pk.Status.ERR_NULL_ARG
@@ -175,3 +197,13 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "_LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="not built"):
         _lib.load()
+
+
+def test_single_hip_runtime_in_process():
+    # libpa.so must share torch's HIP runtime even when the library is loaded
+    # before anything else imports torch (two runtimes break stream handles).
+    code = ("import paged_kv_cache_attend_amd as pk; pk.load(); import torch; "
+            "paths = {l.split()[-1] for l in open('/proc/self/maps') if 'libamdhip64' in l}; "
+            "print(len(paths))")
+    out = subprocess.run(["python", "-c", code], capture_output=True, text=True, cwd=ROOT, check=True).stdout
+    assert out.strip() == "1"

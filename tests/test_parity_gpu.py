@@ -118,6 +118,57 @@ def test_repeat_calls_are_deterministic():
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1].view(np.uint32), b[1].view(np.uint32))
 
 
+def test_graph_replay_matches_eager():
+    # capture one split call in a graph; replay it several times with eager work
+    # in between and check every replay (the counters must come back to zero)
+    p = _case([2303, 700, 0, 1500], hq=32, hkv=8, seed=61)
+    q, k, v = p.layer(0)
+    eager = run_gpu(p, q=q, k=k, v=v, partition_size=256)
+    t = inputs.to_device(p, q, k, v, DEV)
+    out = torch.full(q.shape, OUT_SENTINEL, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+    lse = torch.full(q.shape[:2], LSE_SENTINEL, dtype=torch.int32, device=DEV).view(torch.float32)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        call = pk.PreparedAttend(t["q"], t["k"], t["v"], t["block_table"], t["ctx_lens"], t["q_lens"],
+                                 float(p.scale), out, lse, max_q_len=1, max_ctx_len=p.max_ctx_len,
+                                 partition_size=256)
+        assert call.num_partitions == 9
+        call.launch(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            call.launch(s)
+        for i in range(4):
+            out.view(torch.int16).fill_(OUT_SENTINEL)
+            lse.view(torch.int32).fill_(LSE_SENTINEL)
+            g.replay()
+            torch.cuda.synchronize()
+            ob = out.view(torch.int16).cpu().numpy().view(np.uint16)
+            assert np.array_equal(ob, eager[0]), f"replay {i}"
+            assert np.array_equal(lse.cpu().numpy().view(np.uint32), eager[1].view(np.uint32)), f"replay {i}"
+
+
+def test_workspace_reused_across_shapes():
+    # one workspace, re-initialised for each new shape, serves different batches
+    a = _case([3000, 40, 900], hq=32, hkv=8, seed=67)
+    b = _case([100, 2000, 2000, 64, 5000, 1], hq=32, hkv=8, seed=71)
+    ws = torch.empty(64 << 20, dtype=torch.uint8, device=DEV)
+    for prob in (a, b, a):
+        q, k, v = prob.layer(0)
+        t = inputs.to_device(prob, q, k, v, DEV)
+        out = torch.zeros(q.shape, dtype=torch.bfloat16, device=DEV)
+        lse = torch.zeros(q.shape[:2], dtype=torch.float32, device=DEV)
+        shape = pk.make_shape(prob.num_seqs, prob.total_q, 32, 8, prob.max_blocks_per_seq, 1,
+                              prob.max_ctx_len, prob.num_blocks, 128)
+        pk.workspace_init(shape, ws)
+        pk.attend(t["q"], t["k"], t["v"], t["block_table"], t["ctx_lens"], t["q_lens"], float(prob.scale),
+                  out, lse, max_q_len=1, max_ctx_len=prob.max_ctx_len, partition_size=128, workspace=ws)
+        torch.cuda.synchronize()
+        ob = out.view(torch.int16).cpu().numpy().view(np.uint16)
+        ref = run_oracle(prob)
+        compare(prob, (ob, lse.cpu().numpy()), ref, label=f"reuse {prob.ctx_lens.tolist()}")
+
+
 def test_lse_optional():
     p = _case([37, 100], seed=41)
     ob, lb = run_gpu(p, with_lse=False, partition_size=32)
