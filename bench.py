@@ -46,7 +46,65 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-chunk", action="store_true", help="skip the secondary chunk-path measurement")
     ap.add_argument("--cpu-budget-s", type=float, default=25.0)
+    ap.add_argument("--mode", choices=["bench", "copy"], default="bench",
+                    help="copy: time a plain 1 GiB device copy (counter calibration for rocprofv3)")
+    ap.add_argument("--quick", action="store_true", help="skip the eager and per-launch re-timings")
     return ap.parse_args()
+
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def kernel_source_hash() -> str:
+    """Hash of the HIP sources; counter-derived traffic is only reported for
+    the exact sources it was measured on."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "paged_kv_cache_attend_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str, kernel: str):
+    """(fetch, write) HBM bytes per launch from the committed counter summary,
+    or None if it is missing or was taken on other sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_hash") != kernel_source_hash():
+        return None
+    ent = rec.get("workloads", {}).get(workload, {}).get(kernel)
+    if not ent:
+        return None
+    return ent["fetch_bytes_per_launch"], ent["write_bytes_per_launch"]
+
+
+def copy_mode(steps: int):
+    """A plain 1 GiB device-to-device copy, for calibrating FETCH_SIZE /
+    WRITE_SIZE against a known byte count."""
+    import torch
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    print(json.dumps({"mode": "copy", "bytes_read_per_copy": n, "bytes_written_per_copy": n, "ms_per_copy": ms,
+                      "copy_gbs_read_plus_write": 2 * n / (ms * 1e-3) / 1e9}), flush=True)
 
 
 def build_decode(problem, dev, want_oracle: bool, cpu_budget_s: float):
@@ -167,7 +225,7 @@ def parity(problem, outs, lses, ref):
             "pass": bool(emax <= 1e-2 and emean <= 1e-3 and lmax <= 1e-3)}
 
 
-def chunk_secondary(dev, steps):
+def chunk_secondary(dev, steps, launch="graph"):
     """TFLOP/s of the chunked-denoising workload (4 x 24 heads x 256 rows x 1024 keys)."""
     import torch
     import paged_kv_cache_attend_amd as pk
@@ -184,9 +242,9 @@ def chunk_secondary(dev, steps):
                                       max_ctx_len=p.max_ctx_len))
     flops = 4 * int((p.q_lens.astype(np.int64) * p.ctx_lens).sum()) * p.num_q_heads * p.head_dim
     reps = max(steps, 50)
-    cold_ms, _, _ = time_pass(sets, reps // 16 + 1, 2, "graph")
+    cold_ms, _, _ = time_pass(sets, reps // 16 + 1, 2, launch)
     cold_ms /= len(sets)
-    warm_ms, _, _ = time_pass(sets[:1] * 16, reps // 16 + 1, 2, "graph")
+    warm_ms, _, _ = time_pass(sets[:1] * 16, reps // 16 + 1, 2, launch)
     warm_ms /= 16
     return {"workload": "chunked_denoise", "flop_per_call": flops,
             "tflops_cold": flops / (cold_ms * 1e-3) / 1e12, "tflops_warm": flops / (warm_ms * 1e-3) / 1e12,
@@ -200,6 +258,9 @@ def main():
         print(f"bench.py runs on exactly one GPU (asked for {args.gpus}); multi-GPU runs are not part "
               "of this build", file=sys.stderr)
         sys.exit(2)
+    if args.mode == "copy":
+        copy_mode(args.steps)
+        return
     import torch
     from paged_kv_cache_attend_amd import inputs
     import paged_kv_cache_attend_amd as pk
@@ -222,9 +283,9 @@ def main():
     decode = problem.max_q_len == 1
     ms, wall_ms, _ = time_pass(calls, args.steps, args.warmup, args.launch)
     eager_ms = None
-    if args.launch == "graph":
+    if args.launch == "graph" and not args.quick:
         eager_ms, _, _ = time_pass(calls, max(10, args.steps // 4), 2, "eager")
-    per_call_ms = time_kernel_launches(calls, max(5, args.steps // 10))
+    per_call_ms = ms / len(calls) if args.quick else time_kernel_launches(calls, max(5, args.steps // 10))
 
     kv_read = problem.kv_bytes_read() * problem.num_layers
     kv_unique = problem.kv_bytes_unique() * problem.num_layers
@@ -236,16 +297,26 @@ def main():
         unit = "GB/s"
         per_launch_bytes = headline_bytes / len(calls)
         achieved = per_launch_bytes / (per_call_ms * 1e-3) / 1e9
+        kname = f"decode_kernel<{problem.num_q_heads // problem.num_kv_heads}>"
+        tr = measured_traffic(problem.name, kname)
         roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                    "kernel": "pa_attend (split-KV decode + LSE combine) per layer",
-                    "avg_launch_us": per_call_ms * 1e3}
+                    "frac": achieved / HBM_PEAK_GBS,
+                    "traffic": None if tr is None else tr[0] + tr[1],
+                    "traffic_fetch": None if tr is None else tr[0],
+                    "traffic_write": None if tr is None else tr[1],
+                    "algorithmic_bytes_per_launch": per_launch_bytes,
+                    "kernel": kname + " (split-KV decode with the LSE merge fused), one launch per layer",
+                    "avg_launch_us": per_call_ms * 1e3,
+                    "timing": "HIP events around back-to-back launches on the launch stream"}
     else:
         value = flops / (ms * 1e-3) / 1e12
         unit = "TFLOP/s"
         achieved = (flops / len(calls)) / (per_call_ms * 1e-3) / 1e12
+        tr = measured_traffic(problem.name, "chunk_kernel")
         roofline = {"bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                    "frac": achieved / BF16_PEAK_TFLOPS, "traffic": None, "kernel": "chunk_kernel",
+                    "frac": achieved / BF16_PEAK_TFLOPS,
+                    "traffic": None if tr is None else tr[0] + tr[1],
+                    "algorithmic_flops_per_launch": flops / len(calls), "kernel": "chunk_kernel",
                     "avg_launch_us": per_call_ms * 1e3}
 
     par = parity(problem, outs, lses, ref) if ref else None
@@ -263,7 +334,7 @@ def main():
 
     secondary = None
     if decode and not args.no_chunk:
-        secondary = chunk_secondary(dev, args.steps)
+        secondary = chunk_secondary(dev, args.steps, args.launch)
 
     line = {
         "metric": METRIC,
@@ -302,6 +373,7 @@ def main():
         "cpu_baseline": cpu,
         "parity": par,
         "chunk": secondary,
+        "source_hash": kernel_source_hash(),
     }
     print(json.dumps(line), flush=True)
 
