@@ -8,17 +8,21 @@
 // section 8.2.3).  Both products are dense contractions, so they run on the
 // matrix cores: v_mfma_f32_32x32x16_bf16 with fp32 accumulation.
 //
-// Workgroup: 4 waves, 128 query rows (32 per wave) of one (slot, query head).
-// Loop over 32-key tiles (two 16-token pages):
-//   1. all 256 threads load the tile's K and V rows through the block table
-//      (16-byte loads, one key row per 8 / 16 threads) into registers one tile
-//      ahead, then store them to LDS: K row-major with XOR-swizzled 16-byte
-//      chunks, V transposed (dim-major, rows padded to 72 bytes so the
-//      transposed reads are conflict free);
+// Workgroup: 8 waves over 128 query rows of one (slot, query head).  Wave w
+// takes rows 32 (w % 4) .. +32 and one half of the keys (w / 4); the two
+// halves merge through LDS at the end.  Each half walks its keys in 32-key
+// tiles (two 16-token pages):
+//   1. its 256 threads load a tile's K and V rows through the block table
+//      (page ids by scalar loads; 16-byte loads, one key row per 8 / 16
+//      threads) two tiles ahead into a two-deep register ring, and store each
+//      tile to a double-buffered LDS area: K row-major with XOR-swizzled
+//      16-byte chunks, V transposed (dim-major, rows padded to 72 bytes so
+//      the transposed reads are conflict free).  One barrier per tile;
 //   2. each wave computes S^T = K Q^T (32 keys x 32 rows, 8 MFMAs over the 128
 //      dims).  In the MFMA output layout a lane holds 16 keys of ONE query row,
-//      so the row max and row sum of the online softmax are mostly in-lane;
-//      the other 16 keys of the row sit in lane + 32;
+//      so the row max and sum of the online softmax are mostly in-lane; the
+//      other 16 keys of the row sit in lane + 32.  The accumulators are only
+//      rescaled when the row max grows by more than 2^8;
 //   3. probabilities are rounded to bf16 and used directly, from registers, as
 //      the B operand of O^T += V^T P^T (4 x 32 dims, 2 key steps, 8 MFMAs); the
 //      V^T A operand is read from the transposed LDS tile with the same key
@@ -31,24 +35,35 @@ namespace pa {
 
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;
+constexpr int kHalfThreads = 256;
 constexpr int kTileKeys = 32;
-constexpr int kKRowBytes = kHeadDim * 2;         // 256
-constexpr int kVtRowBytes = kTileKeys * 2 + 8;   // 72: padded dim-major row
-constexpr int kKBytes = kTileKeys * kKRowBytes;  // 8 KiB
-constexpr int kVtBytes = kHeadDim * kVtRowBytes; // 9 KiB
+constexpr int kKRowBytes = kHeadDim * 2;          // 256
+constexpr int kVtRowBytes = kTileKeys * 2 + 8;    // 72: padded dim-major row
+constexpr int kKBytes = kTileKeys * kKRowBytes;   // 8 KiB
+constexpr int kVtBytes = kHeadDim * kVtRowBytes;  // 9 KiB
+constexpr int kStageBytes = kKBytes + kVtBytes;   // one tile
+constexpr float kRescaleSlack = 8.0f;             // log2 units
 
-static_assert(kChunkRows == 4 * 32, "four waves of 32 rows");
+static_assert(kChunkRows == 4 * 32, "four row groups of 32 rows");
 
-__device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& u) { return __builtin_bit_cast(bf16x8_t, u); }
+__device__ __forceinline__ bf16x8_t as_bf16x8(const u32x4_t& u) { return __builtin_bit_cast(bf16x8_t, u); }
 
-__global__ __launch_bounds__(kThreads, 2) void chunk_kernel(ChunkParams p) {
-  __shared__ __attribute__((aligned(16))) uint8_t s_k[kKBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t s_vt[kVtBytes];
+struct TileRegs {
+  u32x4_t k[2];  // key lk_key, chunks lk_c, lk_c + 1
+  u32x4_t v[2];  // keys 2 lv_kp, 2 lv_kp + 1, chunk lv_c
+};
+
+__global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkParams p) {
+  // [key half][stage][K tile | V^T tile]; reused for the final merge.
+  __shared__ __attribute__((aligned(16))) uint8_t s_buf[2][2][kStageBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rg = wave & 3;    // row group
+  const int kh = wave >> 2;   // key half
+  const int lt = tid & (kHalfThreads - 1);  // loader id within the half
   const int col = lane & 31;  // query row within the wave / MFMA column
   const int hh = lane >> 5;   // lane half
 
@@ -59,82 +74,85 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_kernel(ChunkParams p) {
   const int seq = sh / p.num_q_heads;
   const int g = h / (p.num_q_heads / p.num_kv_heads);
 
-  const int m = p.q_lens[seq];
-  const int n = p.ctx_lens[seq];
+  const int m = scalar_load_i32(p.q_lens, seq);
+  const int n = scalar_load_i32(p.ctx_lens, seq);
   if (m <= 0 || n <= 0 || qt * kChunkRows >= m) return;
-  const int q_row0 = q_row_offset(p.q_lens, seq, lane);
-  const int row = qt * kChunkRows + wave * 32 + col;  // row within the slot
+  int q_row0 = 0;
+  for (int i = 0; i < seq; ++i) q_row0 += scalar_load_i32(p.q_lens, i);
+  const int row = qt * kChunkRows + rg * 32 + col;  // row within the slot
   const bool row_live = row < m;
 
   // Q^T operand: lane (row, half) holds dims (hh*8 + s)*8 .. +8 for step s.
-  uint4 qf[8];
+  u32x4_t qf[8];
   {
-    const uint4* qp = reinterpret_cast<const uint4*>(p.q) +
-                      ((size_t)(q_row0 + row) * p.num_q_heads + h) * (kHeadDim / 8);
+    // Rows past m read row 0's query (their results are never written).
+    const u32x4_t* qp = reinterpret_cast<const u32x4_t*>(p.q) +
+                        ((size_t)(q_row0 + (row_live ? row : 0)) * p.num_q_heads + h) * (kHeadDim / 8);
 #pragma unroll
-    for (int s = 0; s < 8; ++s) qf[s] = row_live ? qp[hh * 8 + s] : make_uint4(0u, 0u, 0u, 0u);
+    for (int s = 0; s < 8; ++s) qf[s] = qp[hh * 8 + s];
   }
 
-  // Keys this workgroup needs.
+  // Keys this workgroup needs, split in two halves of whole tiles.
   int kv_end = n;
   if (p.causal) {
     const int last_row = min(m, (qt + 1) * kChunkRows) - 1;
     kv_end = min(n, n - m + last_row + 1);
   }
   const int ntiles = (kv_end + kTileKeys - 1) / kTileKeys;
+  const int T = (ntiles + 1) / 2;       // tiles per half (both halves loop T times)
+  const int tile0 = kh * T;             // this half's first tile
   const int my_limit = p.causal ? (n - m + row) : (n - 1);  // last visible key of this row
 
   const int32_t* bt = p.block_table + (size_t)seq * p.max_blocks;
-  const uint16_t* kpool = p.k;
-  const uint16_t* vpool = p.v;
+  const int last_page = (kv_end - 1) >> 4;
 
-  // Loader roles.  K: key kk = tid / 8, chunks 2*(tid%8), +1.  V: keys
-  // 2*(tid/16), +1, chunk tid % 16.
-  const int lk_key = tid >> 3;
-  const int lk_c = (tid & 7) * 2;
-  const int lv_kp = tid >> 4;
-  const int lv_c = tid & 15;
-  uint4 rk[2], rv[2];
-  auto load_tile = [&](int kt) {
-    const int base = kt * kTileKeys;
-    {
-      const int j = base + lk_key;
-      if (j < kv_end) {
-        const uint4* src = reinterpret_cast<const uint4*>(
-            kpool + cache_offset(bt[j >> 4], g, j & 15, lk_c * 8, p.num_kv_heads));
-        rk[0] = src[0];
-        rk[1] = src[1];
-      } else {
-        rk[0] = rk[1] = make_uint4(0u, 0u, 0u, 0u);
-      }
-    }
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const int j = base + 2 * lv_kp + e;
-      if (j < kv_end) {
-        rv[e] = *reinterpret_cast<const uint4*>(
-            vpool + cache_offset(bt[j >> 4], g, j & 15, lv_c * 8, p.num_kv_heads));
-      } else {
-        rv[e] = make_uint4(0u, 0u, 0u, 0u);
-      }
-    }
+  // Loader roles (within the half).  K: key lk_key, chunks lk_c, lk_c + 1.
+  // V: keys 2 lv_kp and 2 lv_kp + 1 (same page), chunk lv_c.
+  const int lk_key = lt >> 3;
+  const int lk_c = (lt & 7) * 2;
+  const int lv_kp = lt >> 4;
+  const int lv_c = lt & 15;
+
+  // Loads are unconditional (page ids clamped to the last live page, so every
+  // address is inside the pool) and keys past the end are zeroed when the
+  // tile is stored: the load counter then sees a fixed pattern and its waits
+  // leave the next tile in flight.
+  auto load_tile = [&](TileRegs& r, int it) {
+    const int t = tile0 + it;
+    const int32_t id0 = scalar_load_i32(bt, min(2 * t, last_page));
+    const int32_t id1 = scalar_load_i32(bt, min(2 * t + 1, last_page));
+    const int32_t idk = (lk_key >> 4) ? id1 : id0;
+    const int32_t idv = ((2 * lv_kp) >> 4) ? id1 : id0;
+    const u32x4_t* ks = reinterpret_cast<const u32x4_t*>(p.k + cache_offset(idk, g, lk_key & 15, lk_c * 8, p.num_kv_heads));
+    r.k[0] = ks[0];
+    r.k[1] = ks[1];
+    r.v[0] = *reinterpret_cast<const u32x4_t*>(p.v + cache_offset(idv, g, (2 * lv_kp) & 15, lv_c * 8, p.num_kv_heads));
+    r.v[1] = *reinterpret_cast<const u32x4_t*>(p.v + cache_offset(idv, g, (2 * lv_kp + 1) & 15, lv_c * 8, p.num_kv_heads));
   };
-  auto store_tile = [&]() {
+  auto store_tile = [&](const TileRegs& r, int stage, int it) {
+    uint8_t* sk = s_buf[kh][stage];
+    uint8_t* svt = sk + kKBytes;
+    const int base = (tile0 + it) * kTileKeys;
+    const bool tile_ok = it < T;
+    const bool k_ok = tile_ok && base + lk_key < kv_end;
+    const bool v0_ok = tile_ok && base + 2 * lv_kp < kv_end;
+    const bool v1_ok = tile_ok && base + 2 * lv_kp + 1 < kv_end;
+    const u32x4_t zero = u32x4_t{0u, 0u, 0u, 0u};
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
       const int c = lk_c + e;
-      *reinterpret_cast<uint4*>(s_k + lk_key * kKRowBytes + ((c ^ (lk_key & 15)) << 4)) = rk[e];
+      *reinterpret_cast<u32x4_t*>(sk + lk_key * kKRowBytes + ((c ^ (lk_key & 15)) << 4)) = k_ok ? r.k[e] : zero;
     }
-    const uint32_t a[4] = {rv[0].x, rv[0].y, rv[0].z, rv[0].w};
-    const uint32_t b[4] = {rv[1].x, rv[1].y, rv[1].z, rv[1].w};
+    const u32x4_t va = v0_ok ? r.v[0] : zero;
+    const u32x4_t vb = v1_ok ? r.v[1] : zero;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       // dims 8*lv_c + 2w (low halves) and + 2w + 1 (high halves)
-      const uint32_t lo = (a[w] & 0xffffu) | (b[w] << 16);
-      const uint32_t hi = (a[w] >> 16) | (b[w] & 0xffff0000u);
+      const uint32_t lo = __builtin_amdgcn_perm(vb[w], va[w], 0x05040100u);
+      const uint32_t hi = __builtin_amdgcn_perm(vb[w], va[w], 0x07060302u);
       const int d = lv_c * 8 + 2 * w;
-      *reinterpret_cast<uint32_t*>(s_vt + d * kVtRowBytes + lv_kp * 4) = lo;
-      *reinterpret_cast<uint32_t*>(s_vt + (d + 1) * kVtRowBytes + lv_kp * 4) = hi;
+      *reinterpret_cast<uint32_t*>(svt + d * kVtRowBytes + lv_kp * 4) = lo;
+      *reinterpret_cast<uint32_t*>(svt + (d + 1) * kVtRowBytes + lv_kp * 4) = hi;
     }
   };
 
@@ -143,16 +161,12 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_kernel(ChunkParams p) {
   for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
     for (int i = 0; i < 16; ++i) o[mb][i] = 0.f;
-  float m_run = -INFINITY;
-  float l_run = 0.f;
+  float m_run = -INFINITY;  // reference max of this row (log2 domain)
+  float l_run = 0.f;        // this lane's share of the row sum
 
-  if (ntiles > 0) load_tile(0);
-  for (int kt = 0; kt < ntiles; ++kt) {
-    __syncthreads();  // previous tile fully consumed
-    store_tile();
-    __syncthreads();
-    if (kt + 1 < ntiles) load_tile(kt + 1);
-
+  auto compute_tile = [&](int it, int stage) {
+    const uint8_t* sk = s_buf[kh][stage];
+    const uint8_t* svt = sk + kKBytes;
     // S^T = K Q^T: A = K rows (key = col), B = Q^T (row = col).
     f32x16_t st;
 #pragma unroll
@@ -160,12 +174,11 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_kernel(ChunkParams p) {
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
       const int c = hh * 8 + s;
-      const uint4 kf = *reinterpret_cast<const uint4*>(s_k + col * kKRowBytes + ((c ^ (col & 15)) << 4));
+      const u32x4_t kf = *reinterpret_cast<const u32x4_t*>(sk + col * kKRowBytes + ((c ^ (col & 15)) << 4));
       st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf), as_bf16x8(qf[s]), st, 0, 0, 0);
     }
-
     // Online softmax over this lane's 16 keys of its row (log2 domain).
-    const int kbase = kt * kTileKeys + 4 * hh;
+    const int kbase = (tile0 + it) * kTileKeys + 4 * hh;
     float sv[16];
     float mloc = -INFINITY;
 #pragma unroll
@@ -173,53 +186,129 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_kernel(ChunkParams p) {
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
         const int key = kbase + 8 * a + b;
-        const float x = (key <= my_limit) ? st[4 * a + b] * p.scale_log2 : -INFINITY;
+        const float x = (it < T && key <= my_limit) ? st[4 * a + b] * p.scale_log2 : -INFINITY;
         sv[4 * a + b] = x;
         mloc = fmaxf(mloc, x);
       }
     mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
-    const float m_new = fmaxf(m_run, mloc);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = fast_exp2(m_run - m_use);
+    const bool raise = mloc > m_run + kRescaleSlack;
+    if (__builtin_amdgcn_ballot_w64(raise) != 0) {
+      // A row with no visible key so far keeps m = -inf (its sums are 0);
+      // guard the difference so -inf - -inf never makes a NaN.
+      const float m_new = fmaxf(m_run, mloc);
+      const float alpha = fast_exp2(m_run - ((m_new == -INFINITY) ? 0.f : m_new));
+      l_run *= alpha;
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[mb][i] *= alpha;
+      m_run = m_new;
+    }
+    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
     float lsum = 0.f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       sv[i] = fast_exp2(sv[i] - m_use);
       lsum += sv[i];
     }
-    l_run = l_run * alpha + lsum;
-    m_run = m_new;
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) o[mb][i] *= alpha;
-
+    l_run += lsum;
     // P^T operand for key steps 0 and 1: keys 16ks + 4hh + 0..3, 16ks + 8 + 4hh + 0..3.
-    uint4 pf[2];
+    u32x4_t pf[2];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      pf[ks].x = pack_bf16x2(sv[8 * ks + 0], sv[8 * ks + 1]);
-      pf[ks].y = pack_bf16x2(sv[8 * ks + 2], sv[8 * ks + 3]);
-      pf[ks].z = pack_bf16x2(sv[8 * ks + 4], sv[8 * ks + 5]);
-      pf[ks].w = pack_bf16x2(sv[8 * ks + 6], sv[8 * ks + 7]);
+      pf[ks][0] = pack_bf16x2(sv[8 * ks + 0], sv[8 * ks + 1]);
+      pf[ks][1] = pack_bf16x2(sv[8 * ks + 2], sv[8 * ks + 3]);
+      pf[ks][2] = pack_bf16x2(sv[8 * ks + 4], sv[8 * ks + 5]);
+      pf[ks][3] = pack_bf16x2(sv[8 * ks + 6], sv[8 * ks + 7]);
     }
-
     // O^T += V^T P^T.
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
       const int d = mb * 32 + col;
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        const uint8_t* vrow = s_vt + d * kVtRowBytes + (16 * ks + 4 * hh) * 2;
-        const uint2 v0 = *reinterpret_cast<const uint2*>(vrow);
-        const uint2 v1 = *reinterpret_cast<const uint2*>(vrow + 16);
-        const uint4 vf = make_uint4(v0.x, v0.y, v1.x, v1.y);
+        const uint8_t* vrow = svt + d * kVtRowBytes + (16 * ks + 4 * hh) * 2;
+        const u32x2_t v0 = *reinterpret_cast<const u32x2_t*>(vrow);
+        const u32x2_t v1 = *reinterpret_cast<const u32x2_t*>(vrow + 16);
+        const u32x4_t vf = u32x4_t{v0[0], v0[1], v1[0], v1[1]};
         o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vf), as_bf16x8(pf[ks]), o[mb], 0, 0, 0);
       }
     }
+  };
+
+  // Pipeline: tiles it+1 and it+2 sit in registers while tile it is computed
+  // from LDS; LDS is double buffered, one barrier per tile.
+  TileRegs ra, rb;
+  if (T > 0) {
+    load_tile(ra, 0);
+    issue_order_barrier();
+    load_tile(rb, 1);
+    issue_order_barrier();
+    store_tile(ra, 0, 0);
+    issue_order_barrier();
+    load_tile(ra, 2);
+    issue_order_barrier();
+    __syncthreads();
+  }
+  // (issue_order_barrier keeps the compiler from moving a tile's loads ahead
+  // of the store that frees its registers, which would make the load
+  // counter's waits drain the ring.)
+  int it = 0;
+  for (; it + 1 < T; it += 2) {
+    // tile it is in stage 0; rb holds it+1, ra holds it+2
+    store_tile(rb, 1, it + 1);
+    issue_order_barrier();
+    load_tile(rb, it + 3);
+    issue_order_barrier();
+    compute_tile(it, 0);
+    __syncthreads();
+    // tile it+1 is in stage 1; ra holds it+2, rb holds it+3
+    store_tile(ra, 0, it + 2);
+    issue_order_barrier();
+    load_tile(ra, it + 4);
+    issue_order_barrier();
+    compute_tile(it + 1, 1);
+    __syncthreads();
+  }
+  if (it < T) {  // odd tile count: the last tile is in stage 0
+    compute_tile(it, 0);
+    __syncthreads();
   }
 
-  if (!row_live) return;
+  // Merge the key halves: half 1 hands (m, l, o) to half 0 through LDS, in
+  // four rounds of 16 accumulators (16 KiB per round, inside the tile area).
+  float* xbuf = reinterpret_cast<float*>(&s_buf[0][0][0]);  // [rg][18][64] floats
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) {
+    if (kh == 1) {
+      float* dst = xbuf + (size_t)rg * 18 * 64;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) dst[i * 64 + lane] = o[mb][i];
+      if (mb == 0) {
+        dst[16 * 64 + lane] = m_run;
+        dst[17 * 64 + lane] = l_run;
+      }
+    }
+    __syncthreads();
+    if (kh == 0) {
+      const float* src = xbuf + (size_t)rg * 18 * 64;
+      const float m1 = src[16 * 64 + lane];
+      const float l1 = src[17 * 64 + lane];
+      const float M = fmaxf(m_run, m1);
+      const float Mu = (M == -INFINITY) ? 0.f : M;
+      const float s0 = fast_exp2(m_run - Mu);
+      const float s1 = fast_exp2(m1 - Mu);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[mb][i] = o[mb][i] * s0 + src[i * 64 + lane] * s1;
+      if (mb == 3) {
+        l_run = l_run * s0 + l1 * s1;
+        m_run = M;
+      }
+    }
+    __syncthreads();
+  }
+  if (kh == 1 || !row_live) return;
+
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   const float inv = 1.f / l_tot;
   uint16_t* orow = p.out + ((size_t)(q_row0 + row) * p.num_q_heads + h) * kHeadDim;
