@@ -52,7 +52,7 @@ namespace pa {
 
 namespace {
 
-constexpr int kWaves = 4;
+constexpr int kWaves = kDecodeWaves;
 constexpr int kTileBytes = kBlockSize * kHeadDim * 2;  // 4 KiB
 constexpr int kTileVec = kTileBytes / 16;              // uint4 per tile
 constexpr float kRescaleSlack = 8.0f;                  // log2 units
@@ -68,9 +68,9 @@ __device__ __forceinline__ void issue_page(Page& b, const u32x4_t* __restrict__ 
                                            int num_kv_heads, int lane) {
   const size_t base = tile_index(phys, g, num_kv_heads) * kTileVec + lane;
 #pragma unroll
-  for (int k = 0; k < 4; ++k) b.k[k] = kpool[base + k * 64];
+  for (int k = 0; k < 4; ++k) b.k[k] = stream_load(kpool + base + k * 64);
 #pragma unroll
-  for (int k = 0; k < 4; ++k) b.v[k] = vpool[base + k * 64];
+  for (int k = 0; k < 4; ++k) b.v[k] = stream_load(vpool + base + k * 64);
 }
 
 template <int G>
@@ -193,7 +193,7 @@ __device__ __forceinline__ int q_row_scalar(const int32_t* q_lens, int seq) {
 }
 
 template <int G>
-__global__ __launch_bounds__(kDecodeThreads, 2) void decode_kernel(DecodeParams p) {
+__global__ __launch_bounds__(kDecodeThreads, kDecodeWGsPerCU) void decode_kernel(DecodeParams p) {
   static_assert(G == 1 || G == 2 || G == 4, "group size");
   __shared__ __attribute__((aligned(16))) uint8_t s_k[kWaves][kTileBytes];
   __shared__ __attribute__((aligned(16))) uint8_t s_q[G][kHeadDim * 2];

@@ -12,7 +12,14 @@ constexpr int kHeadDim = 128;    // only head size built
 constexpr int kBlockSize = 16;   // tokens per KV block
 constexpr int kNumCUs = 256;     // MI355X compute units (8 XCDs x 32)
 constexpr int kNumXCDs = 8;
-constexpr int kDecodeWGsPerCU = 2;  // decode workgroups resident per CU (register bound)
+#ifndef PA_STREAM_NT
+#define PA_STREAM_NT 1
+#endif
+#ifndef PA_DECODE_WAVES
+#define PA_DECODE_WAVES 4
+#endif
+constexpr int kDecodeWaves = PA_DECODE_WAVES;          // waves per decode workgroup
+constexpr int kDecodeWGsPerCU = 8 / kDecodeWaves;      // resident per CU (2 waves per SIMD)
 
 // Split-KV decode: one workgroup per (KV head, slot, partition).
 struct DecodeParams {
@@ -93,7 +100,7 @@ struct ValidateParams {
 
 // Decode kernels exist for these query-per-KV head group sizes.
 bool decode_supports_group(int group);
-constexpr int kDecodeThreads = 256;
+constexpr int kDecodeThreads = 64 * kDecodeWaves;
 hipError_t launch_decode(const DecodeParams& p, int group, unsigned grid, hipStream_t s);
 hipError_t launch_zero_i32(int32_t* x, size_t n, hipStream_t s);
 
