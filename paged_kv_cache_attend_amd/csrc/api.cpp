@@ -60,20 +60,43 @@ pa_status check_shape(const pa_shape* s) {
   return PA_OK;
 }
 
-// Partition size when the caller leaves it to the library.  The decode grid
-// should fill the chip in one round of resident workgroups (kDecodeWGsPerCU
-// per CU): every (slot, KV head) pair is split into as many equal partitions
-// as fit, so all workgroups start together and finish together.  A partition
-// keeps at least two pages per wave to amortise its prologue and merge.
+// Partition size when the caller leaves it to the library.  A decode
+// workgroup (four waves, three pages in flight each) streams at close to its
+// CU's share of HBM bandwidth, so what matters is how evenly the grid fills
+// the CUs and how much fixed cost (start, merge) each partition carries:
+//  - with at most two resident workgroups per CU for the whole grid, pick
+//    the partition count whose grid fills its last round of CUs best, then
+//    prefer partitions of at least 64 pages, then more partitions;
+//  - with more (slot, KV head) pairs than that, the grid is several rounds
+//    anyway; long contexts are cut into partitions of at most 128 pages so
+//    that a batch's longest requests do not finish last on their own.
+// No partition is smaller than 8 pages (two per wave).
 int auto_part_pages(const pa_shape* s, int max_pages) {
+  constexpr int kMinPages = 8, kGoodPages = 64, kLongPages = 128;
   const long long pairs = (long long)s->num_seqs * s->num_kv_heads;
   const long long resident = (long long)kDecodeWGsPerCU * kNumCUs;
-  long long parts = resident / (pairs > 0 ? pairs : 1);
-  if (parts < 1) parts = 1;
-  if (parts > max_pages) parts = max_pages;
-  int pp = ceil_div(max_pages, (int)parts);
-  if (pp < 8) pp = 8;
-  return pp;
+  if (pairs <= 0 || max_pages <= kMinPages) return kMinPages;
+  if (pairs > resident) return max(kMinPages, ceil_div(max_pages, ceil_div(max_pages, kLongPages)));
+  int best_pp = max_pages;
+  double best_fill = -1.0;
+  bool best_good = false;
+  for (long long parts = 1; parts * pairs <= resident && parts <= max_pages; ++parts) {
+    const int pp = ceil_div(max_pages, (int)parts);
+    if (pp < kMinPages) break;
+    if (ceil_div(max_pages, pp) != parts) continue;  // same grid as a smaller count
+    const double rounds = (double)(pairs * parts) / kNumCUs;
+    const double fill = rounds / std::ceil(rounds);
+    const bool good = pp >= kGoodPages;
+    // Ties in fill (within 1%) go to a good size, then to more partitions.
+    const bool better = fill > best_fill + 0.01 ||
+                        (fill > best_fill - 0.01 && (good > best_good || (good == best_good)));
+    if (better) {
+      best_fill = max(best_fill, fill);
+      best_good = good;
+      best_pp = pp;
+    }
+  }
+  return best_pp;
 }
 
 pa_status make_plan(const pa_shape* s, Plan* plan) {

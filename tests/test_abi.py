@@ -139,12 +139,26 @@ def test_single_partition_needs_no_workspace(lib):
 
 
 def test_auto_partitions_cover_the_chip(lib):
-    # 16 slots x 8 KV heads x 2303 keys: the automatic split must give the
-    # decode grid several workgroups per CU.
+    # 16 slots x 8 KV heads x 2303 keys: two 72-page partitions per pair fill
+    # the 256 CUs exactly once (four 36-page ones would too, with more fixed
+    # cost per page).
     s = _shape(num_seqs=16, total_q=16, max_blocks_per_seq=144, max_ctx_len=2303, num_blocks=2592)
     ws, parts = pk.plan(s)
-    assert parts > 1 and 16 * 8 * parts >= 512
+    assert parts == 2
     assert ws == _ws_bytes(16, 8, parts, 16 * 32)
+
+
+@pytest.mark.parametrize("num_seqs,ctx,parts", [
+    (10, 8447, 6),    # 80 pairs: 480 workgroups of 88 pages (3 x 176 fills the CUs as well)
+    (68, 8355, 5),    # 544 pairs, more than resident: long contexts cut to <= 128 pages
+    (1, 32768, 32),   # one request: 32 x 64 pages, one workgroup per CU
+    (2, 100, 1),      # 7 pages: never below 8 pages per partition
+])
+def test_auto_partition_counts(lib, num_seqs, ctx, parts):
+    mb = (ctx + 15) // 16
+    s = _shape(num_seqs=num_seqs, total_q=num_seqs, max_blocks_per_seq=mb, max_ctx_len=ctx,
+               num_blocks=mb * num_seqs)
+    assert pk.plan(s)[1] == parts
 
 
 def test_chunk_path_needs_no_workspace(lib):

@@ -120,7 +120,7 @@ def test_repeat_calls_are_deterministic():
 
 def test_graph_replay_matches_eager():
     # capture one split call in a graph; replay it several times with eager work
-    # in between and check every replay (the counters must come back to zero)
+    # in between and check every replay (the workspace must stay consistent)
     p = _case([2303, 700, 0, 1500], hq=32, hkv=8, seed=61)
     q, k, v = p.layer(0)
     eager = run_gpu(p, q=q, k=k, v=v, partition_size=256)
@@ -146,6 +146,38 @@ def test_graph_replay_matches_eager():
             ob = out.view(torch.int16).cpu().numpy().view(np.uint16)
             assert np.array_equal(ob, eager[0]), f"replay {i}"
             assert np.array_equal(lse.cpu().numpy().view(np.uint32), eager[1].view(np.uint32)), f"replay {i}"
+
+
+def test_back_to_back_calls_never_read_stale_partials():
+    # Two batches of one shape share a workspace and alternate: every call's
+    # merge must use that call's partials only, never the previous call's.
+    ctx = [2303, 700, 1500, 64]
+    a = _case(ctx, hq=32, hkv=8, seed=73)
+    b = _case(ctx, hq=32, hkv=8, seed=79)
+    ref = {}
+    dev = {}
+    for name, prob in (("a", a), ("b", b)):
+        q, k, v = prob.layer(0)
+        ref[name] = run_gpu(prob, q=q, k=k, v=v, partition_size=128)
+        dev[name] = inputs.to_device(prob, q, k, v, DEV)
+    shape = pk.make_shape(a.num_seqs, a.total_q, 32, 8, a.max_blocks_per_seq, 1, a.max_ctx_len,
+                          a.num_blocks, 128)
+    ws = torch.empty(pk.workspace_size(shape), dtype=torch.uint8, device=DEV)
+    pk.workspace_init(shape, ws)
+    outs = []
+    for i in range(12):
+        name = "ab"[i % 2]
+        t = dev[name]
+        out = torch.full(t["q"].shape, OUT_SENTINEL, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+        lse = torch.full(t["q"].shape[:2], LSE_SENTINEL, dtype=torch.int32, device=DEV).view(torch.float32)
+        pk.attend(t["q"], t["k"], t["v"], t["block_table"], t["ctx_lens"], t["q_lens"], float(a.scale),
+                  out, lse, max_q_len=1, max_ctx_len=a.max_ctx_len, partition_size=128, workspace=ws)
+        outs.append((name, out, lse))
+    torch.cuda.synchronize()
+    for i, (name, out, lse) in enumerate(outs):
+        ob = out.view(torch.int16).cpu().numpy().view(np.uint16)
+        assert np.array_equal(ob, ref[name][0]), f"call {i} ({name})"
+        assert np.array_equal(lse.cpu().numpy().view(np.uint32), ref[name][1].view(np.uint32)), f"call {i}"
 
 
 def test_workspace_reused_across_shapes():
