@@ -45,6 +45,7 @@ def parse():
     ap.add_argument("--launch", choices=["graph", "eager"], default="graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-chunk", action="store_true", help="skip the secondary chunk-path measurement")
+    ap.add_argument("--no-append", action="store_true", help="skip the secondary K/V-append measurement")
     ap.add_argument("--cpu-budget-s", type=float, default=25.0)
     ap.add_argument("--mode", choices=["bench", "copy"], default="bench",
                     help="copy: time a plain 1 GiB device copy (counter calibration for rocprofv3)")
@@ -252,6 +253,49 @@ def chunk_secondary(dev, steps, launch="graph"):
             "frac_of_bf16_peak_warm": flops / (warm_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS}
 
 
+class _WriteCall:
+    """One pa_write_kv call with fixed tensors, launchable like PreparedAttend."""
+
+    def __init__(self, k_new, v_new, table, ctx, q_lens, k_cache, v_cache, max_q_len):
+        self.args = (k_new, v_new, table, ctx, q_lens, k_cache, v_cache)
+        self.max_q_len = max_q_len
+
+    def launch(self, stream):
+        import paged_kv_cache_attend_amd as pk
+        pk.write_kv(*self.args, max_q_len=self.max_q_len, stream=stream)
+
+
+def append_secondary(dev, steps, launch="graph"):
+    """pa_write_kv on the Qwen3-8B-shaped batch (16 slots x 2303 tokens, 8 KV
+    heads): a whole-prompt append (every token new; bytes = new rows read +
+    cache rows written) and a one-token-per-slot decode append (latency)."""
+    import torch
+    from paged_kv_cache_attend_amd import inputs
+    p = inputs.qwen3_short_decode(num_layers=1)
+    hkv, d = p.num_kv_heads, p.head_dim
+    rows = int(p.ctx_lens.sum())
+    ss = np.random.SeedSequence(inputs.SEED_BASE + 900)
+    kn = inputs.bits_to_torch_bf16(inputs.normal_bf16(inputs.child_seed(ss, 0), (rows, hkv, d)), dev)
+    vn = inputs.bits_to_torch_bf16(inputs.normal_bf16(inputs.child_seed(ss, 1), (rows, hkv, d)), dev)
+    kc = torch.zeros((p.num_blocks, hkv, p.block_size, d), dtype=torch.bfloat16, device=dev)
+    vc = torch.zeros_like(kc)
+    table = torch.from_numpy(p.block_table.astype(np.int32)).to(dev)
+    ctx = torch.from_numpy(p.ctx_lens.astype(np.int32)).to(dev)
+    ones = torch.ones_like(ctx)
+    prefill = _WriteCall(kn, vn, table, ctx, ctx, kc, vc, int(p.ctx_lens.max()))
+    decode = _WriteCall(kn[:p.num_seqs], vn[:p.num_seqs], table, ctx, ones, kc, vc, 1)
+    reps = max(steps // 4, 20)
+    pre_ms, _, _ = time_pass([prefill], reps, 2, launch)
+    dec_ms, _, _ = time_pass([decode] * 36, reps, 2, launch)
+    moved = 4 * rows * hkv * d * 2  # K and V: read the new row, write the page slot
+    return {"workload": "qwen3_8b_short_decode prompt and decode appends (one layer per call)",
+            "prompt_rows": rows, "prompt_bytes_moved": moved, "prompt_us": pre_ms * 1e3,
+            "prompt_gbs": moved / (pre_ms * 1e-3) / 1e9,
+            "prompt_frac_of_hbm_peak": moved / (pre_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "decode_append_us_per_layer": dec_ms * 1e3 / 36,
+            "parity": "bit-exact against the oracle scatter in the GPU tests"}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -335,6 +379,9 @@ def main():
     secondary = None
     if decode and not args.no_chunk:
         secondary = chunk_secondary(dev, args.steps, args.launch)
+    append = None
+    if decode and not args.no_append:
+        append = append_secondary(dev, args.steps, args.launch)
 
     line = {
         "metric": METRIC,
@@ -373,6 +420,7 @@ def main():
         "cpu_baseline": cpu,
         "parity": par,
         "chunk": secondary,
+        "append": append,
         "source_hash": kernel_source_hash(),
     }
     print(json.dumps(line), flush=True)

@@ -45,12 +45,14 @@
  *   lse          fp32  [total_q][num_q_heads]  (may be NULL)
  *
  * Conventions
- *   - Every call only enqueues work on `stream` (a hipStream_t; NULL is the
- *     null stream) and returns; results are ordered on that stream.  No call
- *     allocates memory, synchronises, or reads device memory on the host, so
- *     calls may be captured in a HIP graph (cf. the Photon page, section 3:
- *     fixed buffers, no runtime allocation).
- *   - The library keeps no state and is re-entrant.  The caller keeps every
+ *   - Every device call only enqueues work on `stream` (a hipStream_t; NULL
+ *     is the null stream) and returns; results are ordered on that stream.
+ *     No device call allocates memory, synchronises, or reads device memory
+ *     on the host, so calls may be captured in a HIP graph (cf. the Photon
+ *     page, section 3: fixed buffers, no runtime allocation).
+ *   - Apart from block pools (host objects the caller creates, owns and
+ *     destroys; see pa_pool_create), the library keeps no state, and every
+ *     device call is re-entrant.  The caller keeps every
  *     buffer alive and unmodified (and does not reuse `workspace`) until the
  *     stream has passed the call -- the "free only after the accelerator has
  *     stopped reading" rule of section 8.3.2.
@@ -76,7 +78,8 @@ typedef enum pa_status {
   PA_ERR_BAD_SHAPE = 2,           /* inconsistent or out-of-range sizes */
   PA_ERR_UNSUPPORTED = 3,         /* valid but not implemented (e.g. head_dim != 128) */
   PA_ERR_WORKSPACE_TOO_SMALL = 4, /* workspace_bytes < pa_workspace_size() */
-  PA_ERR_LAUNCH = 5               /* the HIP runtime rejected a kernel launch */
+  PA_ERR_LAUNCH = 5,              /* the HIP runtime rejected a kernel launch */
+  PA_ERR_OUT_OF_BLOCKS = 6        /* the block pool has too few free blocks; nothing changed */
 } pa_status;
 
 /* Request rows may only see keys up to their own position (chunked prefill,
@@ -171,6 +174,109 @@ pa_status pa_gather_kv(const pa_shape* shape, const void* cache,
 pa_status pa_validate(const pa_shape* shape, const int32_t* block_table,
                       const int32_t* ctx_lens, const int32_t* q_lens,
                       int32_t* error_word, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Appending new K/V, and the block pool that hands out pages
+ * ------------------------------------------------------------------------
+ * The chapter's sections 8.3.1 (Fig. 8-10) and 8.3.2 (Figs. 8-13 to 8-15)
+ * describe the life of a page: a growing sequence takes a block from the
+ * free pool when it needs a new one and records it in its block table;
+ * tables may share blocks (a common prefix), each table entry being one
+ * reference; a branch that writes into a shared block that is only partly
+ * filled first takes a private copy of it; and a block goes back to the free
+ * pool only when its last reference is dropped and the accelerator no longer
+ * reads it (Fig. 8-14, and Fig. 8-16 for cancellation).
+ */
+
+/* Write the new tokens' K and V rows into their pages, the step that must
+ * precede pa_attend with the same arguments.  For every slot r with
+ * n = ctx_lens[r] > 0 and m = q_lens[r] > 0, new row i < m (global row
+ * q_off[r] + i, as for pa_attend) is position j = n - m + i:
+ *     k_cache[block_table[r][j / 16]][g][j % 16][:] = k_new[row][g][:]
+ * and likewise V, for every KV head g.
+ *   k_new, v_new  bf16 [total_q][num_kv_heads][head_dim]
+ *   k_cache, v_cache as for pa_attend (written in place)
+ * Uses num_seqs, total_q, num_kv_heads, head_dim, block_size,
+ * max_blocks_per_seq, max_q_len and num_blocks of `shape` (num_q_heads only
+ * has to be a valid multiple).  A position outside the block table or a
+ * table entry outside [0, num_blocks) is skipped rather than written.  Only
+ * enqueues work on `stream`.  Errors: PA_ERR_NULL_ARG, PA_ERR_BAD_SHAPE,
+ * PA_ERR_UNSUPPORTED, PA_ERR_LAUNCH. */
+pa_status pa_write_kv(const pa_shape* shape, const void* k_new, const void* v_new,
+                      const int32_t* block_table, const int32_t* ctx_lens, const int32_t* q_lens,
+                      void* k_cache, void* v_cache, void* stream);
+
+/* Copy whole blocks (every KV head, K and V) src[i] -> dst[i] for
+ * i < num_copies: the copy half of copy-on-write (section 8.3.2, Fig. 8-15).
+ * src, dst: device int32 [num_copies]; no dst may equal any src or another
+ * dst.  Entries outside [0, num_blocks) are skipped.  Caches as for
+ * pa_attend, head_dim 128 and block_size 16. */
+pa_status pa_copy_blocks(int32_t num_copies, const int32_t* src, const int32_t* dst,
+                         int32_t num_kv_heads, int64_t num_blocks, void* k_cache, void* v_cache,
+                         void* stream);
+
+/* Host-side block pool: free pool, per-slot block tables, reference counts,
+ * copy-on-write and fenced release.  Plain host memory, no device calls; not
+ * thread-safe (the caller's scheduler owns it).  Blocks are handed out from
+ * a free stack; which id a request gets is unspecified. */
+typedef struct pa_pool pa_pool;
+
+typedef struct pa_pool_stats {
+  int32_t free_blocks;    /* ready to hand out */
+  int32_t pending_blocks; /* released, waiting for their fence to retire */
+  int32_t used_blocks;    /* referenced by at least one slot */
+  int32_t reserved;
+  int64_t references;     /* block-table entries over all slots */
+} pa_pool_stats;
+
+/* A pool of num_blocks blocks of block_size tokens (any positive size; the
+ * attention kernels use 16) serving num_slots slots of at most
+ * max_blocks_per_seq blocks each.  Errors: PA_ERR_NULL_ARG, PA_ERR_BAD_SHAPE. */
+pa_status pa_pool_create(int32_t num_blocks, int32_t block_size, int32_t num_slots,
+                         int32_t max_blocks_per_seq, pa_pool** pool);
+void pa_pool_destroy(pa_pool* pool);
+
+/* Make room for num_tokens more tokens in `slot` (section 8.3.1): new blocks
+ * come from the free pool.  If the slot's last block is partly filled and
+ * shared with another slot, the slot first gets a private copy of it
+ * (section 8.3.2): *num_copies is then 1 and (copy_src[0], copy_dst[0])
+ * names the copy the caller must make with pa_copy_blocks, on every layer's
+ * caches, before writing into it; otherwise *num_copies is 0.  Returns
+ * PA_ERR_OUT_OF_BLOCKS, changing nothing, when the free pool is too small,
+ * and PA_ERR_BAD_SHAPE for a bad slot, a negative count or a sequence longer
+ * than max_blocks_per_seq blocks. */
+pa_status pa_pool_append(pa_pool* pool, int32_t slot, int32_t num_tokens, int32_t* copy_src,
+                         int32_t* copy_dst, int32_t* num_copies);
+
+/* Let the empty slot dst share the first num_tokens tokens of src (all of
+ * them if num_tokens < 0): dst's table references src's first
+ * ceil(num_tokens / block_size) blocks (section 8.3.2, Fig. 8-13).
+ * PA_ERR_BAD_SHAPE if dst holds tokens, a slot is out of range or
+ * num_tokens exceeds src's length. */
+pa_status pa_pool_fork(pa_pool* pool, int32_t src, int32_t dst, int32_t num_tokens);
+
+/* Drop every reference `slot` holds and empty it.  A block whose count
+ * reaches zero becomes free once a fence >= `fence` is retired: the caller
+ * names the work that may still read it (e.g. the number of the step whose
+ * launches used it) and retires it when that work has finished (Fig. 8-14). */
+pa_status pa_pool_release(pa_pool* pool, int32_t slot, uint64_t fence);
+
+/* All work up to and including `fence` has finished: blocks released under
+ * such fences return to the free pool. */
+pa_status pa_pool_retire(pa_pool* pool, uint64_t fence);
+
+/* Tokens held by `slot` (-1 for a bad slot or pool). */
+int32_t pa_pool_length(const pa_pool* pool, int32_t slot);
+
+/* The pool's block tables, host int32 [num_slots][max_blocks_per_seq], valid
+ * until the pool is destroyed; entries past a slot's last block are 0.
+ * Upload them (or the rows in use) for pa_write_kv / pa_attend. */
+const int32_t* pa_pool_block_table(const pa_pool* pool);
+
+/* References to `block` (-1 for a bad block or pool). */
+int32_t pa_pool_refcount(const pa_pool* pool, int32_t block);
+
+pa_status pa_pool_get_stats(const pa_pool* pool, pa_pool_stats* stats);
 
 /* Static, NUL-terminated description of a status code. */
 const char* pa_status_string(pa_status status);

@@ -10,6 +10,8 @@ Modules
 attend       plain float64 softmax attention gathered through the page table,
              the key-range partial form and the log-sum-exp merge
 closed_forms the byte and block-count identities printed on the serving pages
+paging       a plain model of the paged block allocator (sharing, copy-on-write,
+             fenced release) and of appending new K/V rows to their pages
 """
 
 from .attend import (  # noqa: F401

@@ -10,7 +10,8 @@ implementation.
 
 _BINDING = ("PaError", "Shape", "Status", "attend", "combine", "gather_kv", "validate",
             "lib_path", "load", "make_shape", "plan", "status_string", "workspace_size",
-            "EXPORTS", "PreparedAttend", "workspace_init")
+            "EXPORTS", "PreparedAttend", "workspace_init", "write_kv", "copy_blocks", "Pool",
+            "PoolStats")
 
 
 def __getattr__(name):

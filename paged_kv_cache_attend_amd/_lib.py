@@ -23,7 +23,10 @@ PA_BAD_Q_LEN = 0x4
 PA_BAD_TOTAL_Q = 0x8
 
 EXPORTS = ("pa_workspace_size", "pa_workspace_init", "pa_num_partitions", "pa_attend", "pa_combine",
-           "pa_gather_kv", "pa_validate", "pa_status_string")
+           "pa_gather_kv", "pa_validate", "pa_write_kv", "pa_copy_blocks", "pa_pool_create",
+           "pa_pool_destroy", "pa_pool_append", "pa_pool_fork", "pa_pool_release", "pa_pool_retire",
+           "pa_pool_length", "pa_pool_block_table", "pa_pool_refcount", "pa_pool_get_stats",
+           "pa_status_string")
 
 
 class Status(enum.IntEnum):
@@ -33,6 +36,7 @@ class Status(enum.IntEnum):
     ERR_UNSUPPORTED = 3
     ERR_WORKSPACE_TOO_SMALL = 4
     ERR_LAUNCH = 5
+    ERR_OUT_OF_BLOCKS = 6
 
 
 class PaError(RuntimeError):
@@ -40,6 +44,18 @@ class PaError(RuntimeError):
         self.status = Status(status) if status in Status._value2member_map_ else status
         msg = status_string(status) if _lib is not None else str(status)
         super().__init__(f"{where}: {msg} ({self.status!r})" if where else msg)
+
+
+class PoolStats(ctypes.Structure):
+    """Mirror of ``pa_pool_stats``."""
+
+    _fields_ = [
+        ("free_blocks", ctypes.c_int32),
+        ("pending_blocks", ctypes.c_int32),
+        ("used_blocks", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+        ("references", ctypes.c_int64),
+    ]
 
 
 class Shape(ctypes.Structure):
@@ -95,6 +111,31 @@ def load():
     lib.pa_gather_kv.restype = ctypes.c_int
     lib.pa_validate.argtypes = [shp, P, P, P, P, P]
     lib.pa_validate.restype = ctypes.c_int
+    lib.pa_write_kv.argtypes = [shp, P, P, P, P, P, P, P, P]
+    lib.pa_write_kv.restype = ctypes.c_int
+    lib.pa_copy_blocks.argtypes = [ctypes.c_int32, P, P, ctypes.c_int32, ctypes.c_int64, P, P, P]
+    lib.pa_copy_blocks.restype = ctypes.c_int
+    i32, pi32 = ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)
+    lib.pa_pool_create.argtypes = [i32, i32, i32, i32, ctypes.POINTER(P)]
+    lib.pa_pool_create.restype = ctypes.c_int
+    lib.pa_pool_destroy.argtypes = [P]
+    lib.pa_pool_destroy.restype = None
+    lib.pa_pool_append.argtypes = [P, i32, i32, pi32, pi32, pi32]
+    lib.pa_pool_append.restype = ctypes.c_int
+    lib.pa_pool_fork.argtypes = [P, i32, i32, i32]
+    lib.pa_pool_fork.restype = ctypes.c_int
+    lib.pa_pool_release.argtypes = [P, i32, ctypes.c_uint64]
+    lib.pa_pool_release.restype = ctypes.c_int
+    lib.pa_pool_retire.argtypes = [P, ctypes.c_uint64]
+    lib.pa_pool_retire.restype = ctypes.c_int
+    lib.pa_pool_length.argtypes = [P, i32]
+    lib.pa_pool_length.restype = i32
+    lib.pa_pool_block_table.argtypes = [P]
+    lib.pa_pool_block_table.restype = pi32
+    lib.pa_pool_refcount.argtypes = [P, i32]
+    lib.pa_pool_refcount.restype = i32
+    lib.pa_pool_get_stats.argtypes = [P, ctypes.POINTER(PoolStats)]
+    lib.pa_pool_get_stats.restype = ctypes.c_int
     lib.pa_status_string.argtypes = [ctypes.c_int]
     lib.pa_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -267,6 +308,120 @@ def validate(block_table, ctx_lens, q_lens, error_word, *, num_blocks: int, tota
                             _ptr(error_word), _stream_handle(dev, stream))
     _check(st, "pa_validate")
     return error_word
+
+
+def write_kv(k_new, v_new, block_table, ctx_lens, q_lens, k_cache, v_cache, *, max_q_len: int,
+             stream=None):
+    """``pa_write_kv``: k_new, v_new bf16 [total_q, Hkv, 128] into the caches
+    (bf16 [num_blocks, Hkv, 16, 128]) at positions n - m .. n - 1 of each slot."""
+    torch = _torch()
+    dev = k_cache.device
+    _need(k_new, "k_new", torch.bfloat16, dev, 3)
+    _need(v_new, "v_new", torch.bfloat16, dev, 3)
+    _need(k_cache, "k_cache", torch.bfloat16, dev, 4)
+    _need(v_cache, "v_cache", torch.bfloat16, dev, 4)
+    _need(block_table, "block_table", torch.int32, dev, 2)
+    _need(ctx_lens, "ctx_lens", torch.int32, dev, 1)
+    _need(q_lens, "q_lens", torch.int32, dev, 1)
+    total_q, hkv, d = k_new.shape
+    nb, hkv2, bs, d2 = k_cache.shape
+    if tuple(v_new.shape) != tuple(k_new.shape) or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("k_new/v_new or k_cache/v_cache shapes differ")
+    if hkv != hkv2 or d != d2:
+        raise ValueError("new rows and caches disagree on KV heads or head_dim")
+    num_seqs = block_table.shape[0]
+    if ctx_lens.shape[0] != num_seqs or q_lens.shape[0] != num_seqs:
+        raise ValueError("ctx_lens / q_lens must have one entry per block-table row")
+    shape = make_shape(num_seqs, total_q, hkv, hkv, block_table.shape[1], max_q_len,
+                       bs * block_table.shape[1], nb, head_dim=d, block_size=bs)
+    st = load().pa_write_kv(ctypes.byref(shape), _ptr(k_new), _ptr(v_new), _ptr(block_table),
+                            _ptr(ctx_lens), _ptr(q_lens), _ptr(k_cache), _ptr(v_cache),
+                            _stream_handle(dev, stream))
+    _check(st, "pa_write_kv")
+
+
+def copy_blocks(src, dst, k_cache, v_cache, *, stream=None):
+    """``pa_copy_blocks``: src, dst int32 [num_copies] on the caches' device."""
+    torch = _torch()
+    dev = k_cache.device
+    _need(src, "src", torch.int32, dev, 1)
+    _need(dst, "dst", torch.int32, dev, 1)
+    _need(k_cache, "k_cache", torch.bfloat16, dev, 4)
+    _need(v_cache, "v_cache", torch.bfloat16, dev, 4)
+    if src.shape != dst.shape:
+        raise ValueError("src and dst differ in length")
+    nb, hkv, _, _ = k_cache.shape
+    st = load().pa_copy_blocks(int(src.shape[0]), _ptr(src), _ptr(dst), hkv, nb, _ptr(k_cache),
+                               _ptr(v_cache), _stream_handle(dev, stream))
+    _check(st, "pa_copy_blocks")
+
+
+class Pool:
+    """``pa_pool``: block tables, reference counts, copy-on-write, fenced release.
+
+    Host-side only.  ``append`` returns the (src, dst) block copies the caller
+    must make (``copy_blocks`` on every layer's caches) before writing.
+    """
+
+    def __init__(self, num_blocks: int, block_size: int, num_slots: int, max_blocks_per_seq: int):
+        lib = load()
+        h = ctypes.c_void_p()
+        _check(lib.pa_pool_create(num_blocks, block_size, num_slots, max_blocks_per_seq, ctypes.byref(h)),
+               "pa_pool_create")
+        self._h = h
+        self._lib = lib
+        self.num_blocks, self.block_size = num_blocks, block_size
+        self.num_slots, self.max_blocks = num_slots, max_blocks_per_seq
+
+    def close(self):
+        if self._h:
+            self._lib.pa_pool_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def append(self, slot: int, num_tokens: int):
+        """Copies to make (list of (src, dst)), or None if the pool is too small."""
+        src, dst, n = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+        st = self._lib.pa_pool_append(self._h, slot, num_tokens, ctypes.byref(src), ctypes.byref(dst),
+                                      ctypes.byref(n))
+        if st == Status.ERR_OUT_OF_BLOCKS:
+            return None
+        _check(st, "pa_pool_append")
+        return [(src.value, dst.value)] if n.value else []
+
+    def fork(self, src: int, dst: int, num_tokens: int = -1):
+        _check(self._lib.pa_pool_fork(self._h, src, dst, num_tokens), "pa_pool_fork")
+
+    def release(self, slot: int, fence: int):
+        _check(self._lib.pa_pool_release(self._h, slot, ctypes.c_uint64(fence)), "pa_pool_release")
+
+    def retire(self, fence: int):
+        _check(self._lib.pa_pool_retire(self._h, ctypes.c_uint64(fence)), "pa_pool_retire")
+
+    def length(self, slot: int) -> int:
+        return int(self._lib.pa_pool_length(self._h, slot))
+
+    def refcount(self, block: int) -> int:
+        return int(self._lib.pa_pool_refcount(self._h, block))
+
+    def stats(self) -> PoolStats:
+        s = PoolStats()
+        _check(self._lib.pa_pool_get_stats(self._h, ctypes.byref(s)), "pa_pool_get_stats")
+        return s
+
+    def table(self):
+        """A numpy copy of the block tables, int32 [num_slots, max_blocks_per_seq]."""
+        import numpy as np
+        n = self.num_slots * self.max_blocks
+        ptr = self._lib.pa_pool_block_table(self._h)
+        if n == 0:
+            return np.zeros((self.num_slots, self.max_blocks), dtype=np.int32)
+        return np.ctypeslib.as_array(ptr, shape=(n,)).reshape(self.num_slots, self.max_blocks).copy()
 
 
 class PreparedAttend:

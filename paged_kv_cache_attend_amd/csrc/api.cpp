@@ -291,6 +291,52 @@ pa_status pa_validate(const pa_shape* shape, const int32_t* block_table, const i
   return PA_OK;
 }
 
+pa_status pa_write_kv(const pa_shape* shape, const void* k_new, const void* v_new,
+                      const int32_t* block_table, const int32_t* ctx_lens, const int32_t* q_lens,
+                      void* k_cache, void* v_cache, void* stream) {
+  const pa_status st = check_shape(shape);
+  if (st != PA_OK) return st;
+  if (shape->num_seqs == 0 || shape->total_q == 0 || shape->max_q_len == 0) return PA_OK;
+  if (!k_new || !v_new || !block_table || !ctx_lens || !q_lens || !k_cache || !v_cache)
+    return PA_ERR_NULL_ARG;
+  WriteParams w;
+  w.k_new = static_cast<const uint16_t*>(k_new);
+  w.v_new = static_cast<const uint16_t*>(v_new);
+  w.block_table = block_table;
+  w.ctx_lens = ctx_lens;
+  w.q_lens = q_lens;
+  w.k_cache = static_cast<uint16_t*>(k_cache);
+  w.v_cache = static_cast<uint16_t*>(v_cache);
+  w.num_blocks = shape->num_blocks;
+  w.num_seqs = shape->num_seqs;
+  w.num_kv_heads = shape->num_kv_heads;
+  w.max_blocks = shape->max_blocks_per_seq;
+  w.max_q_len = shape->max_q_len;
+  w.total_q = shape->total_q;
+  if ((long long)ceil_div(shape->max_q_len, 16) * shape->num_seqs > INT_MAX) return PA_ERR_UNSUPPORTED;
+  if (launch_write_kv(w, static_cast<hipStream_t>(stream)) != hipSuccess) return PA_ERR_LAUNCH;
+  return PA_OK;
+}
+
+pa_status pa_copy_blocks(int32_t num_copies, const int32_t* src, const int32_t* dst,
+                         int32_t num_kv_heads, int64_t num_blocks, void* k_cache, void* v_cache,
+                         void* stream) {
+  if (num_copies < 0 || num_kv_heads <= 0 || num_blocks <= 0) return PA_ERR_BAD_SHAPE;
+  if ((long long)num_copies * num_kv_heads * 2 > INT_MAX) return PA_ERR_UNSUPPORTED;
+  if (num_copies == 0) return PA_OK;
+  if (!src || !dst || !k_cache || !v_cache) return PA_ERR_NULL_ARG;
+  CopyParams c;
+  c.src = src;
+  c.dst = dst;
+  c.k_cache = static_cast<uint16_t*>(k_cache);
+  c.v_cache = static_cast<uint16_t*>(v_cache);
+  c.num_blocks = num_blocks;
+  c.num_copies = num_copies;
+  c.num_kv_heads = num_kv_heads;
+  if (launch_copy_blocks(c, static_cast<hipStream_t>(stream)) != hipSuccess) return PA_ERR_LAUNCH;
+  return PA_OK;
+}
+
 const char* pa_status_string(pa_status status) {
   switch (status) {
     case PA_OK: return "ok";
@@ -299,6 +345,7 @@ const char* pa_status_string(pa_status status) {
     case PA_ERR_UNSUPPORTED: return "valid but unsupported configuration";
     case PA_ERR_WORKSPACE_TOO_SMALL: return "workspace smaller than pa_workspace_size()";
     case PA_ERR_LAUNCH: return "kernel launch failed";
+    case PA_ERR_OUT_OF_BLOCKS: return "the block pool has too few free blocks";
   }
   return "unknown status";
 }

@@ -108,7 +108,35 @@ constexpr int kChunkRows = 128;  // query rows per chunk workgroup
 hipError_t launch_chunk(const ChunkParams& p, unsigned grid, hipStream_t s);
 
 hipError_t launch_combine(const CombineParams& p, hipStream_t s);
+struct WriteParams {
+  const uint16_t* k_new;      // bf16 [total_q][Hkv][128]
+  const uint16_t* v_new;
+  const int32_t* block_table;
+  const int32_t* ctx_lens;
+  const int32_t* q_lens;
+  uint16_t* k_cache;          // bf16 [num_blocks][Hkv][16][128]
+  uint16_t* v_cache;
+  int64_t num_blocks;
+  int32_t num_seqs;
+  int32_t num_kv_heads;
+  int32_t max_blocks;
+  int32_t max_q_len;
+  int32_t total_q;            // rows of k_new / v_new
+};
+
+struct CopyParams {
+  const int32_t* src;         // [num_copies] block ids
+  const int32_t* dst;
+  uint16_t* k_cache;
+  uint16_t* v_cache;
+  int64_t num_blocks;
+  int32_t num_copies;
+  int32_t num_kv_heads;
+};
+
 hipError_t launch_gather(const GatherParams& p, hipStream_t s);
+hipError_t launch_write_kv(const WriteParams& p, hipStream_t s);
+hipError_t launch_copy_blocks(const CopyParams& p, hipStream_t s);
 hipError_t launch_validate(const ValidateParams& p, hipStream_t s);
 
 }  // namespace pa

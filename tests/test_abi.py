@@ -221,3 +221,33 @@ def test_single_hip_runtime_in_process():
             "print(len(paths))")
     out = subprocess.run(["python", "-c", code], capture_output=True, text=True, cwd=ROOT, check=True).stdout
     assert out.strip() == "1"
+
+
+def test_write_kv_and_copy_blocks_host_errors(lib):
+    s = _shape()
+    args = [FAKE] * 8
+    assert lib.pa_write_kv(None, *args[:7], None) == pk.Status.ERR_NULL_ARG
+    for i in range(7):
+        a = list(args[:7])
+        a[i] = None
+        assert lib.pa_write_kv(ctypes.byref(s), *a, None) == pk.Status.ERR_NULL_ARG, i
+    bad = _shape(head_dim=64)
+    assert lib.pa_write_kv(ctypes.byref(bad), *args[:7], None) == pk.Status.ERR_UNSUPPORTED
+    empty = _shape(num_seqs=0)
+    assert lib.pa_write_kv(ctypes.byref(empty), *args[:7], None) == pk.Status.OK
+    assert lib.pa_copy_blocks(-1, FAKE, FAKE, 8, 64, FAKE, FAKE, None) == pk.Status.ERR_BAD_SHAPE
+    assert lib.pa_copy_blocks(1, FAKE, FAKE, 0, 64, FAKE, FAKE, None) == pk.Status.ERR_BAD_SHAPE
+    assert lib.pa_copy_blocks(1, None, FAKE, 8, 64, FAKE, FAKE, None) == pk.Status.ERR_NULL_ARG
+    assert lib.pa_copy_blocks(0, None, None, 8, 64, None, None, None) == pk.Status.OK
+
+
+def test_pool_null_handles(lib):
+    st = pk.PoolStats()
+    i = ctypes.c_int32()
+    assert lib.pa_pool_create(4, 16, 1, 1, None) == pk.Status.ERR_NULL_ARG
+    assert lib.pa_pool_append(None, 0, 1, ctypes.byref(i), ctypes.byref(i), ctypes.byref(i)) == pk.Status.ERR_NULL_ARG
+    assert lib.pa_pool_fork(None, 0, 1, -1) == pk.Status.ERR_NULL_ARG
+    assert lib.pa_pool_release(None, 0, 0) == pk.Status.ERR_NULL_ARG
+    assert lib.pa_pool_retire(None, 0) == pk.Status.ERR_NULL_ARG
+    assert lib.pa_pool_get_stats(None, ctypes.byref(st)) == pk.Status.ERR_NULL_ARG
+    lib.pa_pool_destroy(None)
