@@ -73,6 +73,10 @@ def gather_request_kv(cache_bits, table_row, n: int, kv_head: int, block_size: i
     rest of the last block is unused tail (section 8.3.1: at most
     ``block_size - 1`` wasted slots) and is never read.
 
+    The cache holds bf16 bit patterns (uint16), or values already widened
+    to float64 (pages decoded from a quantised format), which pass through
+    unchanged.
+
     Returns float64 ``[n][head_dim]``.
     """
     rows = []
@@ -86,7 +90,10 @@ def gather_request_kv(cache_bits, table_row, n: int, kv_head: int, block_size: i
         logical += 1
     if not rows:
         return np.zeros((0, cache_bits.shape[-1]), dtype=np.float64)
-    return bf16_bits_to_f64(np.concatenate(rows, axis=0))
+    block = np.concatenate(rows, axis=0)
+    if block.dtype == np.float64:
+        return block
+    return bf16_bits_to_f64(block)
 
 
 def _query_offsets(q_lens) -> list[int]:
