@@ -46,6 +46,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-chunk", action="store_true", help="skip the secondary chunk-path measurement")
     ap.add_argument("--no-append", action="store_true", help="skip the secondary K/V-append measurement")
+    ap.add_argument("--no-quant", action="store_true", help="skip the secondary quantised-KV decode measurement")
     ap.add_argument("--cpu-budget-s", type=float, default=25.0)
     ap.add_argument("--mode", choices=["bench", "copy"], default="bench",
                     help="copy: time a plain 1 GiB device copy (counter calibration for rocprofv3)")
@@ -296,6 +297,71 @@ def append_secondary(dev, steps, launch="graph"):
             "parity": "bit-exact against the oracle scatter in the GPU tests"}
 
 
+def quant_secondary(dev, steps, launch, bf16_us_per_layer):
+    """Decode of the Qwen3-8B-shaped batch (16 x 2303 keys, 32/8 heads) over
+    FP8, q8_0 and q4_0 pages: microseconds per layer, GB/s over the bytes the
+    format reads (codes + group scales), and the trade of section 8.4.2,
+    Delta T = Delta D / beta - T_c, against the bf16 time measured above."""
+    import torch
+    import paged_kv_cache_attend_amd as pk
+    from paged_kv_cache_attend_amd import inputs
+    p = inputs.qwen3_short_decode(num_layers=1)
+    nb, hkv = p.num_blocks, p.num_kv_heads
+    q = inputs.bits_to_torch_bf16(inputs.normal_bf16(np.random.SeedSequence(inputs.SEED_BASE + 4200),
+                                                     (p.total_q, p.num_q_heads, p.head_dim)), dev)
+    table = torch.from_numpy(p.block_table.astype(np.int32)).to(dev)
+    ctx = torch.from_numpy(p.ctx_lens.astype(np.int32)).to(dev)
+    ql = torch.from_numpy(p.q_lens.astype(np.int32)).to(dev)
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:2], dtype=torch.float32, device=dev)
+    shape = pk.make_shape(p.num_seqs, p.total_q, p.num_q_heads, hkv, p.max_blocks_per_seq, 1,
+                          p.max_ctx_len, nb)
+    ws = torch.empty(max(pk.workspace_size(shape), 1), dtype=torch.uint8, device=dev)
+    pk.workspace_init(shape, ws)
+    tokens = int(p.ctx_lens.sum())
+    bf16_bytes = tokens * hkv * 512
+    distinct = 12  # 12 distinct layers of pages (over 500 MB even for q4_0), cycled to 36 launches
+    res = {}
+    for name, fmt, per_tok in (("fp8", pk.KV_FP8_E4M3, 256), ("q8_0", pk.KV_Q8_0, 272),
+                               ("q4_0", pk.KV_Q4_0, 144)):
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(inputs.SEED_BASE + 4100 + fmt)
+        calls = []
+        keep = []
+        for _ in range(distinct):
+            c = pk.QuantCache.empty(fmt, nb, hkv, dev, 1.0 / 64, 1.0 / 256)
+            for codes in (c.k_codes, c.v_codes):
+                if fmt == pk.KV_Q8_0:
+                    codes.copy_(torch.randint(-127, 128, codes.shape, generator=gen, device=dev, dtype=torch.int8))
+                else:
+                    r = torch.randint(0, 256, codes.shape, generator=gen, device=dev, dtype=torch.int32)
+                    if fmt == pk.KV_FP8_E4M3:
+                        r = torch.where((r & 0x7F) == 0x7F, r & 0xF7, r)   # no NaN codes
+                    codes.copy_(r.to(torch.uint8))
+            for sc in (c.k_scales, c.v_scales):
+                if sc is not None:
+                    lo, hi = (0.004, 0.0157) if fmt == pk.KV_Q8_0 else (0.05, 0.25)
+                    sc.copy_((torch.rand(sc.shape, generator=gen, device=dev) * (hi - lo) + lo).half())
+            keep.append(c)
+            calls.append(pk.attend_kv(q, c, table, ctx, ql, float(p.scale), out, lse, max_q_len=1,
+                                      max_ctx_len=p.max_ctx_len, workspace=ws, prepared=True))
+        ms, _, _ = time_pass(calls * 3, max(steps // 4, 20), 3, launch)
+        us = ms * 1e3 / (3 * distinct)
+        moved = tokens * hkv * per_tok
+        beta = bf16_bytes / (bf16_us_per_layer * 1e-6)          # bf16's achieved read rate
+        saved_read_us = (bf16_bytes - moved) / beta * 1e6       # Delta D / beta
+        res[name] = {"us_per_layer": us, "bytes_per_layer": moved, "gbs": moved / (us * 1e-6) / 1e9,
+                     "frac_of_hbm_peak": moved / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                     "speedup_vs_bf16": bf16_us_per_layer / us,
+                     "delta_T_us": bf16_us_per_layer - us, "delta_D_over_beta_us": saved_read_us,
+                     "T_c_us": saved_read_us - (bf16_us_per_layer - us)}
+        del calls, keep
+        torch.cuda.empty_cache()
+    res["workload"] = "qwen3_8b_short_decode, 12 distinct layers of random codes cycled to 36 launches"
+    res["parity"] = "against the FP64 oracle over decoded pages in the GPU tests"
+    return res
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -382,6 +448,9 @@ def main():
     append = None
     if decode and not args.no_append:
         append = append_secondary(dev, args.steps, args.launch)
+    quant = None
+    if decode and not args.no_quant and problem.name == "qwen3_8b_short_decode":
+        quant = quant_secondary(dev, args.steps, args.launch, ms / len(calls) * 1e3)
 
     line = {
         "metric": METRIC,
@@ -421,6 +490,7 @@ def main():
         "parity": par,
         "chunk": secondary,
         "append": append,
+        "quantised": quant,
         "source_hash": kernel_source_hash(),
     }
     print(json.dumps(line), flush=True)

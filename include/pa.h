@@ -105,7 +105,8 @@ typedef struct pa_shape {
   uint32_t reserved;          /* must be 0 */
 } pa_shape;
 
-/* Bytes of scratch pa_attend needs for this shape: one int32 counter per
+/* Bytes of scratch pa_attend (and pa_attend_kv, whatever the page format)
+ * needs for this shape: one int32 counter per
  * (slot, KV head), then the split-KV partials (fp32 LSE and normalised fp32
  * output per partition and row).  0 when the call needs none.  Returns 0 for
  * a shape pa_attend would reject. */
@@ -123,6 +124,11 @@ pa_status pa_workspace_init(const pa_shape* shape, void* workspace, size_t works
 /* Number of split-KV partitions pa_attend will use for this shape (1 = no
  * split, or the path that does not split); 0 for an invalid shape. */
 int32_t pa_num_partitions(const pa_shape* shape);
+
+/* The same for pa_attend_kv with pages in `format` (a pa_kv_format): with
+ * an automatic partition size, compressed pages are split into more
+ * partitions; 0 for an invalid shape or format. */
+int32_t pa_num_partitions_kv(const pa_shape* shape, int32_t format);
 
 /* Attention of the new rows against the paged cache, as defined above.
  * `workspace` (initialised with pa_workspace_init for this shape) may be
@@ -174,6 +180,71 @@ pa_status pa_gather_kv(const pa_shape* shape, const void* cache,
 pa_status pa_validate(const pa_shape* shape, const int32_t* block_table,
                       const int32_t* ctx_lens, const int32_t* q_lens,
                       int32_t* error_word, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Quantised KV pages
+ * ------------------------------------------------------------------------
+ * The chapter's section 8.4.2 ("KV compression and read cost", Fig. 8-23)
+ * stores KV in groups of 32 values with one 2-byte scale each: q8_0 keeps
+ * one-byte codes (34 bytes per group where bf16 needs 64), q4_0 4-bit codes
+ * (18 bytes).  Section 8.4.4 studies an FP8 cache and keeps the query in
+ * bf16, as everything here does.  Reading fewer bytes pays when the
+ * conversion costs less than the bytes saved: Delta T = Delta D / beta - T_c.
+ *
+ * Layouts (per layer, K and V alike; a group is 32 consecutive dims of one
+ * token row of one KV head):
+ *   PA_KV_BF16      codes = the bf16 cache of pa_attend
+ *   PA_KV_FP8_E4M3  codes uint8 [num_blocks][Hkv][16][128], OCP E4M3 (bias 7,
+ *                   no infinities, max 448); value = decode(code) * scale,
+ *                   one fp32 scale per cache
+ *   PA_KV_Q8_0      codes int8  [num_blocks][Hkv][16][128]; scales fp16
+ *                   [num_blocks][Hkv][16][4]; value = code * scale
+ *   PA_KV_Q4_0      codes uint8 [num_blocks][Hkv][16][64], byte b holding dim
+ *                   2b in its low and 2b+1 in its high nibble; scales fp16
+ *                   [num_blocks][Hkv][16][4]; value = (nibble - 8) * scale
+ * Encoding (pa_write_kv_cache): q8_0 scale = max|x| / 127 and q4_0 scale =
+ * (the group's value of largest magnitude) / -8, both rounded to fp16 (a
+ * zero scale stored as +0); code
+ * = x / stored scale in fp32, rounded half away from zero, clamped to the
+ * code range; FP8 code = nearest E4M3 of x / scale (ties to even, saturating
+ * at +-448). */
+typedef enum pa_kv_format {
+  PA_KV_BF16 = 0,
+  PA_KV_FP8_E4M3 = 1,
+  PA_KV_Q8_0 = 2,
+  PA_KV_Q4_0 = 3
+} pa_kv_format;
+
+typedef struct pa_kv_cache {
+  int32_t format;   /* pa_kv_format */
+  int32_t reserved; /* must be 0 */
+  void* k_codes;    /* layouts above (device memory) */
+  void* v_codes;
+  void* k_scales;   /* q8_0, q4_0: fp16 group scales; otherwise unused */
+  void* v_scales;
+  float k_scale;    /* FP8: per-cache scales; otherwise unused */
+  float v_scale;
+} pa_kv_cache;
+
+/* pa_attend over a cache in any of the formats: the same definition, with
+ * K and V the decoded values above.  PA_KV_BF16 is pa_attend itself.  The
+ * quantised formats take the decode path only (max_q_len == 1 and a query
+ * group of 1, 2 or 4 heads); other shapes return PA_ERR_UNSUPPORTED.  The
+ * workspace is pa_workspace_size(shape), initialised with pa_workspace_init,
+ * as for pa_attend (pa_num_partitions_kv gives the partition count).  Errors as for
+ * pa_attend, plus PA_ERR_BAD_SHAPE for an unknown format, a non-finite or
+ * non-positive FP8 scale, or reserved != 0. */
+pa_status pa_attend_kv(const pa_shape* shape, const pa_kv_cache* cache, const void* q,
+                       const int32_t* block_table, const int32_t* ctx_lens,
+                       const int32_t* q_lens, float scale, void* out, float* lse,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* pa_write_kv into a cache in any of the formats: each new bf16 row is
+ * encoded (per the rules above) into the codes and scales at its position.
+ * PA_KV_BF16 is pa_write_kv itself.  Skips as pa_write_kv does. */
+pa_status pa_write_kv_cache(const pa_shape* shape, const pa_kv_cache* cache, const void* k_new,
+                            const void* v_new, const int32_t* block_table,
+                            const int32_t* ctx_lens, const int32_t* q_lens, void* stream);
 
 /* ------------------------------------------------------------------------
  * Appending new K/V, and the block pool that hands out pages

@@ -24,7 +24,8 @@ Readings (where the pages leave the encoding open)
   d = m / -8 stored as fp16; code = x / d_stored rounded half away from zero,
   clamped to [-8, 7], stored as code + 8 in a nibble; value = (nibble - 8) *
   d_stored.  The extreme value maps to code -8 exactly;
-* a stored scale of zero gives codes 0 (values 0);
+* a stored scale of zero gives codes 0 (values 0) and is stored as +0 (the
+  sign of a zero scale changes no value, so it is fixed to one pattern);
 * FP8 is the OCP E4M3 format (sign, 4 exponent bits with bias 7, 3 mantissa
   bits; no infinities; S.1111.111 is NaN; largest finite 448); code = the
   E4M3 value nearest to x / s (fp32 division), ties to the even code,
@@ -73,6 +74,7 @@ def q8_0_encode(x):
     amax = np.abs(g).max(axis=-1)
     d = (amax / np.float32(127)).astype(np.float32)          # fp32, correctly rounded
     d_bits = fp16_bits(d)
+    d_bits = np.where(fp16_value(d_bits) == 0, np.uint16(0), d_bits)   # +0, not -0
     d_st = fp16_value(d_bits).astype(np.float32)
     with np.errstate(divide="ignore", invalid="ignore"):
         ratio = (g / d_st[..., None]).astype(np.float32)      # fp32 division
@@ -98,6 +100,7 @@ def q4_0_encode(x):
     m = np.take_along_axis(g, idx[..., None], axis=-1)[..., 0]
     d = (m / np.float32(-8)).astype(np.float32)
     d_bits = fp16_bits(d)
+    d_bits = np.where(fp16_value(d_bits) == 0, np.uint16(0), d_bits)   # +0, not -0
     d_st = fp16_value(d_bits).astype(np.float32)
     with np.errstate(divide="ignore", invalid="ignore"):
         ratio = (g / d_st[..., None]).astype(np.float32)

@@ -26,7 +26,13 @@ EXPORTS = ("pa_workspace_size", "pa_workspace_init", "pa_num_partitions", "pa_at
            "pa_gather_kv", "pa_validate", "pa_write_kv", "pa_copy_blocks", "pa_pool_create",
            "pa_pool_destroy", "pa_pool_append", "pa_pool_fork", "pa_pool_release", "pa_pool_retire",
            "pa_pool_length", "pa_pool_block_table", "pa_pool_refcount", "pa_pool_get_stats",
-           "pa_status_string")
+           "pa_attend_kv", "pa_write_kv_cache", "pa_num_partitions_kv", "pa_status_string")
+
+# pa_kv_format
+KV_BF16 = 0
+KV_FP8_E4M3 = 1
+KV_Q8_0 = 2
+KV_Q4_0 = 3
 
 
 class Status(enum.IntEnum):
@@ -55,6 +61,21 @@ class PoolStats(ctypes.Structure):
         ("used_blocks", ctypes.c_int32),
         ("reserved", ctypes.c_int32),
         ("references", ctypes.c_int64),
+    ]
+
+
+class KVCache(ctypes.Structure):
+    """Mirror of ``pa_kv_cache``."""
+
+    _fields_ = [
+        ("format", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+        ("k_codes", ctypes.c_void_p),
+        ("v_codes", ctypes.c_void_p),
+        ("k_scales", ctypes.c_void_p),
+        ("v_scales", ctypes.c_void_p),
+        ("k_scale", ctypes.c_float),
+        ("v_scale", ctypes.c_float),
     ]
 
 
@@ -103,6 +124,8 @@ def load():
     lib.pa_workspace_init.restype = ctypes.c_int
     lib.pa_num_partitions.argtypes = [shp]
     lib.pa_num_partitions.restype = ctypes.c_int32
+    lib.pa_num_partitions_kv.argtypes = [shp, ctypes.c_int32]
+    lib.pa_num_partitions_kv.restype = ctypes.c_int32
     lib.pa_attend.argtypes = [shp, P, P, P, P, P, P, ctypes.c_float, P, P, P, ctypes.c_size_t, P]
     lib.pa_attend.restype = ctypes.c_int
     lib.pa_combine.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P, P, P, P, P]
@@ -136,6 +159,11 @@ def load():
     lib.pa_pool_refcount.restype = i32
     lib.pa_pool_get_stats.argtypes = [P, ctypes.POINTER(PoolStats)]
     lib.pa_pool_get_stats.restype = ctypes.c_int
+    kvp = ctypes.POINTER(KVCache)
+    lib.pa_attend_kv.argtypes = [shp, kvp, P, P, P, P, ctypes.c_float, P, P, P, ctypes.c_size_t, P]
+    lib.pa_attend_kv.restype = ctypes.c_int
+    lib.pa_write_kv_cache.argtypes = [shp, kvp, P, P, P, P, P, P]
+    lib.pa_write_kv_cache.restype = ctypes.c_int
     lib.pa_status_string.argtypes = [ctypes.c_int]
     lib.pa_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -354,6 +382,134 @@ def copy_blocks(src, dst, k_cache, v_cache, *, stream=None):
     st = load().pa_copy_blocks(int(src.shape[0]), _ptr(src), _ptr(dst), hkv, nb, _ptr(k_cache),
                                _ptr(v_cache), _stream_handle(dev, stream))
     _check(st, "pa_copy_blocks")
+
+
+class QuantCache:
+    """One layer's K/V pages in a ``pa_kv_format`` (torch tensors on one GPU).
+
+    bf16: k_codes, v_codes bf16 [num_blocks, Hkv, 16, 128].
+    FP8:  uint8 codes [num_blocks, Hkv, 16, 128] and one fp32 scale per cache.
+    q8_0: int8 codes [num_blocks, Hkv, 16, 128], fp16 scales [num_blocks, Hkv, 16, 4].
+    q4_0: uint8 codes [num_blocks, Hkv, 16, 64], fp16 scales as q8_0.
+    """
+
+    def __init__(self, fmt: int, k_codes, v_codes, k_scales=None, v_scales=None, k_scale: float = 1.0,
+                 v_scale: float = 1.0):
+        self.format = int(fmt)
+        self.k_codes, self.v_codes = k_codes, v_codes
+        self.k_scales, self.v_scales = k_scales, v_scales
+        self.k_scale, self.v_scale = float(k_scale), float(v_scale)
+        self.num_blocks, self.num_kv_heads = int(k_codes.shape[0]), int(k_codes.shape[1])
+
+    @classmethod
+    def empty(cls, fmt: int, num_blocks: int, num_kv_heads: int, device, k_scale: float = 1.0,
+              v_scale: float = 1.0):
+        torch = _torch()
+        dims = {KV_BF16: (128, torch.bfloat16), KV_FP8_E4M3: (128, torch.uint8), KV_Q8_0: (128, torch.int8),
+                KV_Q4_0: (64, torch.uint8)}
+        if fmt not in dims:
+            raise ValueError(f"unknown KV format {fmt}")
+        d, dt = dims[fmt]
+        shape = (num_blocks, num_kv_heads, 16, d)
+        k = torch.zeros(shape, dtype=dt, device=device)
+        v = torch.zeros(shape, dtype=dt, device=device)
+        ks = vs = None
+        if fmt in (KV_Q8_0, KV_Q4_0):
+            ks = torch.zeros((num_blocks, num_kv_heads, 16, 4), dtype=torch.float16, device=device)
+            vs = torch.zeros_like(ks)
+        return cls(fmt, k, v, ks, vs, k_scale, v_scale)
+
+    def struct(self) -> KVCache:
+        return KVCache(self.format, 0, _ptr(self.k_codes).value, _ptr(self.v_codes).value,
+                       None if self.k_scales is None else _ptr(self.k_scales).value,
+                       None if self.v_scales is None else _ptr(self.v_scales).value,
+                       self.k_scale, self.v_scale)
+
+    def check(self, device):
+        torch = _torch()
+        want = {KV_BF16: torch.bfloat16, KV_FP8_E4M3: torch.uint8, KV_Q8_0: torch.int8, KV_Q4_0: torch.uint8}
+        dim = 64 if self.format == KV_Q4_0 else 128
+        for t, name in ((self.k_codes, "k_codes"), (self.v_codes, "v_codes")):
+            _need(t, name, want[self.format], device, 4)
+            if t.shape[2:] != (16, dim):
+                raise ValueError(f"{name} must be [num_blocks, Hkv, 16, {dim}]")
+        if self.k_codes.shape != self.v_codes.shape:
+            raise ValueError("k_codes and v_codes differ in shape")
+        if self.format in (KV_Q8_0, KV_Q4_0):
+            for t, name in ((self.k_scales, "k_scales"), (self.v_scales, "v_scales")):
+                _need(t, name, torch.float16, device, 4)
+                if tuple(t.shape) != (self.num_blocks, self.num_kv_heads, 16, 4):
+                    raise ValueError(f"{name} must be [num_blocks, Hkv, 16, 4]")
+
+
+def attend_kv(q, cache: QuantCache, block_table, ctx_lens, q_lens, scale, out, lse=None, *,
+              max_q_len: int, max_ctx_len: int, partition_size: int = 0, workspace=None, stream=None,
+              prepared: bool = False):
+    """``pa_attend_kv`` on torch tensors; with ``prepared=True`` returns a
+    launchable object (for graphs and timing) instead of launching once."""
+    torch = _torch()
+    dev = q.device
+    _need(q, "q", torch.bfloat16, dev, 3)
+    _need(out, "out", torch.bfloat16, dev, 3)
+    _need(block_table, "block_table", torch.int32, dev, 2)
+    _need(ctx_lens, "ctx_lens", torch.int32, dev, 1)
+    _need(q_lens, "q_lens", torch.int32, dev, 1)
+    cache.check(dev)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, dev, 2)
+    total_q, hq, d = q.shape
+    if tuple(out.shape) != tuple(q.shape):
+        raise ValueError("out must match q")
+    num_seqs = block_table.shape[0]
+    shape = make_shape(num_seqs, total_q, hq, cache.num_kv_heads, block_table.shape[1], max_q_len,
+                       max_ctx_len, cache.num_blocks, partition_size, head_dim=d)
+    need = workspace_size(shape)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        workspace_init(shape, workspace, stream=stream)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    kv = cache.struct()
+    args = [ctypes.byref(shape), ctypes.byref(kv), _ptr(q), _ptr(block_table), _ptr(ctx_lens), _ptr(q_lens),
+            ctypes.c_float(float(scale)), _ptr(out), _ptr(lse), _ptr(workspace), ctypes.c_size_t(ws_bytes)]
+    fn = load().pa_attend_kv
+
+    class _Call:
+        keep = (shape, kv, q, cache, block_table, ctx_lens, q_lens, out, lse, workspace)
+        num_partitions = int(load().pa_num_partitions_kv(ctypes.byref(shape), cache.format))
+
+        def launch(self, s=None):
+            st = fn(*args, _stream_handle(dev, s))
+            if st:
+                raise PaError(st, "pa_attend_kv")
+
+    call = _Call()
+    if prepared:
+        return call
+    call.launch(stream)
+    return out, lse
+
+
+def write_kv_cache(k_new, v_new, block_table, ctx_lens, q_lens, cache: QuantCache, *, max_q_len: int,
+                   stream=None):
+    """``pa_write_kv_cache``: encode new bf16 rows [total_q, Hkv, 128] into the cache."""
+    torch = _torch()
+    dev = k_new.device
+    _need(k_new, "k_new", torch.bfloat16, dev, 3)
+    _need(v_new, "v_new", torch.bfloat16, dev, 3)
+    _need(block_table, "block_table", torch.int32, dev, 2)
+    _need(ctx_lens, "ctx_lens", torch.int32, dev, 1)
+    _need(q_lens, "q_lens", torch.int32, dev, 1)
+    cache.check(dev)
+    total_q, hkv, d = k_new.shape
+    if tuple(v_new.shape) != tuple(k_new.shape) or hkv != cache.num_kv_heads:
+        raise ValueError("new rows disagree with each other or with the cache")
+    num_seqs = block_table.shape[0]
+    shape = make_shape(num_seqs, total_q, hkv, hkv, block_table.shape[1], max_q_len,
+                       16 * block_table.shape[1], cache.num_blocks, head_dim=d)
+    kv = cache.struct()
+    st = load().pa_write_kv_cache(ctypes.byref(shape), ctypes.byref(kv), _ptr(k_new), _ptr(v_new),
+                                  _ptr(block_table), _ptr(ctx_lens), _ptr(q_lens), _stream_handle(dev, stream))
+    _check(st, "pa_write_kv_cache")
 
 
 class Pool:

@@ -21,8 +21,15 @@
 //   each with four 128-bit loads per lane (fully coalesced, 1 KiB per
 //   instruction) into a three-page register ring: two pages are in flight
 //   while one is consumed, and a page's loads are issued as soon as its
-//   buffer is free.  Page ids come from scalar loads one issue ahead.  The partition's block-table entries
-//   are read once into lanes and broadcast with readlane.
+//   buffer is free.  Page ids come from scalar loads one issue ahead.
+// * Quantised pages (the chapter's section 8.4.2; FP8 E4M3, q8_0, q4_0) use
+//   the same schedule: a lane loads the codes of the same (token, 8 dims)
+//   chunks -- 8, 8 or 4 bytes instead of 16 -- plus, for q8_0 / q4_0, the
+//   fp16 scale of each chunk's 32-value group, and turns the codes into bf16
+//   in registers (exact: E4M3 values and small integers are bf16 values).
+//   Group scales multiply the per-group partial scores of K and the PV
+//   weights of V; FP8's per-cache K scale is folded into the softmax scale
+//   and its V scale into the weights.
 // * Scores: the K tile goes to LDS (XOR-swizzled 16-byte chunks, conflict
 //   free); lane (token t = lane % 16, head h = lane / 16) forms the 128-long
 //   dot product of its query head with key t using v_dot2c_f32_bf16 against
@@ -54,23 +61,110 @@ namespace {
 
 constexpr int kWaves = kDecodeWaves;
 constexpr int kTileBytes = kBlockSize * kHeadDim * 2;  // 4 KiB
-constexpr int kTileVec = kTileBytes / 16;              // uint4 per tile
 constexpr float kRescaleSlack = 8.0f;                  // log2 units
 
-struct Page {
-  u32x4_t k[4];
-  u32x4_t v[4];
+// One page of one KV head as loaded: per lane, the codes of chunks
+// c = lane + 64 k (k < 4) -- token c / 16, dims 8 (c % 16) .. +8 -- of the K
+// and the V tile, and for the grouped formats the scale of each chunk.
+template <int F>
+struct Page;
+template <>
+struct Page<kFmtBF16> {
+  u32x4_t k[4], v[4];
+};
+template <>
+struct Page<kFmtFP8> {
+  u32x2_t k[4], v[4];
+};
+// Grouped formats: lane L also holds the fp16 scale of (token L / 4, group
+// L % 4) of the K and of the V tile -- the tile's 64 scales, one per lane.
+template <>
+struct Page<kFmtQ8> {
+  u32x2_t k[4], v[4];
+  uint32_t ks, vs;
+};
+template <>
+struct Page<kFmtQ4> {
+  uint32_t k[4], v[4];
+  uint32_t ks, vs;
 };
 
+// Bytes of codes per (block, KV head) tile.
+template <int F>
+constexpr int tile_code_bytes() {
+  return F == kFmtBF16 ? 4096 : (F == kFmtQ4 ? 1024 : 2048);
+}
+
 // Issue the loads of one page (K and V tiles of KV head g) into `b`.
-__device__ __forceinline__ void issue_page(Page& b, const u32x4_t* __restrict__ kpool,
-                                           const u32x4_t* __restrict__ vpool, int32_t phys, int g,
-                                           int num_kv_heads, int lane) {
-  const size_t base = tile_index(phys, g, num_kv_heads) * kTileVec + lane;
+template <int F>
+__device__ __forceinline__ void issue_page(Page<F>& b, const DecodeParams& p, int32_t phys, int g,
+                                           int lane) {
+  const size_t ti = tile_index(phys, g, p.num_kv_heads);
+  constexpr int kChunks = kBlockSize * kHeadDim / 8;  // 256 chunks of 8 values per tile
+  if constexpr (F == kFmtBF16) {
+    const u32x4_t* kp = reinterpret_cast<const u32x4_t*>(p.k) + ti * kChunks + lane;
+    const u32x4_t* vp = reinterpret_cast<const u32x4_t*>(p.v) + ti * kChunks + lane;
 #pragma unroll
-  for (int k = 0; k < 4; ++k) b.k[k] = stream_load(kpool + base + k * 64);
+    for (int k = 0; k < 4; ++k) b.k[k] = stream_load(kp + k * 64);
 #pragma unroll
-  for (int k = 0; k < 4; ++k) b.v[k] = stream_load(vpool + base + k * 64);
+    for (int k = 0; k < 4; ++k) b.v[k] = stream_load(vp + k * 64);
+  } else if constexpr (F == kFmtFP8 || F == kFmtQ8) {
+    const u32x2_t* kp = reinterpret_cast<const u32x2_t*>(p.k) + ti * kChunks + lane;
+    const u32x2_t* vp = reinterpret_cast<const u32x2_t*>(p.v) + ti * kChunks + lane;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) b.k[k] = stream_load(kp + k * 64);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) b.v[k] = stream_load(vp + k * 64);
+  } else {
+    const uint32_t* kp = reinterpret_cast<const uint32_t*>(p.k) + ti * kChunks + lane;
+    const uint32_t* vp = reinterpret_cast<const uint32_t*>(p.v) + ti * kChunks + lane;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) b.k[k] = stream_load(kp + k * 64);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) b.v[k] = stream_load(vp + k * 64);
+  }
+  if constexpr (F == kFmtQ8 || F == kFmtQ4) {
+    b.ks = stream_load(p.k_scales + ti * (kBlockSize * 4) + lane);
+    b.vs = stream_load(p.v_scales + ti * (kBlockSize * 4) + lane);
+  }
+}
+
+__device__ __forceinline__ float half_bits_to_float(uint32_t h) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+
+// Eight codes of one chunk -> eight bf16 values (exact for every format).
+template <int F, typename T>
+__device__ __forceinline__ u32x4_t chunk_to_bf16(const T& c) {
+  if constexpr (F == kFmtBF16) {
+    return c;
+  } else if constexpr (F == kFmtFP8) {
+    u32x4_t r;
+    typedef float f2_t __attribute__((ext_vector_type(2)));
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+      const f2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)c[w], false);
+      const f2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)c[w], true);
+      r[2 * w] = pack_bf16x2(lo.x, lo.y);
+      r[2 * w + 1] = pack_bf16x2(hi.x, hi.y);
+    }
+    return r;
+  } else if constexpr (F == kFmtQ8) {
+    u32x4_t r;
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+      const int32_t x = (int32_t)c[w];
+      r[2 * w] = pack_bf16x2((float)((x << 24) >> 24), (float)((x << 16) >> 24));
+      r[2 * w + 1] = pack_bf16x2((float)((x << 8) >> 24), (float)(x >> 24));
+    }
+    return r;
+  } else {
+    u32x4_t r;
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+      r[w] = pack_bf16x2((float)(int)((c >> (8 * w)) & 15u) - 8.f, (float)(int)((c >> (8 * w + 4)) & 15u) - 8.f);
+    return r;
+  }
 }
 
 template <int G>
@@ -80,33 +174,50 @@ struct WaveState {
   float acc[G][8];  // PV layout accumulators
 };
 
-// One page: scores, online softmax, PV.  `sk` is this wave's 4 KiB LDS tile,
-// `sp` its 16 x 4 weight buffer, `salpha` its 4 rescale factors.
-template <int G>
-__device__ __forceinline__ void consume_page(WaveState<G>& st, Page& b, const uint8_t* sq,
-                                             uint8_t* sk, float* sp, float* salpha, int valid,
-                                             float scale_log2, int lane) {
+// One page: scores, online softmax, PV.  `sk` is this wave's 4 KiB LDS tile
+// (bf16), `sks` its 16 x 4 K group scales, `sp` its 16 x 4 weight buffer,
+// `salpha` its 4 rescale factors.
+template <int G, int F>
+__device__ __forceinline__ void consume_page(WaveState<G>& st, Page<F>& b, const uint8_t* sq,
+                                             uint8_t* sk, float* sks, float* sp, float* salpha,
+                                             int valid, float scale_log2, float v_scale, int lane) {
   const int tq = lane & 15;
   const int hq = (lane >> 4) % G;
   const int pr = lane >> 4;
   const int pc = lane & 15;
+  constexpr bool kGrouped = F == kFmtQ8 || F == kFmtQ4;
 
-  // K tile -> LDS.  Row t (256 B) keeps its 16-byte chunk c at slot c ^ t.
+  // K tile -> LDS as bf16.  Row t (256 B) keeps its 16-byte chunk c at slot c ^ t.
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const int t = 4 * k + pr;
-    *reinterpret_cast<u32x4_t*>(sk + t * 256 + ((pc ^ t) << 4)) = b.k[k];
+    *reinterpret_cast<u32x4_t*>(sk + t * 256 + ((pc ^ t) << 4)) = chunk_to_bf16<F>(b.k[k]);
   }
+  if constexpr (kGrouped) sks[lane] = half_bits_to_float(b.ks);  // [token][group]
   wave_lds_sync();
 
   // Score of (token tq, head hq).  The query of head h keeps its 16-byte chunk
   // c at slot c ^ h, so the four heads' broadcast reads use different banks.
   float s = 0.f;
+  if constexpr (kGrouped) {
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const u32x4_t kk = *reinterpret_cast<const u32x4_t*>(sk + tq * 256 + ((i ^ tq) << 4));
-    const u32x4_t qq = *reinterpret_cast<const u32x4_t*>(sq + hq * 256 + ((i ^ hq) << 4));
-    s = dot8_bf16(qq, kk, s);
+    for (int gr = 0; gr < 4; ++gr) {
+      float sg = 0.f;
+#pragma unroll
+      for (int i = 4 * gr; i < 4 * gr + 4; ++i) {
+        const u32x4_t kk = *reinterpret_cast<const u32x4_t*>(sk + tq * 256 + ((i ^ tq) << 4));
+        const u32x4_t qq = *reinterpret_cast<const u32x4_t*>(sq + hq * 256 + ((i ^ hq) << 4));
+        sg = dot8_bf16(qq, kk, sg);
+      }
+      s = fmaf(sks[tq * 4 + gr], sg, s);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const u32x4_t kk = *reinterpret_cast<const u32x4_t*>(sk + tq * 256 + ((i ^ tq) << 4));
+      const u32x4_t qq = *reinterpret_cast<const u32x4_t*>(sq + hq * 256 + ((i ^ hq) << 4));
+      s = dot8_bf16(qq, kk, s);
+    }
   }
   const float sl = (tq < valid) ? s * scale_log2 : -INFINITY;
   const float tmax = row16_max(sl);
@@ -136,8 +247,20 @@ __device__ __forceinline__ void consume_page(WaveState<G>& st, Page& b, const ui
     }
   }
 
-  // Weights of this lane's tokens t_k = 4k + pr, all heads, as bf16 pairs
-  // (t0, t1) and (t2, t3).
+  // V scale of this lane's tokens t_k = 4k + pr (its group pc / 4); zero
+  // past the end, where the stored scale may be anything.
+  float vsc[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    float x = 1.f;
+    // chunk 4 k + pr's group scale sits in lane 4 (4 k + pr) + pc / 4
+    if constexpr (kGrouped) x = half_bits_to_float((uint32_t)__shfl((int)b.vs, 16 * k + 4 * pr + (pc >> 2), 64));
+    if constexpr (F == kFmtFP8) x = v_scale;
+    vsc[k] = (4 * k + pr < valid) ? x : 0.f;
+  }
+
+  // Weights of this lane's tokens, all heads, as bf16 pairs (t0, t1) and
+  // (t2, t3), each times its V scale.
   uint32_t w01[G], w23[G];
   {
     const float4 p0 = *reinterpret_cast<const float4*>(sp + (0 + pr) * 4);
@@ -150,24 +273,32 @@ __device__ __forceinline__ void consume_page(WaveState<G>& st, Page& b, const ui
     const float a3[4] = {p3.x, p3.y, p3.z, p3.w};
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      w01[h] = pack_bf16x2(a0[h], a1[h]);
-      w23[h] = pack_bf16x2(a2[h], a3[h]);
+      if constexpr (F == kFmtBF16) {
+        w01[h] = pack_bf16x2(a0[h], a1[h]);
+        w23[h] = pack_bf16x2(a2[h], a3[h]);
+      } else {
+        w01[h] = pack_bf16x2(a0[h] * vsc[0], a1[h] * vsc[1]);
+        w23[h] = pack_bf16x2(a2[h] * vsc[2], a3[h] * vsc[3]);
+      }
     }
   }
 
-  // V of tokens past the end holds anything (NaN included): zero it.
+  // V as bf16; tokens past the end hold anything (NaN included): zero them.
+  u32x4_t vb[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) vb[k] = chunk_to_bf16<F>(b.v[k]);
   if (valid < kBlockSize) {
 #pragma unroll
     for (int k = 0; k < 4; ++k)
-      if (4 * k + pr >= valid) b.v[k] = u32x4_t{0u, 0u, 0u, 0u};
+      if (4 * k + pr >= valid) vb[k] = u32x4_t{0u, 0u, 0u, 0u};
   }
   // V pairs: dims (2w, 2w+1) of tokens (t0, t1) and (t2, t3).
 #pragma unroll
   for (int wd = 0; wd < 4; ++wd) {
-    const uint32_t lo01 = __builtin_amdgcn_perm(b.v[1][wd], b.v[0][wd], 0x05040100u);
-    const uint32_t hi01 = __builtin_amdgcn_perm(b.v[1][wd], b.v[0][wd], 0x07060302u);
-    const uint32_t lo23 = __builtin_amdgcn_perm(b.v[3][wd], b.v[2][wd], 0x05040100u);
-    const uint32_t hi23 = __builtin_amdgcn_perm(b.v[3][wd], b.v[2][wd], 0x07060302u);
+    const uint32_t lo01 = __builtin_amdgcn_perm(vb[1][wd], vb[0][wd], 0x05040100u);
+    const uint32_t hi01 = __builtin_amdgcn_perm(vb[1][wd], vb[0][wd], 0x07060302u);
+    const uint32_t lo23 = __builtin_amdgcn_perm(vb[3][wd], vb[2][wd], 0x05040100u);
+    const uint32_t hi23 = __builtin_amdgcn_perm(vb[3][wd], vb[2][wd], 0x07060302u);
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       st.acc[h][2 * wd] = dot2_bf16(w01[h], lo01, st.acc[h][2 * wd]);
@@ -192,13 +323,14 @@ __device__ __forceinline__ int q_row_scalar(const int32_t* q_lens, int seq) {
   return s;
 }
 
-template <int G>
+template <int G, int F>
 __global__ __launch_bounds__(kDecodeThreads, kDecodeWGsPerCU) void decode_kernel(DecodeParams p) {
   static_assert(G == 1 || G == 2 || G == 4, "group size");
   __shared__ __attribute__((aligned(16))) uint8_t s_k[kWaves][kTileBytes];
   __shared__ __attribute__((aligned(16))) uint8_t s_q[G][kHeadDim * 2];
   __shared__ __attribute__((aligned(16))) float s_p[kWaves][kBlockSize * 4];
   __shared__ __attribute__((aligned(16))) float s_alpha[kWaves][4];
+  __shared__ __attribute__((aligned(16))) float s_ks[kWaves][kBlockSize * 4];  // q8_0 / q4_0 K scales
   __shared__ __attribute__((aligned(16))) float s_acc[kWaves][4][G][kHeadDim];
   __shared__ float s_m[kWaves][G];
   __shared__ float s_l[kWaves][G];
@@ -225,8 +357,6 @@ __global__ __launch_bounds__(kDecodeThreads, kDecodeWGsPerCU) void decode_kernel
   const bool has_work = n > 0 && pstart < pend;
 
   const int32_t* bt = p.block_table + (size_t)seq * p.max_blocks;
-  const u32x4_t* kpool = reinterpret_cast<const u32x4_t*>(p.k);
-  const u32x4_t* vpool = reinterpret_cast<const u32x4_t*>(p.v);
   const int last_page = pend - 1;
   auto page_id = [&](int page) -> int32_t { return scalar_load_i32(bt, min(page, last_page)); };
 
@@ -242,21 +372,21 @@ __global__ __launch_bounds__(kDecodeThreads, kDecodeWGsPerCU) void decode_kernel
   // third pages.  Every load here is unconditional within the workgroup-
   // uniform has_work branch -- a wave with fewer than three pages re-reads a
   // valid page -- so the load counter's waits stay exact.
-  Page ring0, ring1, ring2;
+  Page<F> ring0, ring1, ring2;
   const int page0 = pstart + wave;
   const int cnt = (has_work && page0 < pend) ? (pend - page0 + kWaves - 1) / kWaves : 0;
   int q_row = 0;
   int32_t next_id = 0;
   if (has_work) {
-    issue_page(ring0, kpool, vpool, page_id(page0), g, p.num_kv_heads, lane);
+    issue_page<F>(ring0, p, page_id(page0), g, lane);
     issue_order_barrier();
     q_row = q_row_scalar(p.q_lens, seq);
     const int qh = (threadIdx.x >> 4) % G, qc = threadIdx.x & 15;
     const u32x4_t qchunk =
         reinterpret_cast<const u32x4_t*>(p.q)[((size_t)q_row * p.num_q_heads + h0 + qh) * 16 + qc];
     issue_order_barrier();
-    issue_page(ring1, kpool, vpool, page_id(page0 + kWaves), g, p.num_kv_heads, lane);
-    issue_page(ring2, kpool, vpool, page_id(page0 + 2 * kWaves), g, p.num_kv_heads, lane);
+    issue_page<F>(ring1, p, page_id(page0 + kWaves), g, lane);
+    issue_page<F>(ring2, p, page_id(page0 + 2 * kWaves), g, lane);
     next_id = page_id(page0 + 3 * kWaves);
     // Query of heads h0 .. h0+G-1 -> LDS, 16-byte chunk c of head h at slot c ^ h.
     if (threadIdx.x < G * 16) *reinterpret_cast<u32x4_t*>(&s_q[qh][(qc ^ qh) << 4]) = qchunk;
@@ -277,16 +407,18 @@ __global__ __launch_bounds__(kDecodeThreads, kDecodeWGsPerCU) void decode_kernel
     uint8_t* sk = s_k[wave];
     float* sp = s_p[wave];
     float* sa = s_alpha[wave];
+    float* sks = s_ks[wave];
     const uint8_t* sq = &s_q[0][0];
     // This wave's pages are page0 + 4k for k < cnt; page k lives in ring k % 3.
     // The main loop reissues unconditionally, so the (in-order) load counter
     // sees the same pattern on every trip and each wait leaves the other two
     // pages in flight; the last pages are peeled off.
     auto valid_of = [&](int k) { return min(kBlockSize, n - (page0 + kWaves * k) * kBlockSize); };
-#define PA_CONSUME(RING, K) consume_page<G>(st, RING, sq, sk, sp, sa, valid_of(K), p.scale_log2, lane)
+#define PA_CONSUME(RING, K) \
+  consume_page<G, F>(st, RING, sq, sk, sks, sp, sa, valid_of(K), p.scale_log2, p.v_scale, lane)
 #define PA_REISSUE(RING, K)                                          \
   {                                                                  \
-    issue_page(RING, kpool, vpool, next_id, g, p.num_kv_heads, lane); \
+    issue_page<F>(RING, p, next_id, g, lane);                        \
     next_id = page_id(page0 + kWaves * ((K) + 1));                   \
   }
     int k = 0;
@@ -443,14 +575,25 @@ __global__ __launch_bounds__(256) void zero_kernel(int32_t* __restrict__ x, size
 
 bool decode_supports_group(int group) { return group == 1 || group == 2 || group == 4; }
 
-hipError_t launch_decode(const DecodeParams& p, int group, unsigned grid, hipStream_t s) {
-  const void* fn = nullptr;
+template <int F>
+const void* decode_entry(int group) {
   switch (group) {
-    case 1: fn = reinterpret_cast<const void*>(&decode_kernel<1>); break;
-    case 2: fn = reinterpret_cast<const void*>(&decode_kernel<2>); break;
-    case 4: fn = reinterpret_cast<const void*>(&decode_kernel<4>); break;
-    default: return hipErrorInvalidValue;
+    case 1: return reinterpret_cast<const void*>(&decode_kernel<1, F>);
+    case 2: return reinterpret_cast<const void*>(&decode_kernel<2, F>);
+    case 4: return reinterpret_cast<const void*>(&decode_kernel<4, F>);
   }
+  return nullptr;
+}
+
+hipError_t launch_decode(const DecodeParams& p, int group, int format, unsigned grid, hipStream_t s) {
+  const void* fn = nullptr;
+  switch (format) {
+    case kFmtBF16: fn = decode_entry<kFmtBF16>(group); break;
+    case kFmtFP8: fn = decode_entry<kFmtFP8>(group); break;
+    case kFmtQ8: fn = decode_entry<kFmtQ8>(group); break;
+    case kFmtQ4: fn = decode_entry<kFmtQ4>(group); break;
+  }
+  if (!fn) return hipErrorInvalidValue;
   DecodeParams arg = p;
   void* args[] = {&arg};
   return hipLaunchKernel(fn, dim3(grid), dim3(kDecodeThreads), args, 0, s);

@@ -150,6 +150,18 @@ __device__ __forceinline__ u32x4_t stream_load(const u32x4_t* p) {
 #endif
 }
 
+#if PA_STREAM_NT
+__device__ __forceinline__ u32x2_t stream_load(const u32x2_t* p) { return __builtin_nontemporal_load(p); }
+__device__ __forceinline__ uint32_t stream_load(const uint32_t* p) { return __builtin_nontemporal_load(p); }
+__device__ __forceinline__ uint32_t stream_load(const uint16_t* p) {
+  return (uint32_t)__builtin_nontemporal_load(p);
+}
+#else
+__device__ __forceinline__ u32x2_t stream_load(const u32x2_t* p) { return *p; }
+__device__ __forceinline__ uint32_t stream_load(const uint32_t* p) { return *p; }
+__device__ __forceinline__ uint32_t stream_load(const uint16_t* p) { return (uint32_t)*p; }
+#endif
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 

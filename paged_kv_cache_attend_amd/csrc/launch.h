@@ -22,10 +22,19 @@ constexpr int kDecodeWaves = PA_DECODE_WAVES;          // waves per decode workg
 constexpr int kDecodeWGsPerCU = 8 / kDecodeWaves;      // resident per CU (2 waves per SIMD)
 
 // Split-KV decode: one workgroup per (KV head, slot, partition).
+// Page formats of the K/V caches (values of pa_kv_format in pa.h).
+constexpr int kFmtBF16 = 0;
+constexpr int kFmtFP8 = 1;   // OCP E4M3 codes, one fp32 scale per cache
+constexpr int kFmtQ8 = 2;    // q8_0: int8 codes, fp16 scale per 32 values
+constexpr int kFmtQ4 = 3;    // q4_0: 4-bit codes, fp16 scale per 32 values
+
 struct DecodeParams {
   const uint16_t* q;          // bf16 [total_q][Hq][128]
-  const uint16_t* k;          // bf16 [num_blocks][Hkv][16][128]
-  const uint16_t* v;
+  const uint16_t* k;          // page codes: bf16 [num_blocks][Hkv][16][128], or the
+  const uint16_t* v;          // byte layouts of the quantised formats
+  const uint16_t* k_scales;   // fp16 [num_blocks][Hkv][16][4] (q8_0, q4_0)
+  const uint16_t* v_scales;
+  float v_scale;              // FP8: per-cache V scale (K's is folded into scale_log2)
   const int32_t* block_table; // [num_seqs][max_blocks]
   const int32_t* ctx_lens;
   const int32_t* q_lens;
@@ -101,7 +110,7 @@ struct ValidateParams {
 // Decode kernels exist for these query-per-KV head group sizes.
 bool decode_supports_group(int group);
 constexpr int kDecodeThreads = 64 * kDecodeWaves;
-hipError_t launch_decode(const DecodeParams& p, int group, unsigned grid, hipStream_t s);
+hipError_t launch_decode(const DecodeParams& p, int group, int format, unsigned grid, hipStream_t s);
 hipError_t launch_zero_i32(int32_t* x, size_t n, hipStream_t s);
 
 constexpr int kChunkRows = 128;  // query rows per chunk workgroup
@@ -124,6 +133,15 @@ struct WriteParams {
   int32_t total_q;            // rows of k_new / v_new
 };
 
+// Quantising append: new bf16 rows -> codes (+ scales) at their positions.
+struct WriteQuantParams {
+  WriteParams w;              // rows, table, lengths; k_cache / v_cache hold the codes
+  uint16_t* k_scales;         // fp16 [num_blocks][Hkv][16][4] (q8_0, q4_0)
+  uint16_t* v_scales;
+  float k_scale;              // FP8: per-cache scales (codes of x / scale)
+  float v_scale;
+};
+
 struct CopyParams {
   const int32_t* src;         // [num_copies] block ids
   const int32_t* dst;
@@ -137,6 +155,7 @@ struct CopyParams {
 hipError_t launch_gather(const GatherParams& p, hipStream_t s);
 hipError_t launch_write_kv(const WriteParams& p, hipStream_t s);
 hipError_t launch_copy_blocks(const CopyParams& p, hipStream_t s);
+hipError_t launch_write_kv_quant(const WriteQuantParams& p, int format, hipStream_t s);
 hipError_t launch_validate(const ValidateParams& p, hipStream_t s);
 
 }  // namespace pa

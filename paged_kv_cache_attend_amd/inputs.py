@@ -172,6 +172,57 @@ class PagedProblem:
             pool[phys, :, self.block_fill[phys]:, :] = BF16_NAN
 
 
+# Quantised pages: random codes and scales drawn directly (not encoded from
+# values), so a test of the decoding side does not depend on any encoder.
+QUANT_FORMATS = ("fp8", "q8_0", "q4_0")
+FP16_NAN = np.uint16(0x7E00)
+E4M3_NAN = np.uint8(0x7F)
+
+
+def quant_pages(problem: PagedProblem, fmt: str, layer: int = 0):
+    """Random K and V pages of one layer in a quantised format.
+
+    Returns (k_codes, v_codes, k_scales, v_scales, k_scale, v_scale):
+    fp8 codes are uint8 E4M3 patterns (never NaN) with per-cache scales
+    1/64 (K, values up to 7) and 1/256 (V, values up to 1.75, so outputs stay
+    in the range the bf16 tolerances are derived for); q8_0 codes int8 in [-127, 127] with fp16 group scales in
+    [0.004, 0.0157]; q4_0 packed nibbles with fp16 group scales of either sign,
+    |scale| in [0.05, 0.25] -- every decoded value within +-2, like the bf16
+    inputs.  Past each block's valid slots (and in spare
+    blocks) FP8 codes are E4M3 NaN and group scales fp16 NaN: no kernel may
+    read them.
+    """
+    if fmt not in QUANT_FORMATS:
+        raise ValueError(fmt)
+    ss = child_seed(np.random.SeedSequence(SEED_BASE + 4000 + QUANT_FORMATS.index(fmt)),
+                    int(problem._value_seeds[layer].entropy % (1 << 31)) + layer)
+    rng = np.random.default_rng(ss)
+    nb, hkv, bs = problem.num_blocks, problem.num_kv_heads, problem.block_size
+    out = []
+    for _kv in range(2):
+        if fmt == "fp8":
+            c = rng.integers(0, 256, (nb, hkv, bs, 128), dtype=np.uint8)
+            c[(c & 0x7F) == 0x7F] &= np.uint8(0xF7)          # no NaN codes in live slots
+            sc = None
+        elif fmt == "q8_0":
+            c = rng.integers(-127, 128, (nb, hkv, bs, 128), dtype=np.int8)
+            sc = rng.uniform(0.004, 0.0157, (nb, hkv, bs, 4)).astype(np.float16).view(np.uint16)
+        else:
+            c = rng.integers(0, 256, (nb, hkv, bs, 64), dtype=np.uint8)
+            mag = rng.uniform(0.05, 0.25, (nb, hkv, bs, 4))
+            sign = np.where(rng.integers(0, 2, (nb, hkv, bs, 4)) == 0, -1.0, 1.0)
+            sc = (mag * sign).astype(np.float16).view(np.uint16)
+        for phys in np.nonzero(problem.block_fill < bs)[0]:
+            f = problem.block_fill[phys]
+            if fmt == "fp8":
+                c[phys, :, f:, :] = E4M3_NAN
+            else:
+                sc[phys, :, f:, :] = FP16_NAN
+        out.append((c, sc))
+    (kc, ks), (vc, vs) = out
+    return kc, vc, ks, vs, 1.0 / 64, 1.0 / 256
+
+
 def make_problem(name: str, seed: int, ctx_lens, q_lens, num_q_heads: int, num_kv_heads: int,
                  head_dim: int = 128, block_size: int = 16, num_layers: int = 1,
                  shared_prefix_tokens: int = 0, max_blocks_per_seq: int | None = None,

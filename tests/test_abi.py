@@ -145,7 +145,13 @@ def test_auto_partitions_cover_the_chip(lib):
     s = _shape(num_seqs=16, total_q=16, max_blocks_per_seq=144, max_ctx_len=2303, num_blocks=2592)
     ws, parts = pk.plan(s)
     assert parts == 2
-    assert ws == _ws_bytes(16, 8, parts, 16 * 32)
+    # compressed pages prefer the four-way split; the workspace covers both
+    lib = pk.load()
+    assert lib.pa_num_partitions_kv(ctypes.byref(s), pk.KV_BF16) == 2
+    for fmt in (pk.KV_FP8_E4M3, pk.KV_Q8_0, pk.KV_Q4_0):
+        assert lib.pa_num_partitions_kv(ctypes.byref(s), fmt) == 4
+    assert lib.pa_num_partitions_kv(ctypes.byref(s), 9) == 0
+    assert ws == _ws_bytes(16, 8, 4, 16 * 32)
 
 
 @pytest.mark.parametrize("num_seqs,ctx,parts", [
@@ -251,3 +257,46 @@ def test_pool_null_handles(lib):
     assert lib.pa_pool_retire(None, 0) == pk.Status.ERR_NULL_ARG
     assert lib.pa_pool_get_stats(None, ctypes.byref(st)) == pk.Status.ERR_NULL_ARG
     lib.pa_pool_destroy(None)
+
+
+def _kv(fmt, scales=True, k_scale=1.0, v_scale=1.0, reserved=0):
+    s = FAKE.value if scales else None
+    return pk.KVCache(fmt, reserved, FAKE.value, FAKE.value, s, s, k_scale, v_scale)
+
+
+def test_attend_kv_host_errors(lib):
+    s = _shape()
+    args = (FAKE, FAKE, FAKE, FAKE, ctypes.c_float(0.1), FAKE, None, FAKE, ctypes.c_size_t(1 << 30), None)
+    f = lib.pa_attend_kv
+    assert f(ctypes.byref(s), None, *args) == pk.Status.ERR_NULL_ARG
+    assert f(ctypes.byref(s), ctypes.byref(_kv(7)), *args) == pk.Status.ERR_BAD_SHAPE
+    assert f(ctypes.byref(s), ctypes.byref(_kv(pk.KV_Q8_0, reserved=1)), *args) == pk.Status.ERR_BAD_SHAPE
+    for ks in (0.0, -1.0, math.inf, math.nan):
+        assert f(ctypes.byref(s), ctypes.byref(_kv(pk.KV_FP8_E4M3, k_scale=ks)), *args) == pk.Status.ERR_BAD_SHAPE
+    for fmt in (pk.KV_Q8_0, pk.KV_Q4_0):
+        assert f(ctypes.byref(s), ctypes.byref(_kv(fmt, scales=False)), *args) == pk.Status.ERR_NULL_ARG
+    # quantised pages take the decode path only
+    chunk = _shape(total_q=8, max_q_len=2)
+    assert f(ctypes.byref(chunk), ctypes.byref(_kv(pk.KV_Q8_0)), *args) == pk.Status.ERR_UNSUPPORTED
+    # a bad shape is reported as for pa_attend
+    assert f(ctypes.byref(_shape(head_dim=64)), ctypes.byref(_kv(pk.KV_Q8_0)), *args) == pk.Status.ERR_UNSUPPORTED
+
+
+def test_write_kv_cache_host_errors(lib):
+    s = _shape()
+    args = (FAKE, FAKE, FAKE, FAKE, FAKE, None)
+    f = lib.pa_write_kv_cache
+    assert f(ctypes.byref(s), None, *args) == pk.Status.ERR_NULL_ARG
+    assert f(ctypes.byref(s), ctypes.byref(_kv(4)), *args) == pk.Status.ERR_BAD_SHAPE
+    assert f(ctypes.byref(s), ctypes.byref(_kv(pk.KV_Q4_0, scales=False)), *args) == pk.Status.ERR_NULL_ARG
+    assert f(ctypes.byref(s), ctypes.byref(_kv(pk.KV_FP8_E4M3, v_scale=0.0)), *args) == pk.Status.ERR_BAD_SHAPE
+    assert f(ctypes.byref(s), ctypes.byref(_kv(pk.KV_Q8_0)), None, FAKE, FAKE, FAKE, FAKE, None) == \
+        pk.Status.ERR_NULL_ARG
+    empty = _shape(num_seqs=0)
+    assert f(ctypes.byref(empty), ctypes.byref(_kv(pk.KV_Q8_0)), *args) == pk.Status.OK
+
+
+def test_kv_cache_struct_layout():
+    # int32 x 2, four pointers, two floats: 8 + 32 + 8 = 48 bytes
+    assert ctypes.sizeof(pk.KVCache) == 48
+    assert pk.KVCache.k_codes.offset == 8 and pk.KVCache.k_scale.offset == 40

@@ -80,6 +80,7 @@ def test_q4_0_codes_are_the_nearest():
     rng = np.random.default_rng(3)
     x = (rng.standard_normal((6, 128)) * 5).astype(np.float32)
     x[2, 0:32] = np.linspace(-1, 1, 32, dtype=np.float32)
+    x[4, 64:96] = 0.0                    # a zero group: scale stored as +0, codes 8
     packed, sb = quant.q4_0_encode(x)
     d = quant.fp16_value(sb)
     nib = np.empty((6, 128), dtype=np.int64)
@@ -90,7 +91,11 @@ def test_q4_0_codes_are_the_nearest():
         for g in range(4):
             grp = x[r, 32 * g:32 * g + 32]
             m = grp[np.argmax(np.abs(grp))]
-            assert sb[r, g] == np.float32(m / np.float32(-8)).astype(np.float16).view(np.uint16)
+            want_bits = np.float32(m / np.float32(-8)).astype(np.float16).view(np.uint16)
+            assert sb[r, g] == (0 if m == 0 else want_bits)
+            if d[r, g] == 0:
+                assert (nib[r, 32 * g:32 * g + 32] == 8).all()   # zero scale: code 0
+                continue
             for i in range(32):
                 want = _nearest_code(np.float32(grp[i]), np.float32(d[r, g]), allc) + 8
                 assert nib[r, 32 * g + i] == want, (r, g, i)
