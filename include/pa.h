@@ -182,6 +182,54 @@ pa_status pa_validate(const pa_shape* shape, const int32_t* block_table,
                       int32_t* error_word, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Prefix-grouped (cascade) decode
+ * ------------------------------------------------------------------------
+ * Requests that share a prefix reference the same physical blocks
+ * (section 8.3.2, Figs. 8-13 / 8-14: one copy of the common context serves
+ * several requests).  pa_attend_prefix computes exactly what pa_attend
+ * computes, but reads each group's shared pages once per KV head for all of
+ * the group's query rows: a first pass attends the group's rows -- (member,
+ * query head) pairs -- to the shared pages on the matrix cores; the decode
+ * pass then attends each member to its own remaining keys and merges both
+ * by log-sum-exp.
+ *
+ * Groups are runs of consecutive slots [group_start[k], group_start[k+1]).
+ * Preconditions for group k with prefix length L = prefix_len[k] (a multiple
+ * of 16): for every member r, block_table[r][0 .. L/16) equals row
+ * group_start[k]'s first L/16 entries, and ctx_lens[r] >= L for members with
+ * new tokens.  Slots outside every group have no prefix.  Decode only
+ * (max_q_len == 1, 1, 2 or 4 query heads per KV head): other shapes return
+ * PA_ERR_UNSUPPORTED. */
+typedef struct pa_prefix_groups {
+  int32_t num_groups;
+  int32_t max_members;         /* >= slots in any group */
+  int32_t max_prefix_len;      /* >= every prefix_len; a multiple of 16, <= max_ctx_len */
+  int32_t min_prefix_len;      /* <= the prefix of every slot with new tokens (0 if some have
+                                  none); a multiple of 16.  Sizes the suffix split only. */
+  int32_t reserved;            /* must be 0 */
+  int32_t reserved2;
+  const int32_t* group_start;  /* device int32 [num_groups + 1], ascending */
+  const int32_t* prefix_len;   /* device int32 [num_groups] */
+} pa_prefix_groups;
+
+/* Workspace bytes for pa_attend_prefix (never 0 for a valid shape); 0 for an
+ * invalid shape or group description. */
+size_t pa_prefix_workspace_size(const pa_shape* shape, const pa_prefix_groups* groups);
+
+/* Prepare a workspace for pa_attend_prefix with this shape and group sizes
+ * (zeroes its counters); as pa_workspace_init. */
+pa_status pa_prefix_workspace_init(const pa_shape* shape, const pa_prefix_groups* groups,
+                                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* Attention as pa_attend (same arguments and results), reading shared
+ * prefixes once per group.  Errors as for pa_attend, plus PA_ERR_BAD_SHAPE
+ * for an inconsistent group description. */
+pa_status pa_attend_prefix(const pa_shape* shape, const pa_prefix_groups* groups, const void* q,
+                           const void* k_cache, const void* v_cache, const int32_t* block_table,
+                           const int32_t* ctx_lens, const int32_t* q_lens, float scale, void* out,
+                           float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * Quantised KV pages
  * ------------------------------------------------------------------------
  * The chapter's section 8.4.2 ("KV compression and read cost", Fig. 8-23)

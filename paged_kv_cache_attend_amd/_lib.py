@@ -26,7 +26,8 @@ EXPORTS = ("pa_workspace_size", "pa_workspace_init", "pa_num_partitions", "pa_at
            "pa_gather_kv", "pa_validate", "pa_write_kv", "pa_copy_blocks", "pa_pool_create",
            "pa_pool_destroy", "pa_pool_append", "pa_pool_fork", "pa_pool_release", "pa_pool_retire",
            "pa_pool_length", "pa_pool_block_table", "pa_pool_refcount", "pa_pool_get_stats",
-           "pa_attend_kv", "pa_write_kv_cache", "pa_num_partitions_kv", "pa_status_string")
+           "pa_attend_kv", "pa_write_kv_cache", "pa_num_partitions_kv", "pa_prefix_workspace_size",
+           "pa_prefix_workspace_init", "pa_attend_prefix", "pa_status_string")
 
 # pa_kv_format
 KV_BF16 = 0
@@ -61,6 +62,21 @@ class PoolStats(ctypes.Structure):
         ("used_blocks", ctypes.c_int32),
         ("reserved", ctypes.c_int32),
         ("references", ctypes.c_int64),
+    ]
+
+
+class PrefixGroups(ctypes.Structure):
+    """Mirror of ``pa_prefix_groups``."""
+
+    _fields_ = [
+        ("num_groups", ctypes.c_int32),
+        ("max_members", ctypes.c_int32),
+        ("max_prefix_len", ctypes.c_int32),
+        ("min_prefix_len", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+        ("reserved2", ctypes.c_int32),
+        ("group_start", ctypes.c_void_p),
+        ("prefix_len", ctypes.c_void_p),
     ]
 
 
@@ -164,6 +180,13 @@ def load():
     lib.pa_attend_kv.restype = ctypes.c_int
     lib.pa_write_kv_cache.argtypes = [shp, kvp, P, P, P, P, P, P]
     lib.pa_write_kv_cache.restype = ctypes.c_int
+    pgp = ctypes.POINTER(PrefixGroups)
+    lib.pa_prefix_workspace_size.argtypes = [shp, pgp]
+    lib.pa_prefix_workspace_size.restype = ctypes.c_size_t
+    lib.pa_prefix_workspace_init.argtypes = [shp, pgp, P, ctypes.c_size_t, P]
+    lib.pa_prefix_workspace_init.restype = ctypes.c_int
+    lib.pa_attend_prefix.argtypes = [shp, pgp, P, P, P, P, P, P, ctypes.c_float, P, P, P, ctypes.c_size_t, P]
+    lib.pa_attend_prefix.restype = ctypes.c_int
     lib.pa_status_string.argtypes = [ctypes.c_int]
     lib.pa_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -382,6 +405,63 @@ def copy_blocks(src, dst, k_cache, v_cache, *, stream=None):
     st = load().pa_copy_blocks(int(src.shape[0]), _ptr(src), _ptr(dst), hkv, nb, _ptr(k_cache),
                                _ptr(v_cache), _stream_handle(dev, stream))
     _check(st, "pa_copy_blocks")
+
+
+def attend_prefix(q, k_cache, v_cache, block_table, ctx_lens, q_lens, scale, out, lse=None, *,
+                  group_start, prefix_len, max_members: int, max_prefix_len: int, min_prefix_len: int = 0,
+                  max_ctx_len: int, partition_size: int = 0, workspace=None, stream=None,
+                  prepared: bool = False):
+    """``pa_attend_prefix``: pa_attend with groups of consecutive slots that
+    share a prefix (group_start int32 [num_groups + 1], prefix_len int32
+    [num_groups], on the device).  With ``prepared=True`` returns a
+    launchable object instead of launching once."""
+    torch = _torch()
+    dev = q.device
+    for t, name, dt, nd in ((q, "q", torch.bfloat16, 3), (out, "out", torch.bfloat16, 3),
+                            (k_cache, "k_cache", torch.bfloat16, 4), (v_cache, "v_cache", torch.bfloat16, 4),
+                            (block_table, "block_table", torch.int32, 2), (ctx_lens, "ctx_lens", torch.int32, 1),
+                            (q_lens, "q_lens", torch.int32, 1), (group_start, "group_start", torch.int32, 1),
+                            (prefix_len, "prefix_len", torch.int32, 1)):
+        _need(t, name, dt, dev, nd)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, dev, 2)
+    if group_start.shape[0] != prefix_len.shape[0] + 1:
+        raise ValueError("group_start must have one entry more than prefix_len")
+    total_q, hq, d = q.shape
+    nb, hkv, bs, _ = k_cache.shape
+    shape = make_shape(block_table.shape[0], total_q, hq, hkv, block_table.shape[1], 1, max_ctx_len, nb,
+                       partition_size, head_dim=d, block_size=bs)
+    groups = PrefixGroups(int(prefix_len.shape[0]), int(max_members), int(max_prefix_len), int(min_prefix_len),
+                          0, 0, _ptr(group_start).value, _ptr(prefix_len).value)
+    lib = load()
+    need = int(lib.pa_prefix_workspace_size(ctypes.byref(shape), ctypes.byref(groups)))
+    if need == 0:
+        raise PaError(Status.ERR_BAD_SHAPE, "pa_prefix_workspace_size")
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        _check(lib.pa_prefix_workspace_init(ctypes.byref(shape), ctypes.byref(groups), _ptr(workspace),
+                                            ctypes.c_size_t(need), _stream_handle(dev, stream)),
+               "pa_prefix_workspace_init")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    args = [ctypes.byref(shape), ctypes.byref(groups), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+            _ptr(ctx_lens), _ptr(q_lens), ctypes.c_float(float(scale)), _ptr(out), _ptr(lse), _ptr(workspace),
+            ctypes.c_size_t(ws_bytes)]
+    fn = lib.pa_attend_prefix
+
+    class _Call:
+        keep = (shape, groups, q, k_cache, v_cache, block_table, ctx_lens, q_lens, group_start, prefix_len,
+                out, lse, workspace)
+
+        def launch(self, s=None):
+            st = fn(*args, _stream_handle(dev, s))
+            if st:
+                raise PaError(st, "pa_attend_prefix")
+
+    call = _Call()
+    if prepared:
+        return call
+    call.launch(stream)
+    return out, lse
 
 
 class QuantCache:

@@ -150,6 +150,38 @@ pa_status make_plan(const pa_shape* s, Plan* plan, bool compressed = false) {
 
 namespace {
 
+// Kernel arguments of the decode path for a plan; `ws` holds the split-KV
+// region at offset 0.
+DecodeParams decode_params(const pa_shape* shape, const Plan& plan, const pa_kv_cache& kv,
+                           const void* q, const int32_t* block_table, const int32_t* ctx_lens,
+                           const int32_t* q_lens, float scale_log2, void* out, float* lse, char* ws) {
+  DecodeParams d = {};
+  d.q = static_cast<const uint16_t*>(q);
+  d.k = static_cast<const uint16_t*>(kv.k_codes);
+  d.v = static_cast<const uint16_t*>(kv.v_codes);
+  d.block_table = block_table;
+  d.ctx_lens = ctx_lens;
+  d.q_lens = q_lens;
+  d.out = static_cast<uint16_t*>(out);
+  d.lse = lse;
+  const bool split = plan.num_parts > 1;
+  d.counters = split ? reinterpret_cast<int32_t*>(ws) : nullptr;
+  d.part_lse = split ? reinterpret_cast<float*>(ws + plan.lse_offset) : nullptr;
+  d.part_out = split ? reinterpret_cast<float*>(ws + plan.out_offset) : nullptr;
+  d.scale_log2 = scale_log2;
+  d.num_seqs = shape->num_seqs;
+  d.num_q_heads = shape->num_q_heads;
+  d.num_kv_heads = shape->num_kv_heads;
+  d.max_blocks = shape->max_blocks_per_seq;
+  d.total_q = shape->total_q;
+  d.part_pages = plan.part_pages;
+  d.num_parts = plan.num_parts;
+  d.k_scales = static_cast<const uint16_t*>(kv.k_scales);
+  d.v_scales = static_cast<const uint16_t*>(kv.v_scales);
+  d.v_scale = kv.format == kFmtFP8 ? kv.v_scale : 1.f;
+  return d;
+}
+
 // The attention call for any page format.  `kv` carries the codes (and
 // scales); bf16 caches take either path, quantised ones the decode path.
 pa_status attend_impl(const pa_shape* shape, const pa_kv_cache& kv, const void* q,
@@ -177,36 +209,13 @@ pa_status attend_impl(const pa_shape* shape, const pa_kv_cache& kv, const void* 
   const float scale_log2 = scale * (kv.format == kFmtFP8 ? kv.k_scale : 1.f) * kLog2e;
 
   if (plan.decode) {
-    DecodeParams d;
-    d.q = static_cast<const uint16_t*>(q);
-    d.k = static_cast<const uint16_t*>(k_cache);
-    d.v = static_cast<const uint16_t*>(v_cache);
-    d.block_table = block_table;
-    d.ctx_lens = ctx_lens;
-    d.q_lens = q_lens;
-    d.out = static_cast<uint16_t*>(out);
-    d.lse = lse;
-    char* ws = static_cast<char*>(workspace);
-    const bool split = plan.num_parts > 1;
-    d.counters = split ? reinterpret_cast<int32_t*>(ws) : nullptr;
-    d.part_lse = split ? reinterpret_cast<float*>(ws + plan.lse_offset) : nullptr;
-    d.part_out = split ? reinterpret_cast<float*>(ws + plan.out_offset) : nullptr;
-    d.scale_log2 = scale_log2;
-    d.num_seqs = shape->num_seqs;
-    d.num_q_heads = shape->num_q_heads;
-    d.num_kv_heads = shape->num_kv_heads;
-    d.max_blocks = shape->max_blocks_per_seq;
-    d.total_q = shape->total_q;
-    d.part_pages = plan.part_pages;
-    d.num_parts = plan.num_parts;
-    d.k_scales = static_cast<const uint16_t*>(kv.k_scales);
-    d.v_scales = static_cast<const uint16_t*>(kv.v_scales);
-    d.v_scale = kv.format == kFmtFP8 ? kv.v_scale : 1.f;
+    const DecodeParams d = decode_params(shape, plan, kv, q, block_table, ctx_lens, q_lens, scale_log2,
+                                         out, lse, static_cast<char*>(workspace));
     if (launch_decode(d, plan.group, kv.format, plan.grid, s) != hipSuccess) return PA_ERR_LAUNCH;
     return PA_OK;
   }
 
-  ChunkParams c;
+  ChunkParams c = {};
   c.q = static_cast<const uint16_t*>(q);
   c.k = static_cast<const uint16_t*>(k_cache);
   c.v = static_cast<const uint16_t*>(v_cache);
@@ -226,6 +235,67 @@ pa_status attend_impl(const pa_shape* shape, const pa_kv_cache& kv, const void* 
   return PA_OK;
 }
 
+
+// Prefix-grouped decode: the suffix pass is the decode path with keys
+// starting after each slot's prefix (sized for the longest possible suffix,
+// max_ctx_len - min_prefix_len); the prefix pass gets as many partitions per
+// (group, KV head, row tile) as fill one round of CUs, at most 16 (the
+// partials are merged in one batch per row), with at least one 32-key tile
+// each.  Workspace: [suffix split-KV region][slot prefix lengths]
+// [prefix partial LSE][prefix partial out].
+#ifndef PA_PREFIX_MAX_PARTS
+#define PA_PREFIX_MAX_PARTS 16
+#endif
+constexpr int kPrefixMaxParts = PA_PREFIX_MAX_PARTS;
+
+struct PrefixPlan {
+  Plan suffix;
+  int row_tiles = 0;
+  int pre_parts = 1;
+  int pre_pages = 1;
+  unsigned pre_grid = 0;
+  size_t plen_offset = 0, pre_lse_offset = 0, pre_out_offset = 0, ws_bytes = 0;
+};
+
+pa_status make_prefix_plan(const pa_shape* s, const pa_prefix_groups* gr, PrefixPlan* out) {
+  pa_status st = check_shape(s);
+  if (st != PA_OK) return st;
+  if (!gr) return PA_ERR_NULL_ARG;
+  if (gr->num_groups < 0 || gr->max_members < 0 || gr->max_prefix_len < 0 || gr->min_prefix_len < 0 ||
+      gr->reserved != 0)
+    return PA_ERR_BAD_SHAPE;
+  if (gr->max_prefix_len % kBlockSize || gr->min_prefix_len % kBlockSize) return PA_ERR_BAD_SHAPE;
+  if (gr->min_prefix_len > gr->max_prefix_len || gr->max_prefix_len > s->max_ctx_len) return PA_ERR_BAD_SHAPE;
+  if (gr->max_members > s->num_seqs || gr->num_groups > s->num_seqs) return PA_ERR_BAD_SHAPE;
+  const int G = s->num_q_heads / s->num_kv_heads;
+  if (s->max_q_len > 1 || !decode_supports_group(G)) return PA_ERR_UNSUPPORTED;
+  PrefixPlan pp;
+  pa_shape suf = *s;
+  suf.max_ctx_len = s->max_ctx_len - gr->min_prefix_len;
+  if (suf.max_ctx_len < kBlockSize) suf.max_ctx_len = kBlockSize;
+  st = make_plan(&suf, &pp.suffix);
+  if (st != PA_OK) return st;
+  const size_t rows = (size_t)s->total_q * s->num_q_heads;
+  pp.row_tiles = ceil_div(gr->max_members * G, 64);
+  const int max_pages = gr->max_prefix_len / kBlockSize;
+  const long long base = (long long)gr->num_groups * s->num_kv_heads * pp.row_tiles;
+  if (base > 0 && max_pages > 0) {
+    long long parts = (long long)kNumCUs / base;
+    parts = parts < 1 ? 1 : (parts > kPrefixMaxParts ? kPrefixMaxParts : parts);
+    if (parts > ceil_div(max_pages, 2)) parts = ceil_div(max_pages, 2);
+    pp.pre_pages = ceil_div(max_pages, (int)parts);
+    pp.pre_parts = ceil_div(max_pages, pp.pre_pages);
+    const long long grid = base * pp.pre_parts;
+    if (grid + 1 > INT_MAX) return PA_ERR_UNSUPPORTED;
+    pp.pre_grid = (unsigned)grid;
+  }
+  pp.plen_offset = align256(pp.suffix.ws_bytes);
+  pp.pre_lse_offset = pp.plen_offset + align256((size_t)s->num_seqs * sizeof(int32_t));
+  pp.pre_out_offset = pp.pre_lse_offset + align256((size_t)pp.pre_parts * rows * sizeof(float));
+  pp.ws_bytes = pp.pre_out_offset + (size_t)pp.pre_parts * rows * kHeadDim * sizeof(float);
+  *out = pp;
+  return PA_OK;
+}
 
 }  // namespace
 
@@ -291,7 +361,7 @@ pa_status pa_combine(int32_t num_partials, int32_t rows, int32_t head_dim,
   if ((long long)rows * head_dim * num_partials > (long long)1 << 40) return PA_ERR_UNSUPPORTED;
   if (rows == 0) return PA_OK;
   if (!partial_out || !partial_lse || !out) return PA_ERR_NULL_ARG;
-  CombineParams c;
+  CombineParams c = {};
   c.part_out = partial_out;
   c.part_lse = partial_lse;
   c.out = static_cast<uint16_t*>(out);
@@ -309,7 +379,7 @@ pa_status pa_gather_kv(const pa_shape* shape, const void* cache, const int32_t* 
   if (st != PA_OK) return st;
   if (shape->num_seqs == 0 || shape->max_ctx_len == 0) return PA_OK;
   if (!cache || !block_table || !ctx_lens || !dst) return PA_ERR_NULL_ARG;
-  GatherParams g;
+  GatherParams g = {};
   g.cache = static_cast<const uint16_t*>(cache);
   g.block_table = block_table;
   g.ctx_lens = ctx_lens;
@@ -329,7 +399,7 @@ pa_status pa_validate(const pa_shape* shape, const int32_t* block_table, const i
   if (st != PA_OK) return st;
   if (!error_word) return PA_ERR_NULL_ARG;
   if (shape->num_seqs > 0 && (!block_table || !ctx_lens || !q_lens)) return PA_ERR_NULL_ARG;
-  ValidateParams v;
+  ValidateParams v = {};
   v.block_table = block_table;
   v.ctx_lens = ctx_lens;
   v.q_lens = q_lens;
@@ -352,7 +422,7 @@ pa_status pa_write_kv(const pa_shape* shape, const void* k_new, const void* v_ne
   if (shape->num_seqs == 0 || shape->total_q == 0 || shape->max_q_len == 0) return PA_OK;
   if (!k_new || !v_new || !block_table || !ctx_lens || !q_lens || !k_cache || !v_cache)
     return PA_ERR_NULL_ARG;
-  WriteParams w;
+  WriteParams w = {};
   w.k_new = static_cast<const uint16_t*>(k_new);
   w.v_new = static_cast<const uint16_t*>(v_new);
   w.block_table = block_table;
@@ -378,7 +448,7 @@ pa_status pa_copy_blocks(int32_t num_copies, const int32_t* src, const int32_t* 
   if ((long long)num_copies * num_kv_heads * 2 > INT_MAX) return PA_ERR_UNSUPPORTED;
   if (num_copies == 0) return PA_OK;
   if (!src || !dst || !k_cache || !v_cache) return PA_ERR_NULL_ARG;
-  CopyParams c;
+  CopyParams c = {};
   c.src = src;
   c.dst = dst;
   c.k_cache = static_cast<uint16_t*>(k_cache);
@@ -418,7 +488,7 @@ pa_status pa_write_kv_cache(const pa_shape* shape, const pa_kv_cache* cache, con
   const bool grouped = cache->format == kFmtQ8 || cache->format == kFmtQ4;
   if (grouped && (!cache->k_scales || !cache->v_scales)) return PA_ERR_NULL_ARG;
   if ((long long)ceil_div(shape->max_q_len, 16) * shape->num_seqs > INT_MAX) return PA_ERR_UNSUPPORTED;
-  WriteQuantParams w;
+  WriteQuantParams w = {};
   w.w.k_new = static_cast<const uint16_t*>(k_new);
   w.w.v_new = static_cast<const uint16_t*>(v_new);
   w.w.block_table = block_table;
@@ -438,6 +508,80 @@ pa_status pa_write_kv_cache(const pa_shape* shape, const pa_kv_cache* cache, con
   w.v_scale = cache->v_scale;
   if (launch_write_kv_quant(w, cache->format, static_cast<hipStream_t>(stream)) != hipSuccess)
     return PA_ERR_LAUNCH;
+  return PA_OK;
+}
+
+size_t pa_prefix_workspace_size(const pa_shape* shape, const pa_prefix_groups* groups) {
+  PrefixPlan pp;
+  if (make_prefix_plan(shape, groups, &pp) != PA_OK) return 0;
+  return pp.ws_bytes;
+}
+
+pa_status pa_prefix_workspace_init(const pa_shape* shape, const pa_prefix_groups* groups,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+  PrefixPlan pp;
+  const pa_status st = make_prefix_plan(shape, groups, &pp);
+  if (st != PA_OK) return st;
+  if (!workspace) return PA_ERR_NULL_ARG;
+  if (workspace_bytes < pp.ws_bytes) return PA_ERR_WORKSPACE_TOO_SMALL;
+  if (pp.suffix.counters_bytes == 0) return PA_OK;
+  if (launch_zero_i32(static_cast<int32_t*>(workspace), pp.suffix.counters_bytes / sizeof(int32_t),
+                      static_cast<hipStream_t>(stream)) != hipSuccess)
+    return PA_ERR_LAUNCH;
+  return PA_OK;
+}
+
+pa_status pa_attend_prefix(const pa_shape* shape, const pa_prefix_groups* groups, const void* q,
+                           const void* k_cache, const void* v_cache, const int32_t* block_table,
+                           const int32_t* ctx_lens, const int32_t* q_lens, float scale, void* out,
+                           float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  PrefixPlan pp;
+  const pa_status st = make_prefix_plan(shape, groups, &pp);
+  if (st != PA_OK) return st;
+  if (!std::isfinite(scale)) return PA_ERR_BAD_SHAPE;
+  if (pp.suffix.empty) return PA_OK;
+  if (!q || !k_cache || !v_cache || !block_table || !ctx_lens || !q_lens || !out) return PA_ERR_NULL_ARG;
+  if (groups->num_groups > 0 && (!groups->group_start || !groups->prefix_len)) return PA_ERR_NULL_ARG;
+  if (!workspace) return PA_ERR_NULL_ARG;
+  if (workspace_bytes < pp.ws_bytes) return PA_ERR_WORKSPACE_TOO_SMALL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  const float scale_log2 = scale * kLog2e;
+
+  PrefixParams pr = {};
+  pr.q = static_cast<const uint16_t*>(q);
+  pr.k = static_cast<const uint16_t*>(k_cache);
+  pr.v = static_cast<const uint16_t*>(v_cache);
+  pr.block_table = block_table;
+  pr.ctx_lens = ctx_lens;
+  pr.q_lens = q_lens;
+  pr.group_start = groups->group_start;
+  pr.prefix_len = groups->prefix_len;
+  pr.pre_out = reinterpret_cast<float*>(ws + pp.pre_out_offset);
+  pr.pre_lse = reinterpret_cast<float*>(ws + pp.pre_lse_offset);
+  pr.slot_plen = reinterpret_cast<int32_t*>(ws + pp.plen_offset);
+  pr.scale_log2 = scale_log2;
+  pr.num_seqs = shape->num_seqs;
+  pr.num_q_heads = shape->num_q_heads;
+  pr.num_kv_heads = shape->num_kv_heads;
+  pr.max_blocks = shape->max_blocks_per_seq;
+  pr.total_q = shape->total_q;
+  pr.num_groups = groups->num_groups;
+  pr.row_tiles = pp.row_tiles > 0 ? pp.row_tiles : 1;
+  pr.pre_parts = pp.pre_parts;
+  pr.part_pages = pp.pre_pages;
+  if (launch_prefix(pr, pp.pre_grid, s) != hipSuccess) return PA_ERR_LAUNCH;
+
+  pa_kv_cache kv = {};
+  kv.format = kFmtBF16;
+  kv.k_codes = const_cast<void*>(k_cache);
+  kv.v_codes = const_cast<void*>(v_cache);
+  DecodeParams d = decode_params(shape, pp.suffix, kv, q, block_table, ctx_lens, q_lens, scale_log2, out, lse, ws);
+  d.slot_plen = pr.slot_plen;
+  d.pre_out = pr.pre_out;
+  d.pre_lse = pr.pre_lse;
+  d.pre_parts = pp.pre_grid > 0 ? pp.pre_parts : 0;
+  if (launch_decode(d, pp.suffix.group, kFmtBF16, pp.suffix.grid, s) != hipSuccess) return PA_ERR_LAUNCH;
   return PA_OK;
 }
 

@@ -352,8 +352,13 @@ __global__ __launch_bounds__(kDecodeThreads, kDecodeWGsPerCU) void decode_kernel
   if (m <= 0) return;  // no row: nothing to write, no partial to count
   const int n = scalar_load_i32(p.ctx_lens, seq);
   const int npages = (n + kBlockSize - 1) / kBlockSize;
-  const int pstart = part * p.part_pages;
-  const int pend = min(npages, pstart + p.part_pages);
+  // Prefix-grouped decode: this slot's keys start after its shared prefix,
+  // whose partials the prefix pass has written; the last partition runs to
+  // the slot's end whatever the prefix length.
+  const int plen = p.slot_plen ? scalar_load_i32(p.slot_plen, seq) : 0;
+  const int npre = (plen > 0 && n > 0) ? p.pre_parts : 0;
+  const int pstart = plen / kBlockSize + part * p.part_pages;
+  const int pend = part == P - 1 ? npages : min(npages, pstart + p.part_pages);
   const bool has_work = n > 0 && pstart < pend;
 
   const int32_t* bt = p.block_table + (size_t)seq * p.max_blocks;
@@ -492,11 +497,56 @@ __global__ __launch_bounds__(kDecodeThreads, kDecodeWGsPerCU) void decode_kernel
     }
   }
 
+  // Online log-sum-exp merge state (M, W, a0, a1): the result is a / W with
+  // LSE M + ln W.  A partial with LSE = -inf weighs 0 and is never read.
+  auto fold = [](float& M, float& W, float& a0, float& a1, float l, float o0, float o1) {
+    if (l == -INFINITY) return;
+    const float M2 = fmaxf(M, l);
+    const float sc = fast_exp2((M - M2) * 1.4426950408889634f);  // 0 when M = -inf
+    const float w = fast_exp2((l - M2) * 1.4426950408889634f);
+    W = fmaf(W, sc, w);
+    a0 = fmaf(a0, sc, w * o0);
+    a1 = fmaf(a1, sc, w * o1);
+    M = M2;
+  };
+  // The prefix pass's partials of this row (written by the previous launch),
+  // in batches of 8 loads issued before any is used.
+  auto fold_prefix = [&](size_t row, float& M, float& W, float& a0, float& a1) {
+    const float* pl = p.pre_lse + row;
+    const float* po = p.pre_out + row * kHeadDim + my_d;
+    const size_t ostride = rows * kHeadDim;
+    for (int q0 = 0; q0 < npre; q0 += 8) {
+      float lv[8];
+      float2 ov[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int q = min(q0 + i, npre - 1);
+        lv[i] = pl[(size_t)q * rows];
+        ov[i] = *reinterpret_cast<const float2*>(po + (size_t)q * ostride);
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (q0 + i < npre) fold(M, W, a0, a1, lv[i], ov[i].x, ov[i].y);
+    }
+  };
+
   if (P == 1) {
-    if (has_work && my_out) {
-      const size_t row = (size_t)q_row * p.num_q_heads + h0 + my_h;
-      reinterpret_cast<uint32_t*>(p.out)[(row * kHeadDim + my_d) / 2] = pack_bf16x2(my_o0, my_o1);
-      if (my_d == 0 && p.lse) p.lse[row] = my_lse;
+    if (!my_out) return;
+    const size_t row = (size_t)q_row * p.num_q_heads + h0 + my_h;
+    if (npre == 0) {
+      if (has_work) {
+        reinterpret_cast<uint32_t*>(p.out)[(row * kHeadDim + my_d) / 2] = pack_bf16x2(my_o0, my_o1);
+        if (my_d == 0 && p.lse) p.lse[row] = my_lse;
+      }
+      return;
+    }
+    float M = -INFINITY, W = 0.f, a0 = 0.f, a1 = 0.f;
+    if (has_work) fold(M, W, a0, a1, my_lse, my_o0, my_o1);
+    fold_prefix(row, M, W, a0, a1);
+    if (M != -INFINITY) {
+      const float inv = 1.f / W;
+      reinterpret_cast<uint32_t*>(p.out)[(row * kHeadDim + my_d) / 2] = pack_bf16x2(a0 * inv, a1 * inv);
+      if (my_d == 0 && p.lse) p.lse[row] = M + fast_log2(W) * kLn2;
     }
     return;
   }
@@ -544,18 +594,11 @@ __global__ __launch_bounds__(kDecodeThreads, kDecodeWGsPerCU) void decode_kernel
         ov[i] = __hip_atomic_load(po + (size_t)q * ostride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float l = (q0 + i < P) ? lv[i] : -INFINITY;
-        if (l == -INFINITY) continue;
-        const float M2 = fmaxf(M, l);
-        const float sc = fast_exp2((M - M2) * 1.4426950408889634f);  // 0 when M = -inf
-        const float w = fast_exp2((l - M2) * 1.4426950408889634f);
-        W = fmaf(W, sc, w);
-        a0 = fmaf(a0, sc, w * __uint_as_float((uint32_t)ov[i]));
-        a1 = fmaf(a1, sc, w * __uint_as_float((uint32_t)(ov[i] >> 32)));
-        M = M2;
-      }
+      for (int i = 0; i < 8; ++i)
+        if (q0 + i < P)
+          fold(M, W, a0, a1, lv[i], __uint_as_float((uint32_t)ov[i]), __uint_as_float((uint32_t)(ov[i] >> 32)));
     }
+    if (npre > 0) fold_prefix(row, M, W, a0, a1);
     if (M != -INFINITY) {
       const float inv = 1.f / W;
       reinterpret_cast<uint32_t*>(p.out)[(row * kHeadDim + my_d) / 2] = pack_bf16x2(a0 * inv, a1 * inv);

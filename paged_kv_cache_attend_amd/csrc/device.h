@@ -130,6 +130,16 @@ __device__ __forceinline__ int32_t scalar_load_i32(const int32_t* p, int idx) {
   return cp[__builtin_amdgcn_readfirstlane(idx)];
 }
 
+// A pointer the compiler may hold in vector registers, made wave-uniform (in
+// scalar registers), so that loads through it can be scalar loads.
+template <typename T>
+__device__ __forceinline__ const T* uniform_ptr(const T* p) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  return reinterpret_cast<const T*>(((uint64_t)hi << 32) | lo);
+}
+
 // Compiler-only barrier for memory operations: keeps the issue order of the
 // loads on either side (emits no instruction).
 __device__ __forceinline__ void issue_order_barrier() { asm volatile("" ::: "memory"); }

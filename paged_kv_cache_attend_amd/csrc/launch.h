@@ -35,6 +35,12 @@ struct DecodeParams {
   const uint16_t* k_scales;   // fp16 [num_blocks][Hkv][16][4] (q8_0, q4_0)
   const uint16_t* v_scales;
   float v_scale;              // FP8: per-cache V scale (K's is folded into scale_log2)
+  // Prefix-grouped decode: a slot's keys start at slot_plen[slot] (null: 0),
+  // and slots with a prefix also merge pre_parts partials of the prefix pass.
+  const int32_t* slot_plen;
+  const float* pre_out;       // fp32 [pre_parts][total_q*Hq][128]
+  const float* pre_lse;       // fp32 [pre_parts][total_q*Hq]
+  int32_t pre_parts;
   const int32_t* block_table; // [num_seqs][max_blocks]
   const int32_t* ctx_lens;
   const int32_t* q_lens;
@@ -133,6 +139,31 @@ struct WriteParams {
   int32_t total_q;            // rows of k_new / v_new
 };
 
+// Shared-prefix pass of prefix-grouped decode.
+struct PrefixParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const int32_t* block_table;
+  const int32_t* ctx_lens;
+  const int32_t* q_lens;
+  const int32_t* group_start;  // [num_groups + 1]
+  const int32_t* prefix_len;   // [num_groups]
+  float* pre_out;              // fp32 [pre_parts][total_q*Hq][128]
+  float* pre_lse;              // fp32 [pre_parts][total_q*Hq]
+  int32_t* slot_plen;          // [num_seqs], written by the set-up workgroup
+  float scale_log2;
+  int32_t num_seqs;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t max_blocks;
+  int32_t total_q;
+  int32_t num_groups;
+  int32_t row_tiles;           // 64-row tiles of (member, query head) rows per group
+  int32_t pre_parts;           // partitions of the prefix
+  int32_t part_pages;          // pages per prefix partition
+};
+
 // Quantising append: new bf16 rows -> codes (+ scales) at their positions.
 struct WriteQuantParams {
   WriteParams w;              // rows, table, lengths; k_cache / v_cache hold the codes
@@ -156,6 +187,7 @@ hipError_t launch_gather(const GatherParams& p, hipStream_t s);
 hipError_t launch_write_kv(const WriteParams& p, hipStream_t s);
 hipError_t launch_copy_blocks(const CopyParams& p, hipStream_t s);
 hipError_t launch_write_kv_quant(const WriteQuantParams& p, int format, hipStream_t s);
+hipError_t launch_prefix(const PrefixParams& p, unsigned grid, hipStream_t s);
 hipError_t launch_validate(const ValidateParams& p, hipStream_t s);
 
 }  // namespace pa

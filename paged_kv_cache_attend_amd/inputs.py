@@ -286,6 +286,69 @@ def make_problem(name: str, seed: int, ctx_lens, q_lens, num_q_heads: int, num_k
     )
 
 
+def make_grouped_problem(name: str, seed: int, groups, singles, num_q_heads: int, num_kv_heads: int,
+                         q_lens=None, num_layers: int = 1, block_size: int = 16):
+    """Slots in groups that share a prefix, then slots in no group.
+
+    ``groups`` is a list of (prefix_tokens, [ctx_len of each member]); the
+    members are consecutive slots, and every member's table row starts with
+    the group's shared blocks (one physical copy) -- also for members without
+    new tokens.  ``singles`` are the ctx_lens of the slots after the groups.
+    ``q_lens`` defaults to 1 for every slot with keys.  Placement is one
+    seeded random permutation of live and spare blocks, as in make_problem.
+    Returns (problem, group_start int32 [num_groups + 1], prefix_len int32
+    [num_groups]).
+    """
+    bs = int(block_size)
+    ctx = [n for _, members in groups for n in members] + list(singles)
+    ql = np.asarray([1 if n > 0 else 0 for n in ctx] if q_lens is None else q_lens, dtype=np.int32)
+    ctx = np.asarray(ctx, dtype=np.int32)
+    ss = np.random.SeedSequence(seed)
+    children = [child_seed(ss, i) for i in range(1 + num_layers)]
+    rng = np.random.default_rng(children[0])
+    # logical blocks: (owner list, fill) in order
+    blocks = []
+    rows = []              # per slot: list of logical block indices
+    starts, plens = [0], []
+    for prefix, members in groups:
+        if prefix % bs:
+            raise ValueError("prefix must be whole blocks")
+        shared = list(range(len(blocks), len(blocks) + prefix // bs))
+        blocks += [bs] * (prefix // bs)
+        for n in members:
+            if n > 0 and n < prefix:
+                raise ValueError("a member is shorter than its prefix")
+            own = []
+            for t in range(prefix, max(int(n), prefix), bs):
+                own.append(len(blocks))
+                blocks.append(min(bs, int(n) - t))
+            rows.append(shared + own)
+        starts.append(starts[-1] + len(members))
+        plens.append(prefix)
+    for n in singles:
+        own = []
+        for t in range(0, int(n), bs):
+            own.append(len(blocks))
+            blocks.append(min(bs, int(n) - t))
+        rows.append(own)
+    live = len(blocks)
+    spare = max(1, -(-live // 8))
+    pool = live + spare
+    perm = rng.permutation(pool).astype(np.int32)
+    maxb = max([len(r) for r in rows] + [1])
+    table = np.full((len(ctx), maxb), perm[live], dtype=np.int32)
+    fill = np.zeros(pool, dtype=np.int32)
+    for i, f in enumerate(blocks):
+        fill[perm[i]] = f
+    for r, lb in enumerate(rows):
+        table[r, :len(lb)] = perm[lb]
+    problem = PagedProblem(
+        name=name, num_layers=num_layers, num_q_heads=num_q_heads, num_kv_heads=num_kv_heads,
+        head_dim=128, block_size=bs, num_blocks=pool, block_table=table, ctx_lens=ctx, q_lens=ql,
+        scale=np.float32(1.0) / np.sqrt(np.float32(128)), block_fill=fill, _value_seeds=list(children[1:]))
+    return problem, np.asarray(starts, dtype=np.int32), np.asarray(plens, dtype=np.int32)
+
+
 # ---------------------------------------------------------------------------
 # The five reference workloads.  Sizes restate the Qwen3-8B serving design of
 # the inference-optimisation page (36 layers, 8 KV heads of 128, 2048- and
