@@ -93,35 +93,12 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_kernel(PrefixParams p) {
   const int rows_here = members * G - rt * 64;  // rows of this tile that exist
   if (rows_here <= 0 || plen <= 0) return;
 
-  // This lane's row: member j, query head hq (of KV head g).
-  const int r_tile = rg * 32 + col;
-  const int r = rt * 64 + r_tile;
-  const int j = r / G, hq = r % G;
-  const int slot = s0 + (r_tile < rows_here ? j : 0);
-  const int m_r = p.q_lens[slot];
-  const int n_r = p.ctx_lens[slot];
-  const bool row_live = r_tile < rows_here && m_r > 0 && n_r > 0;
-  // Rows before this slot: those before the group (a wave sum), then the
-  // group's members before it.
-  int q_off = q_row_offset(p.q_lens, s0, lane);
-  for (int i = s0; i < slot; ++i) q_off += p.q_lens[i];
-  const size_t grow = (size_t)q_off * p.num_q_heads + g * G + hq;  // global (row, head) index
-
-  // Q^T operand: lane (row, half) holds dims (hh*8 + s)*8 .. +8 for step s.
-  u32x4_t qf[8];
-  {
-    const u32x4_t* qp = reinterpret_cast<const u32x4_t*>(p.q) + (row_live ? grow : 0) * (kHeadDim / 8);
-#pragma unroll
-    for (int s = 0; s < 8; ++s) qf[s] = qp[hh * 8 + s];
-  }
-
   // Keys of this partition: pages [part * part_pages, ...) of the prefix.
   const int key0 = part * p.part_pages * kBlockSize;
   const int kv_end = part == p.pre_parts - 1 ? plen : min(plen, (part + 1) * p.part_pages * kBlockSize);
   const int ntiles = kv_end > key0 ? (kv_end - key0 + kTileKeys - 1) / kTileKeys : 0;
   const int T = (ntiles + 3) / 4;          // tiles per quarter (all loop T times)
   const int tile0 = kq * T;
-  const int my_limit = min(plen, n_r) - 1;  // last visible key of this row
   const int32_t* bt = uniform_ptr(p.block_table + (size_t)s0 * p.max_blocks);
   const int last_page = max(0, (kv_end - 1) >> 4);
 
@@ -129,7 +106,10 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_kernel(PrefixParams p) {
   const int lc = lt & 15;   // 16-byte chunk
 
   auto tile_key = [&](int it) { return key0 + (tile0 + it) * kTileKeys; };
+  // Tiles past the quarter's share or the partition are not loaded; their
+  // registers are never stored (store_tile zeroes keys past kv_end).
   auto load_tile = [&](TileRegs& t, int it) {
+    if (it >= T || tile0 + it >= ntiles) return;
     const int page = tile_key(it) >> 4;
     const int32_t id0 = scalar_load_i32(bt, min(page, last_page));
     const int32_t id1 = scalar_load_i32(bt, min(page + 1, last_page));
@@ -174,6 +154,45 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_kernel(PrefixParams p) {
       r1[1] = hi23;
     }
   };
+
+  // The first two tiles go out before anything that depends on the rows.
+  TileRegs ra, rb;
+  load_tile(ra, 0);
+  issue_order_barrier();
+  load_tile(rb, 1);
+  issue_order_barrier();
+
+  // This lane's row: member j, query head hq (of KV head g).  The tile's
+  // members start at jf; one load per lane gives their query lengths, a
+  // wave scan their row offsets.
+  const int r_tile = rg * 32 + col;
+  const int r = rt * 64 + r_tile;
+  const int jf = (rt * 64) / G;
+  const int jm = r_tile < rows_here ? r / G - jf : 0;  // 0 .. 63
+  const int slot = s0 + jf + jm;
+  const int ql = jf + lane < members ? p.q_lens[s0 + jf + lane] : 0;
+  const int n_r = p.ctx_lens[slot];
+  const int before = q_row_offset(p.q_lens, s0 + jf, lane);
+  int incl = ql;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(incl, d, 64);
+    incl += lane >= d ? y : 0;
+  }
+  const int m_r = __shfl(ql, jm, 64);
+  const int q_off = before + __shfl(incl - ql, jm, 64);
+  const int hq = r % G;
+  const bool row_live = r_tile < rows_here && m_r > 0 && n_r > 0;
+  const size_t grow = (size_t)q_off * p.num_q_heads + g * G + hq;  // global (row, head) index
+  const int my_limit = min(plen, n_r) - 1;  // last visible key of this row
+
+  // Q^T operand: lane (row, half) holds dims (hh*8 + s)*8 .. +8 for step s.
+  u32x4_t qf[8];
+  {
+    const u32x4_t* qp = reinterpret_cast<const u32x4_t*>(p.q) + (row_live ? grow : 0) * (kHeadDim / 8);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) qf[s] = qp[hh * 8 + s];
+  }
 
   f32x16_t o[4];
 #pragma unroll
@@ -251,12 +270,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_kernel(PrefixParams p) {
 
   // Pipeline as in the chunk kernel: tiles it+1, it+2 in registers while
   // tile it is computed from LDS; double-buffered LDS, one barrier per tile.
-  TileRegs ra, rb;
   if (T > 0) {
-    load_tile(ra, 0);
-    issue_order_barrier();
-    load_tile(rb, 1);
-    issue_order_barrier();
     store_tile(ra, 0, 0);
     issue_order_barrier();
     load_tile(ra, 2);
@@ -286,48 +300,62 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_kernel(PrefixParams p) {
   // Merge the quarters into quarter 0 through LDS (the tile area, free
   // now), one accumulator block per round, each round in its own region so
   // one barrier per round suffices: quarters 1-3 write, quarter 0 folds.
-  constexpr int kX = 2 + 16;  // floats per lane per round (m and l ride with block 0)
-  float* xbuf = reinterpret_cast<float*>(&s_buf[0][0][0]);  // [4 rounds][3 senders x 2 row groups][kX][64]
-  static_assert(4 * 6 * kX * 64 * sizeof(float) <= sizeof(s_buf), "merge buffer exceeds the tile area");
+  // Region layout [sender][chunk of 4 floats][lane]: 16-byte accesses by
+  // consecutive lanes.
+  constexpr int kRound = 6 * 4 * 64;  // float4s per round
+  float4* xacc = reinterpret_cast<float4*>(&s_buf[0][0][0]);
+  float2* xml = reinterpret_cast<float2*>(xacc + 4 * kRound);  // [sender][lane]: (m, l)
+  static_assert((4 * kRound * sizeof(float4) + 6 * 64 * sizeof(float2)) <= sizeof(s_buf),
+                "merge buffer exceeds the tile area");
+  const int sender = (kq - 1) * 2 + rg;
   float a0 = 0.f, aq[3] = {0.f, 0.f, 0.f};
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb) {
-    float* rbuf = xbuf + (size_t)mb * 6 * kX * 64;
+    float4* rbuf = xacc + mb * kRound;
     if (kq != 0) {
-      float* buf = rbuf + (size_t)((kq - 1) * 2 + rg) * kX * 64;
-      if (mb == 0) {
-        buf[lane] = m_run;
-        buf[64 + lane] = l_run;
-      }
+      if (mb == 0) xml[sender * 64 + lane] = make_float2(m_run, l_run);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) buf[(2 + i) * 64 + lane] = o[mb][i];
+      for (int c = 0; c < 4; ++c)
+        rbuf[(sender * 4 + c) * 64 + lane] =
+            make_float4(o[mb][4 * c], o[mb][4 * c + 1], o[mb][4 * c + 2], o[mb][4 * c + 3]);
     }
     __syncthreads();
     if (kq == 0) {
       if (mb == 0) {
-        float ms[3], M = m_run;
+        float2 ml[3];
+        float M = m_run;
 #pragma unroll
         for (int q = 0; q < 3; ++q) {
-          ms[q] = rbuf[(size_t)(q * 2 + rg) * kX * 64 + lane];
-          M = fmaxf(M, ms[q]);
+          ml[q] = xml[(q * 2 + rg) * 64 + lane];
+          M = fmaxf(M, ml[q].x);
         }
         const float Mu = (M == -INFINITY) ? 0.f : M;
         a0 = fast_exp2(m_run - Mu);
         float l = l_run * a0;
 #pragma unroll
         for (int q = 0; q < 3; ++q) {
-          aq[q] = fast_exp2(ms[q] - Mu);
-          l = fmaf(rbuf[(size_t)(q * 2 + rg) * kX * 64 + 64 + lane], aq[q], l);
+          aq[q] = fast_exp2(ml[q].x - Mu);
+          l = fmaf(ml[q].y, aq[q], l);
         }
         l_run = l;
         m_run = M;
       }
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float x = o[mb][i] * a0;
+      for (int c = 0; c < 4; ++c) {
+        float x0 = o[mb][4 * c] * a0, x1 = o[mb][4 * c + 1] * a0;
+        float x2 = o[mb][4 * c + 2] * a0, x3 = o[mb][4 * c + 3] * a0;
 #pragma unroll
-        for (int q = 0; q < 3; ++q) x = fmaf(rbuf[(size_t)(q * 2 + rg) * kX * 64 + (2 + i) * 64 + lane], aq[q], x);
-        o[mb][i] = x;
+        for (int q = 0; q < 3; ++q) {
+          const float4 y = rbuf[((q * 2 + rg) * 4 + c) * 64 + lane];
+          x0 = fmaf(y.x, aq[q], x0);
+          x1 = fmaf(y.y, aq[q], x1);
+          x2 = fmaf(y.z, aq[q], x2);
+          x3 = fmaf(y.w, aq[q], x3);
+        }
+        o[mb][4 * c] = x0;
+        o[mb][4 * c + 1] = x1;
+        o[mb][4 * c + 2] = x2;
+        o[mb][4 * c + 3] = x3;
       }
     }
   }
