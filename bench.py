@@ -47,6 +47,7 @@ def parse():
     ap.add_argument("--no-chunk", action="store_true", help="skip the secondary chunk-path measurement")
     ap.add_argument("--no-append", action="store_true", help="skip the secondary K/V-append measurement")
     ap.add_argument("--no-quant", action="store_true", help="skip the secondary quantised-KV decode measurement")
+    ap.add_argument("--no-prefix", action="store_true", help="skip the secondary prefix-grouped decode measurement")
     ap.add_argument("--cpu-budget-s", type=float, default=25.0)
     ap.add_argument("--mode", choices=["bench", "copy"], default="bench",
                     help="copy: time a plain 1 GiB device copy (counter calibration for rocprofv3)")
@@ -362,6 +363,49 @@ def quant_secondary(dev, steps, launch, bf16_us_per_layer):
     return res
 
 
+def prefix_secondary(dev, steps, launch="graph"):
+    """The shared-prefix batch (10 slots x 8447 keys, the first 6144 one
+    shared copy; 32/8 heads) through pa_attend and through prefix-grouped
+    decode, pa_attend_prefix: microseconds per layer each, and GB/s over the
+    distinct bytes a layer reads (the shared pages counted once)."""
+    import torch
+    import paged_kv_cache_attend_amd as pk
+    from paged_kv_cache_attend_amd import inputs
+    nl = 12  # 12 distinct layers (about 1.4 GB of pages), cycled to 36 launches
+    p = inputs.qwen3_shared_prefix_decode(num_layers=nl)
+    layers = [inputs.to_device(p, *p.layer(l), dev) for l in range(nl)]
+    plen = p.shared_prefix_blocks * p.block_size
+    gs = torch.tensor([0, p.num_seqs], dtype=torch.int32, device=dev)
+    pl = torch.tensor([plen], dtype=torch.int32, device=dev)
+    base, grouped = [], []
+    ws_b = ws_g = None
+    for t in layers:
+        out = torch.empty_like(t["q"])
+        lse = torch.empty(t["q"].shape[:2], dtype=torch.float32, device=dev)
+        c = pk.PreparedAttend(t["q"], t["k"], t["v"], t["block_table"], t["ctx_lens"], t["q_lens"],
+                              float(p.scale), out, lse, max_q_len=1, max_ctx_len=p.max_ctx_len, workspace=ws_b)
+        ws_b = c.workspace
+        base.append(c)
+        g = pk.attend_prefix(t["q"], t["k"], t["v"], t["block_table"], t["ctx_lens"], t["q_lens"],
+                             float(p.scale), out, lse, group_start=gs, prefix_len=pl, max_members=p.num_seqs,
+                             max_prefix_len=plen, min_prefix_len=plen, max_ctx_len=p.max_ctx_len,
+                             workspace=ws_g, prepared=True)
+        ws_g = g.keep[-1]
+        grouped.append(g)
+    reps = max(steps // 4, 20)
+    b_ms, _, _ = time_pass(base * 3, reps, 3, launch)
+    g_ms, _, _ = time_pass(grouped * 3, reps, 3, launch)
+    b_us, g_us = b_ms * 1e3 / (3 * nl), g_ms * 1e3 / (3 * nl)
+    unique = p.kv_bytes_unique()
+    return {"workload": "qwen3_8b_shared_prefix_decode, 12 distinct layers cycled to 36 launches",
+            "unique_bytes_per_layer": unique, "bytes_read_per_layer_unshared": p.kv_bytes_read(),
+            "pa_attend_us_per_layer": b_us, "pa_attend_prefix_us_per_layer": g_us,
+            "pa_attend_gbs_unique": unique / (b_us * 1e-6) / 1e9,
+            "pa_attend_prefix_gbs_unique": unique / (g_us * 1e-6) / 1e9,
+            "speedup": b_us / g_us,
+            "parity": "against the FP64 oracle and pa_attend in the GPU tests"}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -451,6 +495,9 @@ def main():
     quant = None
     if decode and not args.no_quant and problem.name == "qwen3_8b_short_decode":
         quant = quant_secondary(dev, args.steps, args.launch, ms / len(calls) * 1e3)
+    prefix = None
+    if decode and not args.no_prefix and problem.name == "qwen3_8b_short_decode":
+        prefix = prefix_secondary(dev, args.steps, args.launch)
 
     line = {
         "metric": METRIC,
@@ -491,6 +538,7 @@ def main():
         "chunk": secondary,
         "append": append,
         "quantised": quant,
+        "prefix_grouped": prefix,
         "source_hash": kernel_source_hash(),
     }
     print(json.dumps(line), flush=True)

@@ -300,3 +300,63 @@ def test_kv_cache_struct_layout():
     # int32 x 2, four pointers, two floats: 8 + 32 + 8 = 48 bytes
     assert ctypes.sizeof(pk.KVCache) == 48
     assert pk.KVCache.k_codes.offset == 8 and pk.KVCache.k_scale.offset == 40
+
+
+def _groups(num_groups=1, max_members=4, max_prefix_len=64, min_prefix_len=0, reserved=0, ptrs=True):
+    p = FAKE.value if ptrs else None
+    return pk.PrefixGroups(num_groups, max_members, max_prefix_len, min_prefix_len, reserved, 0, p, p)
+
+
+def test_prefix_groups_struct_layout():
+    # int32 x 6, two pointers: 24 + 16 = 40 bytes
+    assert ctypes.sizeof(pk.PrefixGroups) == 40
+    assert pk.PrefixGroups.group_start.offset == 24 and pk.PrefixGroups.prefix_len.offset == 32
+
+
+def test_prefix_workspace_size(lib):
+    size = lambda s, g: lib.pa_prefix_workspace_size(ctypes.byref(s), ctypes.byref(g))
+    s = _shape()
+    ws = size(s, _groups())
+    # suffix workspace | slot prefix lengths | prefix LSEs | prefix partials: 4 slots x 32 heads = 128
+    # rows, one group of 4 x 4 rows on 8 KV heads with 4 prefix pages -> 2 prefix partitions
+    suffix = size(s, _groups(num_groups=0, max_members=0, max_prefix_len=0))
+    assert suffix > 0
+    base = suffix - (_align(4 * 4) + _align(1 * 128 * 4) + 1 * 128 * 128 * 4)
+    assert base >= 0 and base % 256 == 0   # 10 pages: one suffix partition, no suffix workspace
+    assert ws == base + _align(4 * 4) + _align(2 * 128 * 4) + 2 * 128 * 128 * 4
+    for bad in (_groups(reserved=1), _groups(max_prefix_len=40), _groups(min_prefix_len=80),
+                _groups(max_prefix_len=176), _groups(max_members=5), _groups(num_groups=5),
+                _groups(num_groups=-1), _groups(min_prefix_len=-16)):
+        assert size(s, bad) == 0
+    assert lib.pa_prefix_workspace_size(ctypes.byref(s), None) == 0
+    assert size(_shape(num_q_heads=64), _groups()) == 0       # 8 query heads per KV head
+    assert size(_shape(total_q=8, max_q_len=2), _groups()) == 0
+
+
+def test_attend_prefix_host_errors(lib):
+    s = _shape()
+    g = _groups()
+    need = lib.pa_prefix_workspace_size(ctypes.byref(s), ctypes.byref(g))
+    f = lib.pa_attend_prefix
+
+    def call(shape=s, groups=g, scale=0.088, ws=FAKE, ws_bytes=need, q=FAKE):
+        gp = None if groups is None else ctypes.byref(groups)
+        return f(ctypes.byref(shape), gp, q, FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.c_float(scale), FAKE, None, ws,
+                 ctypes.c_size_t(ws_bytes), None)
+
+    assert call(groups=None) == pk.Status.ERR_NULL_ARG
+    assert call(groups=_groups(ptrs=False)) == pk.Status.ERR_NULL_ARG
+    assert call(q=None) == pk.Status.ERR_NULL_ARG
+    assert call(ws=None) == pk.Status.ERR_NULL_ARG
+    assert call(ws_bytes=need - 1) == pk.Status.ERR_WORKSPACE_TOO_SMALL
+    assert call(scale=math.nan) == pk.Status.ERR_BAD_SHAPE
+    assert call(groups=_groups(reserved=1)) == pk.Status.ERR_BAD_SHAPE
+    assert call(groups=_groups(max_prefix_len=24)) == pk.Status.ERR_BAD_SHAPE
+    assert call(shape=_shape(num_q_heads=64)) == pk.Status.ERR_UNSUPPORTED
+    assert call(shape=_shape(total_q=8, max_q_len=2)) == pk.Status.ERR_UNSUPPORTED
+    empty = _shape(num_seqs=0, total_q=0)
+    assert call(shape=empty, groups=_groups(num_groups=0, max_members=0), ws=None, ws_bytes=0) == pk.Status.OK
+    init = lib.pa_prefix_workspace_init
+    assert init(ctypes.byref(s), ctypes.byref(g), None, ctypes.c_size_t(need), None) == pk.Status.ERR_NULL_ARG
+    assert init(ctypes.byref(s), ctypes.byref(g), FAKE, ctypes.c_size_t(need - 1), None) == \
+        pk.Status.ERR_WORKSPACE_TOO_SMALL
