@@ -570,6 +570,7 @@ pa_status pa_attend_prefix(const pa_shape* shape, const pa_prefix_groups* groups
   pr.row_tiles = pp.row_tiles > 0 ? pp.row_tiles : 1;
   pr.pre_parts = pp.pre_parts;
   pr.part_pages = pp.pre_pages;
+  pr.max_members = groups->max_members;
   if (launch_prefix(pr, pp.pre_grid, s) != hipSuccess) return PA_ERR_LAUNCH;
 
   pa_kv_cache kv = {};

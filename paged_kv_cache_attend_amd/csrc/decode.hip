@@ -497,39 +497,6 @@ __global__ __launch_bounds__(kDecodeThreads, kDecodeWGsPerCU) void decode_kernel
     }
   }
 
-  // Online log-sum-exp merge state (M, W, a0, a1): the result is a / W with
-  // LSE M + ln W.  A partial with LSE = -inf weighs 0 and is never read.
-  auto fold = [](float& M, float& W, float& a0, float& a1, float l, float o0, float o1) {
-    if (l == -INFINITY) return;
-    const float M2 = fmaxf(M, l);
-    const float sc = fast_exp2((M - M2) * 1.4426950408889634f);  // 0 when M = -inf
-    const float w = fast_exp2((l - M2) * 1.4426950408889634f);
-    W = fmaf(W, sc, w);
-    a0 = fmaf(a0, sc, w * o0);
-    a1 = fmaf(a1, sc, w * o1);
-    M = M2;
-  };
-  // The prefix pass's partials of this row (written by the previous launch),
-  // in batches of 8 loads issued before any is used.
-  auto fold_prefix = [&](size_t row, float& M, float& W, float& a0, float& a1) {
-    const float* pl = p.pre_lse + row;
-    const float* po = p.pre_out + row * kHeadDim + my_d;
-    const size_t ostride = rows * kHeadDim;
-    for (int q0 = 0; q0 < npre; q0 += 8) {
-      float lv[8];
-      float2 ov[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int q = min(q0 + i, npre - 1);
-        lv[i] = pl[(size_t)q * rows];
-        ov[i] = *reinterpret_cast<const float2*>(po + (size_t)q * ostride);
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        if (q0 + i < npre) fold(M, W, a0, a1, lv[i], ov[i].x, ov[i].y);
-    }
-  };
-
   if (P == 1) {
     if (!my_out) return;
     const size_t row = (size_t)q_row * p.num_q_heads + h0 + my_h;
@@ -540,13 +507,15 @@ __global__ __launch_bounds__(kDecodeThreads, kDecodeWGsPerCU) void decode_kernel
       }
       return;
     }
-    float M = -INFINITY, W = 0.f, a0 = 0.f, a1 = 0.f;
-    if (has_work) fold(M, W, a0, a1, my_lse, my_o0, my_o1);
-    fold_prefix(row, M, W, a0, a1);
-    if (M != -INFINITY) {
-      const float inv = 1.f / W;
-      reinterpret_cast<uint32_t*>(p.out)[(row * kHeadDim + my_d) / 2] = pack_bf16x2(a0 * inv, a1 * inv);
-      if (my_d == 0 && p.lse) p.lse[row] = M + fast_log2(W) * kLn2;
+    // Own result and the prefix pass's partials of this row (written by the
+    // previous launch).
+    MergeState ms;
+    if (has_work) merge_fold(ms, my_lse, my_o0, my_o1);
+    merge_partials(ms, nullptr, nullptr, 0, p.pre_lse + row, p.pre_out + row * kHeadDim + my_d, npre, rows);
+    if (ms.M != -INFINITY) {
+      const float inv = 1.f / ms.W;
+      reinterpret_cast<uint32_t*>(p.out)[(row * kHeadDim + my_d) / 2] = pack_bf16x2(ms.a0 * inv, ms.a1 * inv);
+      if (my_d == 0 && p.lse) p.lse[row] = ms.M + fast_log2(ms.W) * kLn2;
     }
     return;
   }
@@ -575,34 +544,19 @@ __global__ __launch_bounds__(kDecodeThreads, kDecodeWGsPerCU) void decode_kernel
   __syncthreads();
   if (!s_last) return;
 
-  // Merge by log-sum-exp weights, online over batches of up to 8 partials:
-  // every load of a batch is issued before any is used, and a partial with
-  // LSE = -inf (empty) gets weight 0 without its output being read.
+  // Merge by log-sum-exp weights: this slot's P partials and, with a shared
+  // prefix, the prefix pass's npre, their loads issued in batches before any
+  // is used; a partial with LSE = -inf (empty) gets weight 0 without its
+  // output being read.
   if (my_out) {
     const size_t row = (size_t)q_row * p.num_q_heads + h0 + my_h;
-    const float* pl = p.part_lse + row;
-    const uint64_t* po = part_out64 + (row * kHeadDim + my_d) / 2;
-    const size_t ostride = rows * kHeadDim / 2;
-    float M = -INFINITY, W = 0.f, a0 = 0.f, a1 = 0.f;
-    for (int q0 = 0; q0 < P; q0 += 8) {
-      float lv[8];
-      uint64_t ov[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int q = min(q0 + i, P - 1);
-        lv[i] = __hip_atomic_load(pl + (size_t)q * rows, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        ov[i] = __hip_atomic_load(po + (size_t)q * ostride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        if (q0 + i < P)
-          fold(M, W, a0, a1, lv[i], __uint_as_float((uint32_t)ov[i]), __uint_as_float((uint32_t)(ov[i] >> 32)));
-    }
-    if (npre > 0) fold_prefix(row, M, W, a0, a1);
-    if (M != -INFINITY) {
-      const float inv = 1.f / W;
-      reinterpret_cast<uint32_t*>(p.out)[(row * kHeadDim + my_d) / 2] = pack_bf16x2(a0 * inv, a1 * inv);
-      if (my_d == 0 && p.lse) p.lse[row] = M + fast_log2(W) * kLn2;
+    MergeState ms;
+    merge_partials(ms, p.part_lse + row, p.part_out + row * kHeadDim + my_d, P,
+                   p.pre_lse + row, p.pre_out + row * kHeadDim + my_d, npre, rows);
+    if (ms.M != -INFINITY) {
+      const float inv = 1.f / ms.W;
+      reinterpret_cast<uint32_t*>(p.out)[(row * kHeadDim + my_d) / 2] = pack_bf16x2(ms.a0 * inv, ms.a1 * inv);
+      if (my_d == 0 && p.lse) p.lse[row] = ms.M + fast_log2(ms.W) * kLn2;
     }
   }
   // Leave the counter at zero for the next call (the next launch sees it).

@@ -177,4 +177,66 @@ __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_lo
 
 constexpr float kLn2 = 0.69314718055994530942f;
 
+// Online log-sum-exp merge of split-KV partials (each a normalised output
+// and its natural-log LSE) for one thread's two adjacent dims of one row:
+// the result is (a0, a1) / W with LSE M + ln W.  A partial with LSE = -inf
+// weighs 0 and its output is never read.
+struct MergeState {
+  float M = -INFINITY;
+  float W = 0.f;
+  float a0 = 0.f;
+  float a1 = 0.f;
+};
+
+__device__ __forceinline__ void merge_fold(MergeState& s, float l, float o0, float o1) {
+  if (l == -INFINITY) return;
+  const float M2 = fmaxf(s.M, l);
+  const float sc = fast_exp2((s.M - M2) * 1.4426950408889634f);  // 0 when M = -inf
+  const float w = fast_exp2((l - M2) * 1.4426950408889634f);
+  s.W = fmaf(s.W, sc, w);
+  s.a0 = fmaf(s.a0, sc, w * o0);
+  s.a1 = fmaf(s.a1, sc, w * o1);
+  s.M = M2;
+}
+
+// Fold the partials of one row from two sets: set A's partial i has its LSE
+// at lse_a[i * rows] and its two dims at out_a[i * rows * 128 + 0, 1]
+// (likewise B).  Device-coherent relaxed loads (partials of this launch may
+// come from workgroups on any XCD), in batches whose loads are all issued
+// before any is used: 8 partials for short merges, else 24 (48 loads in
+// flight, within the 6-bit load counter).
+template <int kBatch>
+__device__ __forceinline__ void merge_batches(MergeState& s, const float* lse_a, const float* out_a, int na,
+                                              const float* lse_b, const float* out_b, int n, size_t rows) {
+  const size_t ostride = rows * 128 / 2;
+  for (int q0 = 0; q0 < n; q0 += kBatch) {
+    float lv[kBatch];
+    uint64_t ov[kBatch];
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const int q = min(q0 + i, n - 1);
+      const bool a = q < na;
+      const int k = a ? q : q - na;
+      const float* lp = (a ? lse_a : lse_b) + (size_t)k * rows;
+      const uint64_t* op = reinterpret_cast<const uint64_t*>(a ? out_a : out_b) + (size_t)k * ostride;
+      lv[i] = __hip_atomic_load(lp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      ov[i] = __hip_atomic_load(op, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i)
+      if (q0 + i < n)
+        merge_fold(s, lv[i], __uint_as_float((uint32_t)ov[i]), __uint_as_float((uint32_t)(ov[i] >> 32)));
+  }
+}
+
+__device__ __forceinline__ void merge_partials(MergeState& s, const float* lse_a, const float* out_a, int na,
+                                               const float* lse_b, const float* out_b, int nb, size_t rows) {
+  const int n = na + nb;
+  if (n <= 0) return;
+  if (n <= 8)
+    merge_batches<8>(s, lse_a, out_a, na, lse_b, out_b, n, rows);
+  else
+    merge_batches<24>(s, lse_a, out_a, na, lse_b, out_b, n, rows);
+}
+
 }  // namespace pa

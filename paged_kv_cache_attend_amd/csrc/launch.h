@@ -162,6 +162,7 @@ struct PrefixParams {
   int32_t row_tiles;           // 64-row tiles of (member, query head) rows per group
   int32_t pre_parts;           // partitions of the prefix
   int32_t part_pages;          // pages per prefix partition
+  int32_t max_members;         // rows of a group's first max_members slots only
 };
 
 // Quantising append: new bf16 rows -> codes (+ scales) at their positions.

@@ -49,13 +49,15 @@ struct TileRegs {
   u32x4_t v[4];
 };
 
-// Set-up workgroup: slot_plen[r] = prefix length of r's group, 0 elsewhere.
+// Set-up workgroup: slot_plen[r] = the prefix length of r's group in whole
+// pages, for a group's first max_members slots (the rows this kernel
+// computes); 0 elsewhere, where the decode pass reads all keys.
 __device__ void write_slot_prefix(const PrefixParams& p) {
   for (int r = threadIdx.x; r < p.num_seqs; r += blockDim.x) p.slot_plen[r] = 0;
   __syncthreads();
   for (int k = 0; k < p.num_groups; ++k) {
-    const int s0 = p.group_start[k], s1 = p.group_start[k + 1];
-    const int plen = p.prefix_len[k];
+    const int s0 = p.group_start[k], s1 = min(p.group_start[k + 1], s0 + p.max_members);
+    const int plen = max(p.prefix_len[k], 0) & ~15;
     for (int r = s0 + (int)threadIdx.x; r < s1; r += blockDim.x)
       if (r >= 0 && r < p.num_seqs) p.slot_plen[r] = plen;
   }
@@ -88,7 +90,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_kernel(PrefixParams p) {
 
   const int s0 = scalar_load_i32(p.group_start, grp);
   const int s1 = scalar_load_i32(p.group_start, grp + 1);
-  const int plen = scalar_load_i32(p.prefix_len, grp);
+  const int plen = scalar_load_i32(p.prefix_len, grp) & ~15;  // whole pages, as the decode pass reads it
   const int members = s1 - s0;
   const int rows_here = members * G - rt * 64;  // rows of this tile that exist
   if (rows_here <= 0 || plen <= 0) return;
@@ -182,7 +184,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_kernel(PrefixParams p) {
   const int m_r = __shfl(ql, jm, 64);
   const int q_off = before + __shfl(incl - ql, jm, 64);
   const int hq = r % G;
-  const bool row_live = r_tile < rows_here && m_r > 0 && n_r > 0;
+  // Rows of slots past the group's first max_members get no prefix (the
+  // decode pass attends them to all their keys).
+  const bool row_live = r_tile < rows_here && r / G < p.max_members && m_r > 0 && n_r > 0;
   const size_t grow = (size_t)q_off * p.num_q_heads + g * G + hq;  // global (row, head) index
   const int my_limit = min(plen, n_r) - 1;  // last visible key of this row
 

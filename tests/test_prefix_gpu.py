@@ -25,16 +25,18 @@ def _i32(a):
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(DEV)
 
 
-def run_prefix(p, group_start, prefix_len, *, partition_size=0, min_prefix_len=0, layer=0, repeats=1):
+def run_prefix(p, group_start, prefix_len, *, partition_size=0, min_prefix_len=0, layer=0, repeats=1,
+               max_members=None, max_prefix_len=None):
     q, k, v = p.layer(layer)
     t = inputs.to_device(p, q, k, v, DEV)
     out = torch.full(q.shape, OUT_SENTINEL, dtype=torch.int16, device=DEV).view(torch.bfloat16)
     lse = torch.full(q.shape[:2], LSE_SENTINEL, dtype=torch.int32, device=DEV).view(torch.float32)
-    members = int(np.diff(group_start).max(initial=0))
+    members = int(np.diff(group_start).max(initial=0)) if max_members is None else max_members
+    mpl = int(prefix_len.max(initial=0)) if max_prefix_len is None else max_prefix_len
     for _ in range(repeats):
         pk.attend_prefix(t["q"], t["k"], t["v"], t["block_table"], t["ctx_lens"], t["q_lens"], float(p.scale),
                          out, lse, group_start=_i32(group_start), prefix_len=_i32(prefix_len),
-                         max_members=members, max_prefix_len=int(prefix_len.max(initial=0)),
+                         max_members=members, max_prefix_len=mpl,
                          min_prefix_len=min_prefix_len, max_ctx_len=p.max_ctx_len, partition_size=partition_size)
     torch.cuda.synchronize()
     return out.view(torch.int16).cpu().numpy().view(np.uint16), lse.cpu().numpy()
@@ -70,6 +72,25 @@ def test_prefix_min_prefix_hint_and_repeats():
     b = run_prefix(p, gs, pl, min_prefix_len=128, repeats=3)
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1].view(np.uint32), b[1].view(np.uint32))
     compare(p, a, run_oracle(p), label="hint")
+
+
+def test_prefix_members_past_max_members_are_decoded_whole():
+    # Slots past a group's first max_members get no prefix: the decode pass
+    # attends them to all their keys, and the result is still exact.
+    p, gs, pl = inputs.make_grouped_problem("pre_maxm", 47, [(64, [70, 300, 65, 100, 64])], [40], 32, 8)
+    ref = run_oracle(p)
+    for mm in (1, 3):
+        say(f"attend_prefix max_members={mm}")
+        compare(p, run_prefix(p, gs, pl, max_members=mm), ref, label=f"max_members={mm}")
+
+
+def test_prefix_length_rounded_down_to_pages():
+    # A prefix length that is not a whole number of pages is read as the
+    # pages it covers whole by both passes (the rest are ordinary keys).
+    p, gs, pl = inputs.make_grouped_problem("pre_round", 53, [(64, [70, 300, 65])], [], 32, 8)
+    ref = run_oracle(p)
+    say("attend_prefix prefix_len not a multiple of 16")
+    compare(p, run_prefix(p, gs, pl + 6, max_prefix_len=80, partition_size=32), ref, label="rounded")
 
 
 def test_prefix_graph_replay():
