@@ -13,16 +13,19 @@
 // halves merge through LDS at the end.  Each half walks its keys in 32-key
 // tiles (two 16-token pages):
 //   1. its 256 threads load a tile's K and V rows through the block table
-//      (page ids by scalar loads; 16-byte loads, one key row per 8 / 16
-//      threads) two tiles ahead into a two-deep register ring, and store each
+//      (page ids by scalar loads; a thread holds one 16-byte chunk of two
+//      adjacent keys, so each wave instruction reads four whole 256-byte key
+//      rows) two tiles ahead into a two-deep register ring, and store each
 //      tile to a double-buffered LDS area: K row-major with XOR-swizzled
-//      16-byte chunks, V transposed (dim-major, rows padded to 72 bytes so
-//      the transposed reads are conflict free).  One barrier per tile;
+//      16-byte chunks, V transposed (dim-major, rows padded to 68 bytes, 17
+//      words, which keeps the transposed stores and 4-byte reads spread over
+//      the banks).  One barrier per tile;
 //   2. each wave computes S^T = K Q^T (32 keys x 32 rows, 8 MFMAs over the 128
-//      dims).  In the MFMA output layout a lane holds 16 keys of ONE query row,
-//      so the row max and sum of the online softmax are mostly in-lane; the
-//      other 16 keys of the row sit in lane + 32.  The accumulators are only
-//      rescaled when the row max grows by more than 2^8;
+//      dims, all eight K fragments read before the first product).  In the
+//      MFMA output layout a lane holds 16 keys of ONE query row, so the row
+//      max and sum of the online softmax are mostly in-lane; the other 16
+//      keys of the row sit in lane ^ 32 (v_permlane32_swap).  The
+//      accumulators are only rescaled when the row max grows by more than 2^8;
 //   3. probabilities are rounded to bf16 and used directly, from registers, as
 //      the B operand of O^T += V^T P^T (4 x 32 dims, 2 key steps, 8 MFMAs); the
 //      V^T A operand is read from the transposed LDS tile with the same key
@@ -39,7 +42,7 @@ constexpr int kThreads = 512;
 constexpr int kHalfThreads = 256;
 constexpr int kTileKeys = 32;
 constexpr int kKRowBytes = kHeadDim * 2;          // 256
-constexpr int kVtRowBytes = kTileKeys * 2 + 8;    // 72: padded dim-major row
+constexpr int kVtRowBytes = kTileKeys * 2 + 4;    // 68: padded dim-major row (17 words)
 constexpr int kKBytes = kTileKeys * kKRowBytes;   // 8 KiB
 constexpr int kVtBytes = kHeadDim * kVtRowBytes;  // 9 KiB
 constexpr int kStageBytes = kKBytes + kVtBytes;   // one tile
@@ -50,8 +53,8 @@ static_assert(kChunkRows == 4 * 32, "four row groups of 32 rows");
 __device__ __forceinline__ bf16x8_t as_bf16x8(const u32x4_t& u) { return __builtin_bit_cast(bf16x8_t, u); }
 
 struct TileRegs {
-  u32x4_t k[2];  // key lk_key, chunks lk_c, lk_c + 1
-  u32x4_t v[2];  // keys 2 lv_kp, 2 lv_kp + 1, chunk lv_c
+  u32x4_t k[2];  // keys 2 lv_kp, 2 lv_kp + 1, chunk lv_c
+  u32x4_t v[2];
 };
 
 __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkParams p) {
@@ -82,15 +85,16 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkParams p) {
   const int row = qt * kChunkRows + rg * 32 + col;  // row within the slot
   const bool row_live = row < m;
 
-  // Q^T operand: lane (row, half) holds dims (hh*8 + s)*8 .. +8 for step s.
+  // Q^T operand: lane (row, half) holds dims (hh*8 + s)*8 .. +8 for step s
+  // (loaded after the first tiles are requested, below).  Rows past m read
+  // row 0's query (their results are never written).
   u32x4_t qf[8];
-  {
-    // Rows past m read row 0's query (their results are never written).
+  auto load_q = [&]() {
     const u32x4_t* qp = reinterpret_cast<const u32x4_t*>(p.q) +
                         ((size_t)(q_row0 + (row_live ? row : 0)) * p.num_q_heads + h) * (kHeadDim / 8);
 #pragma unroll
     for (int s = 0; s < 8; ++s) qf[s] = qp[hh * 8 + s];
-  }
+  };
 
   // Keys this workgroup needs, split in two halves of whole tiles.
   int kv_end = n;
@@ -106,10 +110,9 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkParams p) {
   const int32_t* bt = p.block_table + (size_t)seq * p.max_blocks;
   const int last_page = (kv_end - 1) >> 4;
 
-  // Loader roles (within the half).  K: key lk_key, chunks lk_c, lk_c + 1.
-  // V: keys 2 lv_kp and 2 lv_kp + 1 (same page), chunk lv_c.
-  const int lk_key = lt >> 3;
-  const int lk_c = (lt & 7) * 2;
+  // Loader roles (within the half): keys 2 lv_kp and 2 lv_kp + 1 (same
+  // page), 16-byte chunk lv_c, for K and for V -- each wave instruction reads
+  // four whole 256-byte key rows.
   const int lv_kp = lt >> 4;
   const int lv_c = lt & 15;
 
@@ -121,27 +124,26 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkParams p) {
     const int t = tile0 + it;
     const int32_t id0 = scalar_load_i32(bt, min(2 * t, last_page));
     const int32_t id1 = scalar_load_i32(bt, min(2 * t + 1, last_page));
-    const int32_t idk = (lk_key >> 4) ? id1 : id0;
     const int32_t idv = ((2 * lv_kp) >> 4) ? id1 : id0;
-    const u32x4_t* ks = reinterpret_cast<const u32x4_t*>(p.k + cache_offset(idk, g, lk_key & 15, lk_c * 8, p.num_kv_heads));
-    r.k[0] = ks[0];
-    r.k[1] = ks[1];
-    r.v[0] = *reinterpret_cast<const u32x4_t*>(p.v + cache_offset(idv, g, (2 * lv_kp) & 15, lv_c * 8, p.num_kv_heads));
-    r.v[1] = *reinterpret_cast<const u32x4_t*>(p.v + cache_offset(idv, g, (2 * lv_kp + 1) & 15, lv_c * 8, p.num_kv_heads));
+    const size_t off = cache_offset(idv, g, (2 * lv_kp) & 15, lv_c * 8, p.num_kv_heads);
+    r.k[0] = *reinterpret_cast<const u32x4_t*>(p.k + off);
+    r.k[1] = *reinterpret_cast<const u32x4_t*>(p.k + off + kHeadDim);
+    r.v[0] = *reinterpret_cast<const u32x4_t*>(p.v + off);
+    r.v[1] = *reinterpret_cast<const u32x4_t*>(p.v + off + kHeadDim);
   };
   auto store_tile = [&](const TileRegs& r, int stage, int it) {
     uint8_t* sk = s_buf[kh][stage];
     uint8_t* svt = sk + kKBytes;
     const int base = (tile0 + it) * kTileKeys;
     const bool tile_ok = it < T;
-    const bool k_ok = tile_ok && base + lk_key < kv_end;
     const bool v0_ok = tile_ok && base + 2 * lv_kp < kv_end;
     const bool v1_ok = tile_ok && base + 2 * lv_kp + 1 < kv_end;
     const u32x4_t zero = u32x4_t{0u, 0u, 0u, 0u};
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
-      const int c = lk_c + e;
-      *reinterpret_cast<u32x4_t*>(sk + lk_key * kKRowBytes + ((c ^ (lk_key & 15)) << 4)) = k_ok ? r.k[e] : zero;
+      const int key = 2 * lv_kp + e;
+      *reinterpret_cast<u32x4_t*>(sk + key * kKRowBytes + ((lv_c ^ (key & 15)) << 4)) =
+          (e ? v1_ok : v0_ok) ? r.k[e] : zero;
     }
     const u32x4_t va = v0_ok ? r.v[0] : zero;
     const u32x4_t vb = v1_ok ? r.v[1] : zero;
@@ -171,12 +173,18 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkParams p) {
     f32x16_t st;
 #pragma unroll
     for (int i = 0; i < 16; ++i) st[i] = 0.f;
+    // All eight K fragments are read before the first product, so the LDS
+    // latency is paid once rather than before every MFMA.
+    u32x4_t kf[8];
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
       const int c = hh * 8 + s;
-      const u32x4_t kf = *reinterpret_cast<const u32x4_t*>(sk + col * kKRowBytes + ((c ^ (col & 15)) << 4));
-      st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf), as_bf16x8(qf[s]), st, 0, 0, 0);
+      kf[s] = *reinterpret_cast<const u32x4_t*>(sk + col * kKRowBytes + ((c ^ (col & 15)) << 4));
     }
+    __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the products
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+      st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf[s]), as_bf16x8(qf[s]), st, 0, 0, 0);
     // Online softmax over this lane's 16 keys of its row (log2 domain).
     const int kbase = (tile0 + it) * kTileKeys + 4 * hh;
     float sv[16];
@@ -190,7 +198,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkParams p) {
         sv[4 * a + b] = x;
         mloc = fmaxf(mloc, x);
       }
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+    mloc = fmaxf(mloc, other_half(mloc));
     const bool raise = mloc > m_run + kRescaleSlack;
     if (__builtin_amdgcn_ballot_w64(raise) != 0) {
       // A row with no visible key so far keeps m = -inf (its sums are 0);
@@ -227,53 +235,49 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkParams p) {
       const int d = mb * 32 + col;
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        const uint8_t* vrow = svt + d * kVtRowBytes + (16 * ks + 4 * hh) * 2;
-        const u32x2_t v0 = *reinterpret_cast<const u32x2_t*>(vrow);
-        const u32x2_t v1 = *reinterpret_cast<const u32x2_t*>(vrow + 16);
-        const u32x4_t vf = u32x4_t{v0[0], v0[1], v1[0], v1[1]};
+        // (4-byte reads: the 68-byte rows keep only 4-byte alignment)
+        const uint32_t* vrow = reinterpret_cast<const uint32_t*>(svt + d * kVtRowBytes + (16 * ks + 4 * hh) * 2);
+        const u32x4_t vf = u32x4_t{vrow[0], vrow[1], vrow[4], vrow[5]};
         o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vf), as_bf16x8(pf[ks]), o[mb], 0, 0, 0);
       }
     }
   };
 
-  // Pipeline: tiles it+1 and it+2 sit in registers while tile it is computed
-  // from LDS; LDS is double buffered, one barrier per tile.
-  TileRegs ra, rb;
+  // Pipeline: a ring of two tiles in registers per half; tile it goes to
+  // LDS stage it % 2, its ring slot is refilled with tile it + 2, one
+  // barrier, then it is computed.  Two stages suffice: a wave reaches tile
+  // it + 2's store only after the barrier of tile it + 1, which every wave
+  // passes after computing tile it.  Ring loads past the half's last tile
+  // re-read a valid page and are never stored.
+  TileRegs rr[2];
   if (T > 0) {
-    load_tile(ra, 0);
+    load_tile(rr[0], 0);
     issue_order_barrier();
-    load_tile(rb, 1);
+    load_tile(rr[1], 1);
     issue_order_barrier();
-    store_tile(ra, 0, 0);
-    issue_order_barrier();
-    load_tile(ra, 2);
-    issue_order_barrier();
-    __syncthreads();
   }
-  // (issue_order_barrier keeps the compiler from moving a tile's loads ahead
-  // of the store that frees its registers, which would make the load
-  // counter's waits drain the ring.)
+  load_q();
+  issue_order_barrier();
+#define PA_CHUNK_STEP(K, IT, RELOAD)           \
+  do {                                         \
+    store_tile(rr[K], (IT) & 1, IT);           \
+    issue_order_barrier();                     \
+    if (RELOAD) load_tile(rr[K], (IT) + 2);    \
+    issue_order_barrier();                     \
+    __syncthreads();                           \
+    compute_tile(IT, (IT) & 1);                \
+  } while (0)
   int it = 0;
-  for (; it + 1 < T; it += 2) {
-    // tile it is in stage 0; rb holds it+1, ra holds it+2
-    store_tile(rb, 1, it + 1);
-    issue_order_barrier();
-    load_tile(rb, it + 3);
-    issue_order_barrier();
-    compute_tile(it, 0);
-    __syncthreads();
-    // tile it+1 is in stage 1; ra holds it+2, rb holds it+3
-    store_tile(ra, 0, it + 2);
-    issue_order_barrier();
-    load_tile(ra, it + 4);
-    issue_order_barrier();
-    compute_tile(it + 1, 1);
-    __syncthreads();
+  for (; it + 4 <= T; it += 2) {  // every reload is a real tile
+    PA_CHUNK_STEP(0, it, true);
+    PA_CHUNK_STEP(1, it + 1, true);
   }
-  if (it < T) {  // odd tile count: the last tile is in stage 0
-    compute_tile(it, 0);
-    __syncthreads();
-  }
+  // The last 0 .. 3 tiles.
+  if (it < T) PA_CHUNK_STEP(0, it, it + 2 < T);
+  if (it + 1 < T) PA_CHUNK_STEP(1, it + 1, false);
+  if (it + 2 < T) PA_CHUNK_STEP(0, it + 2, false);
+#undef PA_CHUNK_STEP
+  __syncthreads();  // all computes done before the tile area is reused
 
   // Merge the key halves: half 1 hands (m, l, o) to half 0 through LDS, in
   // four rounds of 16 accumulators (16 KiB per round, inside the tile area).

@@ -172,6 +172,16 @@ __device__ __forceinline__ uint32_t stream_load(const uint32_t* p) { return *p; 
 __device__ __forceinline__ uint32_t stream_load(const uint16_t* p) { return (uint32_t)*p; }
 #endif
 
+// The value of the same register in lane l ^ 32 (the other half of the
+// wave), through v_permlane32_swap: the swap leaves lanes 0-31 of the first
+// result and lanes 32-63 of the second holding this lane's own value, the
+// other two holding the partner's.
+__device__ __forceinline__ float other_half(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  const uint32_t lane = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  return __uint_as_float(lane < 32 ? r[1] : r[0]);
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
