@@ -12,25 +12,26 @@
 // takes rows 32 (w % 4) .. +32 and one half of the keys (w / 4); the two
 // halves merge through LDS at the end.  Each half walks its keys in 32-key
 // tiles (two 16-token pages):
-//   1. its 256 threads load a tile's K and V rows through the block table
-//      (page ids by scalar loads; a thread holds one 16-byte chunk of two
-//      adjacent keys, so each wave instruction reads four whole 256-byte key
-//      rows) two tiles ahead into a two-deep register ring, and store each
-//      tile to a double-buffered LDS area: K row-major with XOR-swizzled
-//      16-byte chunks, V transposed (dim-major, rows padded to 68 bytes, 17
-//      words, which keeps the transposed stores and 4-byte reads spread over
-//      the banks).  One barrier per tile;
+//   1. the tile's K and V rows go straight from memory into LDS
+//      (global_load_lds_dwordx4), row-major with XOR-swizzled 16-byte
+//      chunks, into a four-stage ring: three tiles are in flight while one is
+//      computed, no registers hold them and no store instructions move them.
+//      Each lane's source chunk is the one the swizzle puts at its LDS slot;
+//      page ids come from scalar loads one tile ahead.  One barrier per tile;
 //   2. each wave computes S^T = K Q^T (32 keys x 32 rows, 8 MFMAs over the 128
 //      dims, all eight K fragments read before the first product).  In the
 //      MFMA output layout a lane holds 16 keys of ONE query row, so the row
 //      max and sum of the online softmax are mostly in-lane; the other 16
 //      keys of the row sit in lane ^ 32 (v_permlane32_swap).  The
-//      accumulators are only rescaled when the row max grows by more than 2^8;
+//      accumulators are only rescaled when the row max grows by more than
+//      2^8; tiles every row sees whole skip the masking and fold the scale
+//      into the exponent's FMA;
 //   3. probabilities are rounded to bf16 and used directly, from registers, as
-//      the B operand of O^T += V^T P^T (4 x 32 dims, 2 key steps, 8 MFMAs); the
-//      V^T A operand is read from the transposed LDS tile with the same key
-//      order the probabilities already have.
-// Keys >= n are never loaded (zeros) and get -inf scores.
+//      the B operand of O^T += V^T P^T (4 x 32 dims, 2 key steps, 8 MFMAs);
+//      the V^T A operand is read from the row-major V tile with transposing
+//      LDS reads (ds_read_b64_tr_b16), issued before the softmax so that they
+//      complete under it.
+// Keys past the end load the last key (finite) and get -inf scores.
 
 #include "device.h"
 
@@ -39,34 +40,34 @@ namespace pa {
 namespace {
 
 constexpr int kThreads = 512;
-constexpr int kHalfThreads = 256;
 constexpr int kTileKeys = 32;
-constexpr int kKRowBytes = kHeadDim * 2;          // 256
-constexpr int kVtRowBytes = kTileKeys * 2 + 4;    // 68: padded dim-major row (17 words)
-constexpr int kKBytes = kTileKeys * kKRowBytes;   // 8 KiB
-constexpr int kVtBytes = kHeadDim * kVtRowBytes;  // 9 KiB
-constexpr int kStageBytes = kKBytes + kVtBytes;   // one tile
+constexpr int kRowBytes = kHeadDim * 2;           // 256: one key row of K or V
+constexpr int kTileBytes = kTileKeys * kRowBytes; // 8 KiB (K or V)
+constexpr int kStages = 4;                        // LDS stages per key half
 constexpr float kRescaleSlack = 8.0f;             // log2 units
 
 static_assert(kChunkRows == 4 * 32, "four row groups of 32 rows");
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(const u32x4_t& u) { return __builtin_bit_cast(bf16x8_t, u); }
 
-struct TileRegs {
-  u32x4_t k[2];  // keys 2 lv_kp, 2 lv_kp + 1, chunk lv_c
-  u32x4_t v[2];
-};
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+
+// Byte offset of dims d .. of key row `key` in a swizzled K or V tile: the
+// 16-byte chunk index is XORed with the key's low four bits.
+__device__ __forceinline__ int swz(int key, int d) { return key * kRowBytes + ((((d >> 3) ^ key) & 15) << 4) + (d & 7) * 2; }
 
 __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkParams p) {
-  // [key half][stage][K tile | V^T tile]; reused for the final merge.
-  __shared__ __attribute__((aligned(16))) uint8_t s_buf[2][2][kStageBytes];
+  // [key half][stage][K tile | V tile], both row-major with swizzled 16-byte
+  // chunks, filled straight from memory; reused for the final merge.
+  __shared__ __attribute__((aligned(16))) uint8_t s_buf[2][kStages][2][kTileBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int rg = wave & 3;    // row group
   const int kh = wave >> 2;   // key half
-  const int lt = tid & (kHalfThreads - 1);  // loader id within the half
+  const int wh = wave & 3;    // wave within the half (loader role)
   const int col = lane & 31;  // query row within the wave / MFMA column
   const int hh = lane >> 5;   // lane half
 
@@ -110,51 +111,38 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkParams p) {
   const int32_t* bt = p.block_table + (size_t)seq * p.max_blocks;
   const int last_page = (kv_end - 1) >> 4;
 
-  // Loader roles (within the half): keys 2 lv_kp and 2 lv_kp + 1 (same
-  // page), 16-byte chunk lv_c, for K and for V -- each wave instruction reads
-  // four whole 256-byte key rows.
-  const int lv_kp = lt >> 4;
-  const int lv_c = lt & 15;
-
-  // Loads are unconditional (page ids clamped to the last live page, so every
-  // address is inside the pool) and keys past the end are zeroed when the
-  // tile is stored: the load counter then sees a fixed pattern and its waits
-  // leave the next tile in flight.
-  auto load_tile = [&](TileRegs& r, int it) {
+  // Loads straight into LDS (global_load_lds_dwordx4: lane l of a wave
+  // writes bytes 16 l .. of the instruction's LDS base).  Each of a half's
+  // four waves fills key rows 8 wh .. 8 wh + 7 of a tile's K and V with four
+  // instructions of four rows each; lane l takes LDS chunk slot l % 16 of
+  // row l / 16 and so loads the global chunk that the swizzle puts there.
+  // Keys past the end re-read the last key (finite: tail slots are never
+  // read), whose scores are masked and whose probabilities are 0.
+  // Page ids of the next tile to load, read one load ahead.
+  int32_t nid0 = 0, nid1 = 0;
+  auto fetch_ids = [&](int it) {
     const int t = tile0 + it;
-    const int32_t id0 = scalar_load_i32(bt, min(2 * t, last_page));
-    const int32_t id1 = scalar_load_i32(bt, min(2 * t + 1, last_page));
-    const int32_t idv = ((2 * lv_kp) >> 4) ? id1 : id0;
-    const size_t off = cache_offset(idv, g, (2 * lv_kp) & 15, lv_c * 8, p.num_kv_heads);
-    r.k[0] = *reinterpret_cast<const u32x4_t*>(p.k + off);
-    r.k[1] = *reinterpret_cast<const u32x4_t*>(p.k + off + kHeadDim);
-    r.v[0] = *reinterpret_cast<const u32x4_t*>(p.v + off);
-    r.v[1] = *reinterpret_cast<const u32x4_t*>(p.v + off + kHeadDim);
+    nid0 = scalar_load_i32(bt, min(2 * t, last_page));
+    nid1 = scalar_load_i32(bt, min(2 * t + 1, last_page));
   };
-  auto store_tile = [&](const TileRegs& r, int stage, int it) {
-    uint8_t* sk = s_buf[kh][stage];
-    uint8_t* svt = sk + kKBytes;
-    const int base = (tile0 + it) * kTileKeys;
-    const bool tile_ok = it < T;
-    const bool v0_ok = tile_ok && base + 2 * lv_kp < kv_end;
-    const bool v1_ok = tile_ok && base + 2 * lv_kp + 1 < kv_end;
-    const u32x4_t zero = u32x4_t{0u, 0u, 0u, 0u};
+  auto load_tile = [&](int it, int stage) {
+    const int t = tile0 + it;
+    const int32_t id0 = nid0, id1 = nid1;
+    fetch_ids(it + 1);
+    uint8_t* sk = s_buf[kh][stage][0];
+    uint8_t* sv = s_buf[kh][stage][1];
 #pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const int key = 2 * lv_kp + e;
-      *reinterpret_cast<u32x4_t*>(sk + key * kKRowBytes + ((lv_c ^ (key & 15)) << 4)) =
-          (e ? v1_ok : v0_ok) ? r.k[e] : zero;
-    }
-    const u32x4_t va = v0_ok ? r.v[0] : zero;
-    const u32x4_t vb = v1_ok ? r.v[1] : zero;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      // dims 8*lv_c + 2w (low halves) and + 2w + 1 (high halves)
-      const uint32_t lo = __builtin_amdgcn_perm(vb[w], va[w], 0x05040100u);
-      const uint32_t hi = __builtin_amdgcn_perm(vb[w], va[w], 0x07060302u);
-      const int d = lv_c * 8 + 2 * w;
-      *reinterpret_cast<uint32_t*>(svt + d * kVtRowBytes + lv_kp * 4) = lo;
-      *reinterpret_cast<uint32_t*>(svt + (d + 1) * kVtRowBytes + lv_kp * 4) = hi;
+    for (int j = 0; j < 2; ++j) {
+      const int r = 8 * wh + 4 * j + (lane >> 4);  // LDS row of this lane
+      const int key = min(t * kTileKeys + r, kv_end - 1);
+      const int32_t id = (key >> 4) & 1 ? id1 : id0;
+      const int c = (lane & 15) ^ (r & 15);        // global chunk for this slot
+      const size_t off = cache_offset(id, g, key & 15, c * 8, p.num_kv_heads);
+      const int lds_off = (8 * wh + 4 * j) * kRowBytes;  // wave-uniform
+      __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(p.k + off),
+                                       (void __attribute__((address_space(3)))*)(sk + lds_off), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(p.v + off),
+                                       (void __attribute__((address_space(3)))*)(sv + lds_off), 16, 0, 0);
     }
   };
 
@@ -167,8 +155,8 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkParams p) {
   float l_run = 0.f;        // this lane's share of the row sum
 
   auto compute_tile = [&](int it, int stage) {
-    const uint8_t* sk = s_buf[kh][stage];
-    const uint8_t* svt = sk + kKBytes;
+    const uint8_t* sk = s_buf[kh][stage][0];
+    const uint8_t* svv = s_buf[kh][stage][1];
     // S^T = K Q^T: A = K rows (key = col), B = Q^T (row = col).
     f32x16_t st;
 #pragma unroll
@@ -179,25 +167,82 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkParams p) {
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
       const int c = hh * 8 + s;
-      kf[s] = *reinterpret_cast<const u32x4_t*>(sk + col * kKRowBytes + ((c ^ (col & 15)) << 4));
+      kf[s] = *reinterpret_cast<const u32x4_t*>(sk + col * kRowBytes + ((c ^ (col & 15)) << 4));
     }
     __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the products
 #pragma unroll
     for (int s = 0; s < 8; ++s)
       st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf[s]), as_bf16x8(qf[s]), st, 0, 0, 0);
+    // The V^T operand of O^T += V^T P^T (lane: dim mb*32 + l % 32, keys
+    // 16 ks + 4 hh + {0..3, 8..11}) comes from the row-major V tile through
+    // transposing reads (ds_read_b64_tr_b16): in each 16-lane group, lane a
+    // points at 4 dims of key a / 4, and lane i receives dim i of the four
+    // keys.  The sixteen reads are issued here, in an asm block, so that they
+    // complete under the softmax; a second block waits for them.  (Through
+    // the builtin, the compiler would also wait for the loads into LDS still
+    // in flight, which it cannot tell apart from this stage, already
+    // complete: its loads were waited for before the barrier.)  Key + 16 is
+    // 4096 bytes further with the same swizzle; key + 8 has its own address.
+    const int grp16 = lane >> 4;
+    const int a16 = lane & 15;
+    const uint32_t vbase = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)svv;
+    u32x2_t vr[16];  // vr[4 mb + 2 ks + e]: keys 16 ks + 8 e + 4 hh + 0..3
+    {
+      uint32_t va[8];  // va[2 mb + e]: key 8 e + 4 hh + a / 4, 4 dims of block mb
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int e = 0; e < 2; ++e)
+          va[2 * mb + e] = vbase + swz(8 * e + 4 * hh + (a16 >> 2), mb * 32 + (grp16 & 1) * 16 + 4 * (a16 & 3));
+      asm volatile(
+          "ds_read_b64_tr_b16 %0, %16\n\t"
+          "ds_read_b64_tr_b16 %1, %17\n\t"
+          "ds_read_b64_tr_b16 %2, %16 offset:4096\n\t"
+          "ds_read_b64_tr_b16 %3, %17 offset:4096\n\t"
+          "ds_read_b64_tr_b16 %4, %18\n\t"
+          "ds_read_b64_tr_b16 %5, %19\n\t"
+          "ds_read_b64_tr_b16 %6, %18 offset:4096\n\t"
+          "ds_read_b64_tr_b16 %7, %19 offset:4096\n\t"
+          "ds_read_b64_tr_b16 %8, %20\n\t"
+          "ds_read_b64_tr_b16 %9, %21\n\t"
+          "ds_read_b64_tr_b16 %10, %20 offset:4096\n\t"
+          "ds_read_b64_tr_b16 %11, %21 offset:4096\n\t"
+          "ds_read_b64_tr_b16 %12, %22\n\t"
+          "ds_read_b64_tr_b16 %13, %23\n\t"
+          "ds_read_b64_tr_b16 %14, %22 offset:4096\n\t"
+          "ds_read_b64_tr_b16 %15, %23 offset:4096"
+          : "=&v"(vr[0]), "=&v"(vr[1]), "=&v"(vr[2]), "=&v"(vr[3]), "=&v"(vr[4]), "=&v"(vr[5]), "=&v"(vr[6]),
+            "=&v"(vr[7]), "=&v"(vr[8]), "=&v"(vr[9]), "=&v"(vr[10]), "=&v"(vr[11]), "=&v"(vr[12]),
+            "=&v"(vr[13]), "=&v"(vr[14]), "=&v"(vr[15])
+          : "v"(va[0]), "v"(va[1]), "v"(va[2]), "v"(va[3]), "v"(va[4]), "v"(va[5]), "v"(va[6]), "v"(va[7]));
+    }
+
     // Online softmax over this lane's 16 keys of its row (log2 domain).
+    // When every key of the tile is visible to every row (no causal mask, the
+    // tile inside the keys, a positive scale) the scores need no masking and
+    // the scale folds into the exponent's FMA.
     const int kbase = (tile0 + it) * kTileKeys + 4 * hh;
+    const bool open = !p.causal && (tile0 + it + 1) * kTileKeys <= kv_end && p.scale_log2 > 0.f;
     float sv[16];
     float mloc = -INFINITY;
+    if (open) {
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const int key = kbase + 8 * a + b;
-        const float x = (it < T && key <= my_limit) ? st[4 * a + b] * p.scale_log2 : -INFINITY;
-        sv[4 * a + b] = x;
-        mloc = fmaxf(mloc, x);
+      for (int i = 0; i < 16; ++i) {
+        sv[i] = st[i];
+        mloc = fmaxf(mloc, sv[i]);
       }
+      mloc *= p.scale_log2;
+    } else {
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const int key = kbase + 8 * a + b;
+          const float x = (it < T && key <= my_limit) ? st[4 * a + b] * p.scale_log2 : -INFINITY;
+          sv[4 * a + b] = x;
+          mloc = fmaxf(mloc, x);
+        }
+    }
     mloc = fmaxf(mloc, other_half(mloc));
     const bool raise = mloc > m_run + kRescaleSlack;
     if (__builtin_amdgcn_ballot_w64(raise) != 0) {
@@ -214,10 +259,18 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkParams p) {
     }
     const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
     float lsum = 0.f;
+    if (open) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      sv[i] = fast_exp2(sv[i] - m_use);
-      lsum += sv[i];
+      for (int i = 0; i < 16; ++i) {
+        sv[i] = fast_exp2(fmaf(sv[i], p.scale_log2, -m_use));
+        lsum += sv[i];
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        sv[i] = fast_exp2(sv[i] - m_use);
+        lsum += sv[i];
+      }
     }
     l_run += lsum;
     // P^T operand for key steps 0 and 1: keys 16ks + 4hh + 0..3, 16ks + 8 + 4hh + 0..3.
@@ -229,55 +282,50 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkParams p) {
       pf[ks][2] = pack_bf16x2(sv[8 * ks + 4], sv[8 * ks + 5]);
       pf[ks][3] = pack_bf16x2(sv[8 * ks + 6], sv[8 * ks + 7]);
     }
-    // O^T += V^T P^T.
+    // The transposed reads must have landed (the operands pass through this
+    // block, so nothing reads them before it).
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(vr[0]), "+v"(vr[1]), "+v"(vr[2]), "+v"(vr[3]), "+v"(vr[4]), "+v"(vr[5]), "+v"(vr[6]),
+                   "+v"(vr[7]), "+v"(vr[8]), "+v"(vr[9]), "+v"(vr[10]), "+v"(vr[11]), "+v"(vr[12]),
+                   "+v"(vr[13]), "+v"(vr[14]), "+v"(vr[15]));
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-      const int d = mb * 32 + col;
+    for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        // (4-byte reads: the 68-byte rows keep only 4-byte alignment)
-        const uint32_t* vrow = reinterpret_cast<const uint32_t*>(svt + d * kVtRowBytes + (16 * ks + 4 * hh) * 2);
-        const u32x4_t vf = u32x4_t{vrow[0], vrow[1], vrow[4], vrow[5]};
+        const u32x2_t l2 = vr[4 * mb + 2 * ks];
+        const u32x2_t h2 = vr[4 * mb + 2 * ks + 1];
+        const u32x4_t vf = u32x4_t{l2[0], l2[1], h2[0], h2[1]};
         o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vf), as_bf16x8(pf[ks]), o[mb], 0, 0, 0);
       }
-    }
   };
 
-  // Pipeline: a ring of two tiles in registers per half; tile it goes to
-  // LDS stage it % 2, its ring slot is refilled with tile it + 2, one
-  // barrier, then it is computed.  Two stages suffice: a wave reaches tile
-  // it + 2's store only after the barrier of tile it + 1, which every wave
-  // passes after computing tile it.  Ring loads past the half's last tile
-  // re-read a valid page and are never stored.
-  TileRegs rr[2];
+  // Pipeline: tile it sits in stage it % 4; the loads of tiles it + 1 ..
+  // it + 3 are in flight while it is computed.  Iteration it waits for its
+  // own loads, crosses one barrier (every wave's loads of tile it are then
+  // in LDS, and every wave has finished computing tile it - 1), refills the
+  // stage of tile it - 1 with tile it + 3, and computes.  Loads are
+  // unconditional (a tile index past the half clamps to the last key), so
+  // the load counter sees the same pattern on every trip.
   if (T > 0) {
-    load_tile(rr[0], 0);
-    issue_order_barrier();
-    load_tile(rr[1], 1);
-    issue_order_barrier();
+    fetch_ids(0);
+    load_tile(0, 0);
+    load_tile(1, 1);
+    load_tile(2, 2);
   }
   load_q();
-  issue_order_barrier();
-#define PA_CHUNK_STEP(K, IT, RELOAD)           \
-  do {                                         \
-    store_tile(rr[K], (IT) & 1, IT);           \
-    issue_order_barrier();                     \
-    if (RELOAD) load_tile(rr[K], (IT) + 2);    \
-    issue_order_barrier();                     \
-    __syncthreads();                           \
-    compute_tile(IT, (IT) & 1);                \
-  } while (0)
-  int it = 0;
-  for (; it + 4 <= T; it += 2) {  // every reload is a real tile
-    PA_CHUNK_STEP(0, it, true);
-    PA_CHUNK_STEP(1, it + 1, true);
+  for (int it = 0; it < T; ++it) {
+    // this wave's loads of tile it are the oldest but those of it + 1,
+    // it + 2 (4 instructions each); the query rows were loaded before the
+    // loop and are older still.
+    __builtin_amdgcn_s_waitcnt(0x0F78);  // vmcnt(8), other counters unconstrained
+    __syncthreads();
+    load_tile(it + 3, (it + 3) & (kStages - 1));
+    compute_tile(it, it & (kStages - 1));
   }
-  // The last 0 .. 3 tiles.
-  if (it < T) PA_CHUNK_STEP(0, it, it + 2 < T);
-  if (it + 1 < T) PA_CHUNK_STEP(1, it + 1, false);
-  if (it + 2 < T) PA_CHUNK_STEP(0, it + 2, false);
-#undef PA_CHUNK_STEP
-  __syncthreads();  // all computes done before the tile area is reused
+  // The loads past the last tile must land before the tile area is reused,
+  // and every wave must be done computing.
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  __syncthreads();
 
   // Merge the key halves: half 1 hands (m, l, o) to half 0 through LDS, in
   // four rounds of 16 accumulators (16 KiB per round, inside the tile area).
