@@ -14,9 +14,9 @@
 // plus one set-up workgroup that writes every slot's prefix length for the
 // suffix pass.  Eight waves: wave w takes rows 32 (w % 2) .. +32 of the tile
 // and a quarter (w / 2) of the partition's 32-key tiles; the quarters merge
-// through LDS at the end.  Per tile, as in the chunk kernel: the quarter's
-// 128 threads load K and V through the group leader's block-table row two
-// tiles ahead, store K row-major (swizzled) and V transposed to a
+// through LDS at the end.  Per tile: the quarter's 128 threads load K and V
+// through the group leader's block-table row two tiles ahead into registers,
+// store K row-major (swizzled) and V transposed (68-byte rows) to a
 // double-buffered LDS area; S^T = K Q^T and O^T += V^T P^T run on
 // v_mfma_f32_32x32x16_bf16 with the softmax mostly in-lane.  Keys past the
 // partition, the prefix or a member's own length get -inf scores.  Output:
@@ -35,7 +35,7 @@ constexpr int kTileKeys = 32;
 constexpr int kKRowBytes = kHeadDim * 2;          // 256
 constexpr int kVtRowBytes = kTileKeys * 2 + 4;    // 68: padded dim-major row (17 words)
 constexpr int kKBytes = kTileKeys * kKRowBytes;   // 8 KiB
-constexpr int kVtBytes = kHeadDim * kVtRowBytes;  // 9 KiB
+constexpr int kVtBytes = kHeadDim * kVtRowBytes;  // 8.5 KiB
 constexpr int kStageBytes = kKBytes + kVtBytes;
 constexpr float kRescaleSlack = 8.0f;             // log2 units
 
@@ -272,7 +272,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_kernel(PrefixParams p) {
     }
   };
 
-  // Pipeline as in the chunk kernel: tiles it+1, it+2 in registers while
+  // Pipeline: tiles it+1, it+2 in registers while
   // tile it is computed from LDS; double-buffered LDS, one barrier per tile.
   if (T > 0) {
     store_tile(ra, 0, 0);
