@@ -213,19 +213,22 @@ def time_kernel_launches(calls, reps):
 def parity(problem, outs, lses, ref):
     import torch
     import oracle
-    emax = emean = lmax = 0.0
+    emax = emean = lmax = worst = 0.0
     n = 0
     for l, (o_ref, l_ref, written) in ref.items():
         ob = outs[l].view(torch.int16).cpu().numpy().view(np.uint16)
         lb = lses[l].cpu().numpy().astype(np.float64)
         o = oracle.bf16_bits_to_f64(ob)
         err = np.abs(o[written] - o_ref[written])
+        # 1e-2, scaled by |o| / 2 where the exact output is 2 or more (its bf16
+        # spacing alone reaches 1e-2 there)
+        worst = max(worst, float((err / (1e-2 * np.maximum(1.0, np.abs(o_ref[written]) / 2))).max()))
         emax = max(emax, float(err.max()))
         emean = max(emean, float(err.mean()))
         lmax = max(lmax, float(np.abs(lb[written] - l_ref[written]).max()))
         n += 1
     return {"layers_checked": n, "max_abs_out": emax, "mean_abs_out": emean, "max_abs_lse": lmax,
-            "pass": bool(emax <= 1e-2 and emean <= 1e-3 and lmax <= 1e-3)}
+            "pass": bool(worst <= 1.0 and emean <= 1e-3 and lmax <= 1e-3)}
 
 
 def chunk_secondary(dev, steps, launch="graph"):

@@ -16,10 +16,19 @@ DEV = torch.device("cuda:0")
 
 # Tolerances on the output and the LSE (natural log), from the accuracy
 # budget of bf16 storage with fp32 accumulation: half a bf16 ulp at |o| < 2 is
-# 2^-8 ~ 0.004, inside the max bound; the mean stays near 2^-10.
+# at most 2^-8 ~ 0.004, inside the max bound; the mean stays near 2^-10.
+# Where the exact output itself is 2 or more in magnitude, its bf16 spacing
+# alone reaches the bound (half an ulp is 0.0078 on [2, 4), 0.0156 on
+# [4, 8)), so there the max bound scales with it: TOL_MAX * |o| / 2, a 0.5 %
+# relative bound (half an ulp is at most 0.39 % of |o|).
 TOL_MAX = 1e-2
 TOL_MEAN = 1e-3
 TOL_LSE = 1e-3
+
+
+def out_bound(exact: np.ndarray) -> np.ndarray:
+    """Per-element bound on |out - exact| for exact outputs `exact`."""
+    return TOL_MAX * np.maximum(1.0, np.abs(exact) / 2.0)
 
 OUT_SENTINEL = 0x7F81         # a bf16 NaN pattern no kernel produces
 LSE_SENTINEL = 0x7FC12345     # an fp32 NaN pattern no kernel produces
@@ -75,7 +84,8 @@ def compare(problem, gpu, ref, *, label=""):
     assert np.isfinite(o[written]).all(), f"{label}: non-finite output"
     emax = float(err.max()) if err.size else 0.0
     emean = float(err.mean()) if err.size else 0.0
-    assert emax <= TOL_MAX, f"{label}: max |dout| {emax:.3e}"
+    ratio = float((err / out_bound(out[written])).max()) if err.size else 0.0
+    assert ratio <= 1.0, f"{label}: max |dout| {emax:.3e} ({ratio:.3f} of its bound)"
     assert emean <= TOL_MEAN, f"{label}: mean |dout| {emean:.3e}"
     if lb is not None:
         el = np.abs(lb[written].astype(np.float64) - lse[written])

@@ -1,7 +1,8 @@
 """GPU parity: the HIP path (through the C ABI) against the FP64 oracle.
 
-Tolerances: output max |d| <= 1e-2, mean |d| <= 1e-3, LSE max |d| <= 1e-3 on
-every written row; rows of inactive slots keep their sentinel bytes exactly.
+Tolerances: output max |d| <= 1e-2 (scaled by |o| / 2 where the exact output
+is 2 or more in magnitude: its bf16 spacing alone reaches 1e-2 there), mean
+|d| <= 1e-3, LSE max |d| <= 1e-3 on every written row; rows of inactive slots keep their sentinel bytes exactly.
 Bit-exact checks: page gather, page placement, shared-versus-copied prefix,
 single-key output, repeat determinism.
 """
@@ -206,6 +207,21 @@ def test_lse_optional():
     ob, lb = run_gpu(p, with_lse=False, partition_size=32)
     assert lb is None
     compare(p, (ob, None), run_oracle(p), label="no lse")
+
+
+def test_long_contexts_many_partitions():
+    # 2 slots x 65536 keys on 8 KV heads: 32 partitions of 128 pages, so the
+    # merge folds its partials in two batches (24 + 8); plus a batch of 600
+    # short slots (4800 (slot, KV head) pairs, several rounds of workgroups).
+    p = _case([65536, 61000], hq=32, hkv=8, seed=91)
+    shape = pk.make_shape(p.num_seqs, p.total_q, 32, 8, p.max_blocks_per_seq, 1, p.max_ctx_len, p.num_blocks)
+    assert pk.plan(shape)[1] == 32
+    say("decode 2 x 65536 keys")
+    compare(p, run_gpu(p), run_oracle(p), label="long contexts")
+    rng = np.random.default_rng(92)
+    q = _case([int(x) for x in rng.integers(1, 300, 600)], hq=32, hkv=8, seed=93)
+    say("decode 600 short slots")
+    compare(q, run_gpu(q), run_oracle(q), label="600 slots")
 
 
 # ---------------------------------------------------------------------------

@@ -16,7 +16,7 @@ import torch
 import paged_kv_cache_attend_amd as pk
 from paged_kv_cache_attend_amd import inputs
 
-from gpu_util import DEV, LSE_SENTINEL, OUT_SENTINEL, compare, run_gpu, run_oracle, say
+from gpu_util import DEV, LSE_SENTINEL, OUT_SENTINEL, compare, out_bound, run_gpu, run_oracle, say
 
 pytestmark = pytest.mark.gpu
 
@@ -133,7 +133,7 @@ def test_prefix_full_size_shared_prefix_decode():
     rows[seqs] = True
     o = inputs_bf16(ob[rows])
     err = np.abs(o - out[rows])
-    assert err.max() <= 1e-2 and err.mean() <= 1e-3, (err.max(), err.mean())
+    assert (err <= out_bound(out[rows])).all() and err.mean() <= 1e-3, (err.max(), err.mean())
     assert np.abs(lb[rows] - lse[rows]).max() <= 1e-3
     base = run_gpu(p)
     d = np.abs(inputs_bf16(ob) - inputs_bf16(base[0]))

@@ -22,7 +22,7 @@ from oracle import quant
 from oracle.paging import write_kv as ref_scatter
 from paged_kv_cache_attend_amd import inputs
 
-from gpu_util import DEV, LSE_SENTINEL, OUT_SENTINEL, compare, say
+from gpu_util import DEV, LSE_SENTINEL, OUT_SENTINEL, compare, out_bound, say
 
 pytestmark = pytest.mark.gpu
 
@@ -107,7 +107,7 @@ def test_attend_kv_full_size_qwen3_short_decode(fmt):
     rows[seqs] = True
     o = oracle.bf16_bits_to_f64(ob[rows])
     err = np.abs(o - out[rows])
-    assert err.max() <= 1e-2 and err.mean() <= 1e-3, (err.max(), err.mean())
+    assert (err <= out_bound(out[rows])).all() and err.mean() <= 1e-3, (err.max(), err.mean())
     assert np.abs(lb[rows] - lse[rows]).max() <= 1e-3
     assert np.isfinite(oracle.bf16_bits_to_f64(ob)).all()
 
