@@ -50,8 +50,12 @@
 //   its normalised fp32 partial and LSE to the workspace, and the last of the
 //   slot's partitions to finish (an atomic counter per (slot, KV head),
 //   reset to zero by that same workgroup) merges all partials by their LSE
-//   and writes the result, all in the same launch.  Empty partitions and slots with no keys take part
-//   with LSE = -inf; a slot whose partials are all -inf writes nothing.
+//   and writes the result, all in the same launch.  Empty partitions and
+//   slots with no keys take part with LSE = -inf; a slot whose partials are
+//   all -inf writes nothing.
+// * Prefix-grouped decode (pa_attend_prefix): a grouped slot's partitions
+//   start after its group's shared prefix, and the merge also folds the
+//   prefix pass's partials of the slot's rows (written by the launch before).
 
 #include "device.h"
 

@@ -21,13 +21,13 @@ constexpr int kNumXCDs = 8;
 constexpr int kDecodeWaves = PA_DECODE_WAVES;          // waves per decode workgroup
 constexpr int kDecodeWGsPerCU = 8 / kDecodeWaves;      // resident per CU (2 waves per SIMD)
 
-// Split-KV decode: one workgroup per (KV head, slot, partition).
 // Page formats of the K/V caches (values of pa_kv_format in pa.h).
 constexpr int kFmtBF16 = 0;
 constexpr int kFmtFP8 = 1;   // OCP E4M3 codes, one fp32 scale per cache
 constexpr int kFmtQ8 = 2;    // q8_0: int8 codes, fp16 scale per 32 values
 constexpr int kFmtQ4 = 3;    // q4_0: 4-bit codes, fp16 scale per 32 values
 
+// Split-KV decode: one workgroup per (KV head, slot, partition).
 struct DecodeParams {
   const uint16_t* q;          // bf16 [total_q][Hq][128]
   const uint16_t* k;          // page codes: bf16 [num_blocks][Hkv][16][128], or the
@@ -44,9 +44,9 @@ struct DecodeParams {
   const int32_t* block_table; // [num_seqs][max_blocks]
   const int32_t* ctx_lens;
   const int32_t* q_lens;
-  uint16_t* out;              // bf16 [total_q][Hq][128]      (num_parts == 1)
-  float* lse;                 // fp32 [total_q][Hq] or null   (num_parts == 1)
-  float* part_out;            // fp32 [num_parts][total_q*Hq][128] (num_parts > 1)
+  uint16_t* out;              // bf16 [total_q][Hq][128]: the result
+  float* lse;                 // fp32 [total_q][Hq] or null
+  float* part_out;            // fp32 [num_parts][total_q*Hq][128] (split: num_parts > 1)
   float* part_lse;            // fp32 [num_parts][total_q*Hq]
   int32_t* counters;          // [num_seqs][Hkv] finished partitions; zero between calls
   float scale_log2;           // softmax scale * log2(e)
