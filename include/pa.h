@@ -194,12 +194,14 @@ pa_status pa_validate(const pa_shape* shape, const int32_t* block_table,
  * by log-sum-exp.
  *
  * Groups are runs of consecutive slots [group_start[k], group_start[k+1]).
- * Preconditions for group k with prefix length L = prefix_len[k] (a multiple
- * of 16): for every member r, block_table[r][0 .. L/16) equals row
+ * Group k's prefix is its first L = prefix_len[k] keys, read as the
+ * floor(L/16) whole pages they cover (the rest are ordinary keys).
+ * Preconditions: for every member r, block_table[r][0 .. L/16) equals row
  * group_start[k]'s first L/16 entries, and ctx_lens[r] >= L for members with
- * new tokens.  Slots outside every group have no prefix.  Decode only
- * (max_q_len == 1, 1, 2 or 4 query heads per KV head): other shapes return
- * PA_ERR_UNSUPPORTED. */
+ * new tokens.  Slots outside every group, and slots past a group's first
+ * max_members, have no prefix (their keys are all read by the decode pass;
+ * the result is the same).  Decode only (max_q_len == 1, 1, 2 or 4 query
+ * heads per KV head): other shapes return PA_ERR_UNSUPPORTED. */
 typedef struct pa_prefix_groups {
   int32_t num_groups;
   int32_t max_members;         /* >= slots in any group */
