@@ -204,7 +204,7 @@ pa_status pa_validate(const pa_shape* shape, const int32_t* block_table,
  * heads per KV head): other shapes return PA_ERR_UNSUPPORTED. */
 typedef struct pa_prefix_groups {
   int32_t num_groups;
-  int32_t max_members;         /* >= slots in any group */
+  int32_t max_members;         /* prefix rows per group: a group's first max_members slots */
   int32_t max_prefix_len;      /* >= every prefix_len; a multiple of 16, <= max_ctx_len */
   int32_t min_prefix_len;      /* <= the prefix of every slot with new tokens (0 if some have
                                   none); a multiple of 16.  Sizes the suffix split only. */
