@@ -110,6 +110,30 @@ def copy_mode(steps: int):
                       "copy_gbs_read_plus_write": 2 * n / (ms * 1e-3) / 1e9}), flush=True)
 
 
+def copy_ceiling(dev, steps: int = 20):
+    """Read+write GB/s of a plain 1 GiB device-to-device copy on the launch
+    stream: the rate a streaming kernel can hope for on this device."""
+    import torch
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    stream = torch.cuda.current_stream()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        dst.copy_(src)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2 * n / (ms * 1e-3) / 1e9
+
+
 def build_decode(problem, dev, want_oracle: bool, cpu_budget_s: float):
     """Upload every layer; run the oracle on layers while the CPU budget lasts."""
     import torch
@@ -255,7 +279,11 @@ def chunk_secondary(dev, steps, launch="graph"):
     return {"workload": "chunked_denoise", "flop_per_call": flops,
             "tflops_cold": flops / (cold_ms * 1e-3) / 1e12, "tflops_warm": flops / (warm_ms * 1e-3) / 1e12,
             "ms_cold": cold_ms, "ms_warm": warm_ms,
-            "frac_of_bf16_peak_warm": flops / (warm_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS}
+            "frac_of_bf16_peak_warm": flops / (warm_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+            # the call reads and writes 63,012,864 B: AI = 204.5 FLOP/B, so cold
+            # it is capped at min(peak, AI x 8 TB/s) = 1,636 TFLOP/s
+            "frac_of_roofline_cold": flops / (cold_ms * 1e-3) / 1e12
+            / min(BF16_PEAK_TFLOPS, flops / 63012864 * HBM_PEAK_GBS / 1e3)}
 
 
 class _WriteCall:
@@ -405,6 +433,8 @@ def prefix_secondary(dev, steps, launch="graph"):
             "pa_attend_us_per_layer": b_us, "pa_attend_prefix_us_per_layer": g_us,
             "pa_attend_gbs_unique": unique / (b_us * 1e-6) / 1e9,
             "pa_attend_prefix_gbs_unique": unique / (g_us * 1e-6) / 1e9,
+            "pa_attend_effective_gbs": p.kv_bytes_read() / (b_us * 1e-6) / 1e9,
+            "pa_attend_prefix_effective_gbs": p.kv_bytes_read() / (g_us * 1e-6) / 1e9,
             "speedup": b_us / g_us,
             "parity": "against the FP64 oracle and pa_attend in the GPU tests"}
 
@@ -489,6 +519,7 @@ def main():
                    "cores": ncores, "kind": "oracle", "sample": f"{len(ref)} call(s), 1 BLAS thread, {cpu_s:.1f}s"}
         cpu["cpu_model"] = platform.processor() or platform.machine()
 
+    ceiling = copy_ceiling(dev) if decode and not args.quick else None
     secondary = None
     if decode and not args.no_chunk:
         secondary = chunk_secondary(dev, args.steps, args.launch)
@@ -530,6 +561,8 @@ def main():
             "accumulate": "fp32",
         },
         "frac_of_hbm_peak": (value / HBM_PEAK_GBS) if decode else None,
+        "copy_ceiling_gbs": ceiling,
+        "frac_of_copy_ceiling": (value / ceiling) if ceiling else None,
         "kv_bytes_per_step": kv_read if decode else None,
         "kv_unique_bytes_per_step": kv_unique if decode else None,
         "effective_gbs": (kv_read / (ms * 1e-3) / 1e9) if decode else None,
