@@ -312,20 +312,6 @@ __device__ __forceinline__ void consume_page(WaveState<G>& st, Page<F>& b, const
   }
 }
 
-// Scalar prefix sum of q_lens[0 .. seq): the row of slot `seq`'s new token.
-__device__ __forceinline__ int q_row_scalar(const int32_t* q_lens, int seq) {
-  int s = 0;
-  int i = 0;
-  for (; i + 16 <= seq; i += 16) {
-    int t = 0;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) t += scalar_load_i32(q_lens, i + j);
-    s += t;
-  }
-  for (; i < seq; ++i) s += scalar_load_i32(q_lens, i);
-  return s;
-}
-
 template <int G, int F>
 __global__ __launch_bounds__(kDecodeThreads, kDecodeWGsPerCU) void decode_kernel(DecodeParams p) {
   static_assert(G == 1 || G == 2 || G == 4, "group size");
@@ -341,6 +327,10 @@ __global__ __launch_bounds__(kDecodeThreads, kDecodeWGsPerCU) void decode_kernel
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // The kernel arguments the start needs, fetched together (the compiler
+  // would otherwise fetch some of them one round trip later).
+  asm volatile("" ::"s"(p.q_lens), "s"(p.ctx_lens), "s"(p.block_table), "s"(p.slot_plen), "s"(p.num_parts),
+               "s"(p.num_seqs), "s"(p.part_pages), "s"(p.max_blocks), "s"(gridDim.x));
 
   const int wg = xcd_remap(blockIdx.x, gridDim.x);
   const int P = p.num_parts;
@@ -349,24 +339,44 @@ __global__ __launch_bounds__(kDecodeThreads, kDecodeWGsPerCU) void decode_kernel
   const int seq = rest % p.num_seqs;
   const int g = rest / p.num_seqs;
 
-  // Lengths, row offset and page ids are wave-uniform: scalar loads, which
-  // do not share the (in-order) vector load counter with the page stream.
+  // Everything the start needs comes in one round trip, issued before the
+  // first branch: the lengths, the prefix length, the slot's row offset (a
+  // vector load and a wave sum) and the page ids of this wave's first four
+  // pages as they are when the slot has no prefix (checked below, reloaded
+  // otherwise).  Lengths and page ids are wave-uniform scalar loads, which do
+  // not share the (in-order) vector load counter with the page stream.
+  const int32_t* bt = p.block_table + (size_t)seq * p.max_blocks;
+  const int spage0 = part * p.part_pages + wave;  // first page without a prefix
   const int m = scalar_load_i32(p.q_lens, seq);
-  if (m <= 0) return;  // no row: nothing to write, no partial to count
   const int n = scalar_load_i32(p.ctx_lens, seq);
-  const int npages = (n + kBlockSize - 1) / kBlockSize;
   // Prefix-grouped decode: this slot's keys start after its shared prefix,
   // whose partials the prefix pass has written; the last partition runs to
   // the slot's end whatever the prefix length.
   const int plen = p.slot_plen ? scalar_load_i32(p.slot_plen, seq) : 0;
+  int32_t sid[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) sid[k] = scalar_load_i32(bt, min(spage0 + k * kWaves, p.max_blocks - 1));
+  int qsum = 0;  // this lane's share of the row offset
+  for (int i = lane; i < seq; i += 64) qsum += p.q_lens[i];
+  // (Keeps the loads above the branch: the compiler would otherwise sink the
+  // ones only the working path uses below it, one round trip later.  The
+  // wave sum of the row offset waits until the first page is requested.)
+  asm volatile("" : "+s"(sid[0]), "+s"(sid[1]), "+s"(sid[2]), "+s"(sid[3]), "+v"(qsum));
+  if (m <= 0) return;  // no row: nothing to write, no partial to count
+  const int npages = (n + kBlockSize - 1) / kBlockSize;
   const int npre = (plen > 0 && n > 0) ? p.pre_parts : 0;
   const int pstart = plen / kBlockSize + part * p.part_pages;
   const int pend = part == P - 1 ? npages : min(npages, pstart + p.part_pages);
   const bool has_work = n > 0 && pstart < pend;
 
-  const int32_t* bt = p.block_table + (size_t)seq * p.max_blocks;
   const int last_page = pend - 1;
   auto page_id = [&](int page) -> int32_t { return scalar_load_i32(bt, min(page, last_page)); };
+  // Page id of this wave's k-th page (clamped to the partition's last page):
+  // the early load when it is that page.
+  auto first_id = [&](int k) -> int32_t {
+    const int page = pstart + wave + k * kWaves;
+    return (plen == 0 && page <= last_page) ? sid[k] : page_id(page);
+  };
 
   const int h0 = g * G;
   const size_t rows = (size_t)p.total_q * p.num_q_heads;
@@ -383,24 +393,24 @@ __global__ __launch_bounds__(kDecodeThreads, kDecodeWGsPerCU) void decode_kernel
   Page<F> ring0, ring1, ring2;
   const int page0 = pstart + wave;
   const int cnt = (has_work && page0 < pend) ? (pend - page0 + kWaves - 1) / kWaves : 0;
-  int q_row = 0;
   int32_t next_id = 0;
+  int q_row;
   if (has_work) {
-    issue_page<F>(ring0, p, page_id(page0), g, lane);
-    issue_order_barrier();
-    q_row = q_row_scalar(p.q_lens, seq);
+    issue_page<F>(ring0, p, first_id(0), g, lane);
+    __builtin_amdgcn_sched_barrier(0);  // the first page goes out before the row-offset sum
+    q_row = __builtin_amdgcn_readfirstlane(wave_sum_i32(qsum));
     const int qh = (threadIdx.x >> 4) % G, qc = threadIdx.x & 15;
     const u32x4_t qchunk =
         reinterpret_cast<const u32x4_t*>(p.q)[((size_t)q_row * p.num_q_heads + h0 + qh) * 16 + qc];
     issue_order_barrier();
-    issue_page<F>(ring1, p, page_id(page0 + kWaves), g, lane);
-    issue_page<F>(ring2, p, page_id(page0 + 2 * kWaves), g, lane);
-    next_id = page_id(page0 + 3 * kWaves);
+    issue_page<F>(ring1, p, first_id(1), g, lane);
+    issue_page<F>(ring2, p, first_id(2), g, lane);
+    next_id = first_id(3);
     // Query of heads h0 .. h0+G-1 -> LDS, 16-byte chunk c of head h at slot c ^ h.
     if (threadIdx.x < G * 16) *reinterpret_cast<u32x4_t*>(&s_q[qh][(qc ^ qh) << 4]) = qchunk;
     __syncthreads();
   } else {
-    q_row = q_row_scalar(p.q_lens, seq);
+    q_row = __builtin_amdgcn_readfirstlane(wave_sum_i32(qsum));
   }
 
   if (has_work) {
