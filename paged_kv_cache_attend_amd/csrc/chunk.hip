@@ -81,8 +81,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkParams p) {
   const int m = scalar_load_i32(p.q_lens, seq);
   const int n = scalar_load_i32(p.ctx_lens, seq);
   if (m <= 0 || n <= 0 || qt * kChunkRows >= m) return;
-  int q_row0 = 0;
-  for (int i = 0; i < seq; ++i) q_row0 += scalar_load_i32(p.q_lens, i);
+  int q_row0 = 0;  // row offset of the slot, summed once the first tiles are requested
   const int row = qt * kChunkRows + rg * 32 + col;  // row within the slot
   const bool row_live = row < m;
 
@@ -311,6 +310,20 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkParams p) {
     load_tile(0, 0);
     load_tile(1, 1);
     load_tile(2, 2);
+  }
+  // Sixteen independent scalar loads per batch (indices clamped into the
+  // array, the extra ones masked), one wait each: scalar loads leave the
+  // vector load counter, which tracks the tiles, alone.
+  for (int i = 0; i < seq; i += 16) {
+    int x[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) x[j] = scalar_load_i32(p.q_lens, min(i + j, seq - 1));
+    // (all sixteen in flight before the first is used)
+    asm volatile("" : "+s"(x[0]), "+s"(x[1]), "+s"(x[2]), "+s"(x[3]), "+s"(x[4]), "+s"(x[5]), "+s"(x[6]),
+                 "+s"(x[7]), "+s"(x[8]), "+s"(x[9]), "+s"(x[10]), "+s"(x[11]), "+s"(x[12]), "+s"(x[13]),
+                 "+s"(x[14]), "+s"(x[15]));
+#pragma unroll
+    for (int j = 0; j < 16; ++j) q_row0 += i + j < seq ? x[j] : 0;
   }
   load_q();
   for (int it = 0; it < T; ++it) {

@@ -273,6 +273,19 @@ def test_chunk_path(ctx, ql, hq, hkv, causal):
     compare(p, run_gpu(p), run_oracle(p), label=f"chunk {ctx} {ql} causal={causal}")
 
 
+@pytest.mark.parametrize("num_seqs", [37, 70])
+def test_chunk_path_many_slots(num_seqs):
+    # the row offset of a slot sums the query lengths of all earlier slots
+    # (in batches of 16 in the kernel): slots past 16, 32 and 64, some with
+    # no query rows
+    rng = np.random.default_rng(num_seqs)
+    ctx = rng.integers(1, 120, size=num_seqs)
+    ql = np.minimum(ctx, rng.integers(0, 6, size=num_seqs))
+    p = _case(ctx.tolist(), ql.tolist(), hq=4, hkv=2, seed=num_seqs, causal=True)
+    say(f"chunk many slots: {num_seqs}")
+    compare(p, run_gpu(p), run_oracle(p), label=f"chunk {num_seqs} slots")
+
+
 def test_chunk_path_handles_group_sizes_without_decode_kernel():
     # 8 query heads per KV head with one row each takes the MFMA path
     p = _case([37, 100, 1000], hq=64, hkv=8, seed=43)
