@@ -126,8 +126,8 @@ pa_status pa_workspace_init(const pa_shape* shape, void* workspace, size_t works
 int32_t pa_num_partitions(const pa_shape* shape);
 
 /* The same for pa_attend_kv with pages in `format` (a pa_kv_format): with
- * an automatic partition size, compressed pages are split into more
- * partitions; 0 for an invalid shape or format. */
+ * an automatic partition size, q8_0 / q4_0 pages are split into more
+ * partitions than bf16 and FP8 ones; 0 for an invalid shape or format. */
 int32_t pa_num_partitions_kv(const pa_shape* shape, int32_t format);
 
 /* Attention of the new rows against the paged cache, as defined above.

@@ -78,13 +78,13 @@ pa_status check_kv_cache(const pa_kv_cache& c) {
 //    the partition count whose grid fills its last round of CUs best, then
 //    (bf16 pages) the one whose partitions are nearest 64 pages -- long
 //    enough to amortise the workgroup's start and merge, short enough to
-//    keep two workgroups per CU streaming -- or (compressed pages) more
+//    keep two workgroups per CU streaming -- or (q8_0 / q4_0 pages) more
 //    partitions;
 //  - with more (slot, KV head) pairs than that, the grid is several rounds
 //    anyway; long contexts are cut into partitions of at most 128 pages so
 //    that a batch's longest requests do not finish last on their own.
 // No partition is smaller than 8 pages (two per wave).
-int auto_part_pages(const pa_shape* s, int max_pages, bool compressed) {
+int auto_part_pages(const pa_shape* s, int max_pages, bool grouped) {
   constexpr int kMinPages = 8, kGoodPages = 64, kLongPages = 128;
   const long long pairs = (long long)s->num_seqs * s->num_kv_heads;
   const long long resident = (long long)kDecodeWGsPerCU * kNumCUs;
@@ -100,11 +100,14 @@ int auto_part_pages(const pa_shape* s, int max_pages, bool compressed) {
     const double rounds = (double)(pairs * parts) / kNumCUs;
     const double fill = rounds / std::ceil(rounds);
     // Distance of the partition size from 64 pages (a ratio, >= 1).
-    // Compressed pages carry fewer bytes for the same per-page work, so more,
-    // smaller partitions (more resident waves per CU) win there (measured on
-    // the Qwen3-8B-shaped batch: 2 -> 4 partitions, 10-15 % faster): every
-    // size counts as good and later (more) partitions win ties.
-    const double dist = compressed ? 1.0 : std::max((double)pp / kGoodPages, (double)kGoodPages / pp);
+    // q8_0 / q4_0 pages carry fewer bytes for more per-page work (codes and
+    // group scales converted in registers), so more, smaller partitions
+    // (more resident waves per CU) win there (measured on the Qwen3-8B-shaped
+    // batch: 2 -> 4 partitions, 10-15 % faster): every size counts as good
+    // and later (more) partitions win ties.  FP8 pages convert in one
+    // instruction per two values and follow the bf16 rule (2 partitions
+    // measured 7 % faster than 4).
+    const double dist = grouped ? 1.0 : std::max((double)pp / kGoodPages, (double)kGoodPages / pp);
     // Ties in fill (within 1%) go to the size nearer 64 pages, then to more
     // partitions.
     const bool better = fill > best_fill + 0.01 || (fill > best_fill - 0.01 && dist <= best_dist * 1.0001);
@@ -117,7 +120,7 @@ int auto_part_pages(const pa_shape* s, int max_pages, bool compressed) {
   return best_pp;
 }
 
-pa_status make_plan(const pa_shape* s, Plan* plan, bool compressed = false) {
+pa_status make_plan(const pa_shape* s, Plan* plan, bool grouped = false) {
   const pa_status st = check_shape(s);
   if (st != PA_OK) return st;
   Plan p;
@@ -131,7 +134,7 @@ pa_status make_plan(const pa_shape* s, Plan* plan, bool compressed = false) {
   p.decode = (s->max_q_len == 1) && decode_supports_group(p.group);
   if (p.decode) {
     const int max_pages = ceil_div(s->max_ctx_len, kBlockSize);
-    p.part_pages = s->partition_size > 0 ? s->partition_size / kBlockSize : auto_part_pages(s, max_pages, compressed);
+    p.part_pages = s->partition_size > 0 ? s->partition_size / kBlockSize : auto_part_pages(s, max_pages, grouped);
     p.num_parts = ceil_div(max_pages, p.part_pages);
     const long long grid = (long long)s->num_kv_heads * s->num_seqs * p.num_parts;
     if (grid > INT_MAX) return PA_ERR_UNSUPPORTED;
@@ -198,7 +201,7 @@ pa_status attend_impl(const pa_shape* shape, const pa_kv_cache& kv, const void* 
   const void* v_cache = kv.v_codes;
   const bool grouped = kv.format == kFmtQ8 || kv.format == kFmtQ4;
   Plan plan;
-  const pa_status st = make_plan(shape, &plan, kv.format != kFmtBF16);
+  const pa_status st = make_plan(shape, &plan, grouped);
   if (st != PA_OK) return st;
   if (!std::isfinite(scale)) return PA_ERR_BAD_SHAPE;
   if (plan.empty) return PA_OK;
@@ -322,7 +325,7 @@ int32_t pa_num_partitions(const pa_shape* shape) {
 int32_t pa_num_partitions_kv(const pa_shape* shape, int32_t format) {
   if (format < kFmtBF16 || format > kFmtQ4) return 0;
   Plan p;
-  if (make_plan(shape, &p, format != kFmtBF16) != PA_OK) return 0;
+  if (make_plan(shape, &p, format == kFmtQ8 || format == kFmtQ4) != PA_OK) return 0;
   return p.decode ? p.num_parts : 1;
 }
 

@@ -27,24 +27,26 @@
 //   chunks -- 8, 8 or 4 bytes instead of 16 -- plus, for q8_0 / q4_0, the
 //   fp16 scale of each chunk's 32-value group, and turns the codes into bf16
 //   in registers (exact: E4M3 values and small integers are bf16 values).
-//   Group scales multiply the per-group partial scores of K and the PV
-//   weights of V; FP8's per-cache K scale is folded into the softmax scale
-//   and its V scale into the weights.
-// * Scores: the K tile goes to LDS (XOR-swizzled 16-byte chunks, conflict
-//   free); lane (token t = lane % 16, head h = lane / 16) forms the 128-long
-//   dot product of its query head with key t using v_dot2c_f32_bf16 against
-//   the query staged in LDS, so the group of query heads shares one read of
-//   each key.
-// * Online softmax in the log2 domain (scale * log2 e folded in): per-head
-//   row max over the 16 tokens with DPP row rotations; the reference max is
-//   only raised (and the accumulators rescaled) when a score exceeds it by
-//   more than 2^8, which keeps every weight <= 256 and skips the rescale on
-//   almost every page.
-// * PV: the V tile stays in registers in its load layout (lane holds 8 dims
-//   of tokens 4k + lane/16).  Weights reach that layout through a small LDS
-//   buffer, are rounded to bf16 and paired by token; v_perm pairs the V
-//   values the same way, and v_dot2c_f32_bf16 accumulates two tokens per
-//   instruction in fp32.
+//   FP8's per-cache K scale is folded into the softmax scale and its V scale
+//   into the result; group scales are applied as described below.
+// * Each page runs on the matrix cores.  The K and V tiles go to LDS as bf16
+//   (XOR-swizzled 16-byte chunks).  Scores S^T = K Q^T come from four
+//   v_mfma_f32_16x16x32_bf16 (16 tokens x 32 dims each), with the group's
+//   query heads as the first G of 16 columns (the rest a zero query); a
+//   32-dim step is exactly one q8_0 / q4_0 group, so each step's product is
+//   weighted by its tokens' K scales before the sum.  In that output layout
+//   a lane holds 4 tokens of one head, so the online softmax (log2 domain,
+//   scale * log2 e folded in) takes an in-lane max and two lane exchanges
+//   (v_permlane16_swap, v_permlane32_swap); the reference max is only
+//   raised (and the accumulators rescaled) when a score exceeds it by more
+//   than 2^8, which keeps every weight <= 256.
+// * PV: the same lanes hold P^T in exactly the B-operand layout of
+//   v_mfma_f32_16x16x16_bf16, so the weights (times each token's V group
+//   scale, one operand per 32-dim group) are rounded to bf16 and used from
+//   registers; the V^T A operand is read from the V tile with transposing
+//   LDS reads (ds_read_b64_tr_b16), eight 16-dim blocks per page.  Rows past
+//   a slot's end are zeroed in the V tile and get weight 0 by select, since
+//   their stored codes and scales may be anything.
 // * Epilogue: the four waves' (max, sum, acc) merge through LDS.  With one
 //   partition the workgroup writes bf16 out and the LSE.  Otherwise it writes
 //   its normalised fp32 partial and LSE to the workspace, and the last of the
@@ -170,145 +172,138 @@ __device__ __forceinline__ u32x4_t chunk_to_bf16(const T& c) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// One page on the matrix cores (v_mfma_f32_16x16x32_bf16 for the scores,
+// v_mfma_f32_16x16x16_bf16 for PV): S^T = K Q^T is 16 tokens x 16 columns
+// (column n = query head n of the group, columns past G padded with a zero
+// query), and O^T += V^T P^T with P^T taken straight from the score layout.
+// ---------------------------------------------------------------------------
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(const u32x4_t& u) { return __builtin_bit_cast(bf16x8_t, u); }
+__device__ __forceinline__ s16x4_t as_s16x4(uint32_t lo, uint32_t hi) {
+  return __builtin_bit_cast(s16x4_t, u32x2_t{lo, hi});
+}
+
 template <int G>
 struct WaveState {
-  float m_ref;      // reference max (log2 domain) of head hq, uniform over its row
-  float l_lane;     // this lane's running sum of weights
-  float acc[G][8];  // PV layout accumulators
+  float m_ref;    // reference max (log2 domain) of head lane % 16
+  float l_lane;   // this lane's share (tokens 4 (lane / 16) .. + 4 of each page) of that head's sum
+  f32x4_t o[8];   // O^T block b: dims 16 b + 4 (lane / 16) + i of head lane % 16
+  u32x4_t qb[4];  // Q^T operand of step s: dims 32 s + 8 (lane / 16) .. + 8 of head lane % 16
 };
 
-// One page: scores, online softmax, PV.  `sk` is this wave's 4 KiB LDS tile
-// (bf16), `sks` its 16 x 4 K group scales, `sp` its 16 x 4 weight buffer,
-// `salpha` its 4 rescale factors.
+// `sk` / `sv` are this wave's 4 KiB LDS tiles, `sks` / `svs` its 16 x 4
+// group scales (q8_0, q4_0).
 template <int G, int F>
-__device__ __forceinline__ void consume_page(WaveState<G>& st, Page<F>& b, const uint8_t* sq,
-                                             uint8_t* sk, float* sks, float* sp, float* salpha,
-                                             int valid, float scale_log2, float v_scale, int lane) {
-  const int tq = lane & 15;
-  const int hq = (lane >> 4) % G;
+__device__ __forceinline__ void consume_page(WaveState<G>& st, Page<F>& b, uint8_t* sk, uint8_t* sv,
+                                               float* sks, float* svs, int valid, float scale_log2, int lane) {
   const int pr = lane >> 4;
   const int pc = lane & 15;
   constexpr bool kGrouped = F == kFmtQ8 || F == kFmtQ4;
 
-  // K tile -> LDS as bf16.  Row t (256 B) keeps its 16-byte chunk c at slot c ^ t.
+  // K and V tiles -> LDS as bf16, row t keeping its 16-byte chunk c at slot
+  // c ^ t.  V rows past the end are zeroed: their codes may decode to
+  // anything, NaN included, and a zero weight would not cancel that.
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const int t = 4 * k + pr;
     *reinterpret_cast<u32x4_t*>(sk + t * 256 + ((pc ^ t) << 4)) = chunk_to_bf16<F>(b.k[k]);
+    const u32x4_t vv = chunk_to_bf16<F>(b.v[k]);
+    *reinterpret_cast<u32x4_t*>(sv + t * 256 + ((pc ^ t) << 4)) = t < valid ? vv : u32x4_t{0u, 0u, 0u, 0u};
   }
-  if constexpr (kGrouped) sks[lane] = half_bits_to_float(b.ks);  // [token][group]
+  if constexpr (kGrouped) {
+    sks[lane] = half_bits_to_float(b.ks);  // [token][group]
+    svs[lane] = half_bits_to_float(b.vs);
+  }
   wave_lds_sync();
 
-  // Score of (token tq, head hq).  The query of head h keeps its 16-byte chunk
-  // c at slot c ^ h, so the four heads' broadcast reads use different banks.
-  float s = 0.f;
+  // Scores: A = K (row = token pc, dims 32 s + 8 pr .. + 8 of step s), B = Q^T.
+  // A group of 32 dims is one step, so grouped scales weight each step's
+  // product (its own accumulator) before the sum.
+  f32x4_t s4 = {0.f, 0.f, 0.f, 0.f};
   if constexpr (kGrouped) {
+    f32x4_t ksc[4];  // K scales of this lane's tokens 4 pr + i, groups 0..3
 #pragma unroll
-    for (int gr = 0; gr < 4; ++gr) {
-      float sg = 0.f;
+    for (int i = 0; i < 4; ++i) ksc[i] = *reinterpret_cast<const f32x4_t*>(sks + (4 * pr + i) * 4);
 #pragma unroll
-      for (int i = 4 * gr; i < 4 * gr + 4; ++i) {
-        const u32x4_t kk = *reinterpret_cast<const u32x4_t*>(sk + tq * 256 + ((i ^ tq) << 4));
-        const u32x4_t qq = *reinterpret_cast<const u32x4_t*>(sq + hq * 256 + ((i ^ hq) << 4));
-        sg = dot8_bf16(qq, kk, sg);
-      }
-      s = fmaf(sks[tq * 4 + gr], sg, s);
+    for (int sg = 0; sg < 4; ++sg) {
+      const u32x4_t kf = *reinterpret_cast<const u32x4_t*>(sk + pc * 256 + (((4 * sg + pr) ^ pc) << 4));
+      const f32x4_t part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf), as_bf16x8(st.qb[sg]),
+                                                                   f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s4[i] = fmaf(ksc[i][sg], part[i], s4[i]);
     }
   } else {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const u32x4_t kk = *reinterpret_cast<const u32x4_t*>(sk + tq * 256 + ((i ^ tq) << 4));
-      const u32x4_t qq = *reinterpret_cast<const u32x4_t*>(sq + hq * 256 + ((i ^ hq) << 4));
-      s = dot8_bf16(qq, kk, s);
+    for (int sg = 0; sg < 4; ++sg) {
+      const u32x4_t kf = *reinterpret_cast<const u32x4_t*>(sk + pc * 256 + (((4 * sg + pr) ^ pc) << 4));
+      s4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf), as_bf16x8(st.qb[sg]), s4, 0, 0, 0);
     }
   }
-  const float sl = (tq < valid) ? s * scale_log2 : -INFINITY;
-  const float tmax = row16_max(sl);
-  const bool raise = tmax > st.m_ref + kRescaleSlack;
-  const bool any_raise = __builtin_amdgcn_ballot_w64(raise) != 0;
-  float alpha = 1.f;
-  if (any_raise) {
-    const float m_new = fmaxf(st.m_ref, tmax);
-    alpha = fast_exp2(st.m_ref - m_new);  // 0 on the first page (m_ref = -inf)
+
+  // Online softmax of column pc over the page's 16 tokens (this lane holds
+  // tokens 4 pr .. + 4; the others sit in lanes ^ 16 and ^ 32).
+  float sl[4];
+  float mloc = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    sl[i] = 4 * pr + i < valid ? s4[i] * scale_log2 : -INFINITY;
+    mloc = fmaxf(mloc, sl[i]);
+  }
+  mloc = fmaxf(mloc, other16(mloc));
+  mloc = fmaxf(mloc, other_half(mloc));
+  const bool raise = mloc > st.m_ref + kRescaleSlack;
+  if (__builtin_amdgcn_ballot_w64(raise) != 0) {
+    const float m_new = fmaxf(st.m_ref, mloc);
+    const float alpha = fast_exp2(st.m_ref - m_new);  // 0 on the first page (m_ref = -inf)
     st.m_ref = m_new;
     st.l_lane *= alpha;
+#pragma unroll
+    for (int bb = 0; bb < 8; ++bb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) st.o[bb][i] *= alpha;
   }
-  const float w = fast_exp2(sl - st.m_ref);
-  st.l_lane += w;
-  if ((lane >> 4) < G) {
-    sp[tq * 4 + hq] = w;
-    if (tq == 0) salpha[hq] = alpha;
+  float pw[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    pw[i] = fast_exp2(sl[i] - st.m_ref);  // 0 past the end
+    st.l_lane += pw[i];
   }
-  wave_lds_sync();
 
-  if (any_raise) {
+  // V^T operand of block bb (dims 16 bb .. + 16, tokens 4 pr .. + 4): lane a
+  // = pc points at token 4 pr + a / 4, dims 16 bb + 4 (a % 4) .. + 4, and
+  // receives dim 16 bb + a of the four tokens (ds_read_b64_tr_b16).
+  const int tv = 4 * pr + (pc >> 2);
+  const uint8_t* vrow = sv + tv * 256 + (pc & 1) * 8;
+  s16x4_t vt[8];
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float a = salpha[h];
+  for (int bb = 0; bb < 8; ++bb)
+    vt[bb] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_s16x4_t*)(vrow + (((2 * bb + ((pc & 3) >> 1)) ^ tv) << 4)));
+
+  // P^T operand: this lane's tokens 4 pr .. + 4 of column pc, as bf16; with
+  // grouped V scales one operand per 32-dim group (tokens past the end get
+  // weight 0 by select: their stored scales may be anything).
+  if constexpr (kGrouped) {
+    f32x4_t vsc[4];  // V scales of tokens 4 pr + i, groups 0..3
 #pragma unroll
-      for (int j = 0; j < 8; ++j) st.acc[h][j] *= a;
+    for (int i = 0; i < 4; ++i) vsc[i] = *reinterpret_cast<const f32x4_t*>(svs + (4 * pr + i) * 4);
+#pragma unroll
+    for (int gr = 0; gr < 4; ++gr) {
+      float w[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) w[i] = 4 * pr + i < valid ? pw[i] * vsc[i][gr] : 0.f;
+      const s16x4_t pg = as_s16x4(pack_bf16x2(w[0], w[1]), pack_bf16x2(w[2], w[3]));
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2)
+        st.o[2 * gr + h2] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt[2 * gr + h2], pg, st.o[2 * gr + h2], 0, 0, 0);
     }
-  }
-
-  // V scale of this lane's tokens t_k = 4k + pr (its group pc / 4); zero
-  // past the end, where the stored scale may be anything.
-  float vsc[4];
+  } else {
+    const s16x4_t pg = as_s16x4(pack_bf16x2(pw[0], pw[1]), pack_bf16x2(pw[2], pw[3]));
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    float x = 1.f;
-    // chunk 4 k + pr's group scale sits in lane 4 (4 k + pr) + pc / 4
-    if constexpr (kGrouped) x = half_bits_to_float((uint32_t)__shfl((int)b.vs, 16 * k + 4 * pr + (pc >> 2), 64));
-    if constexpr (F == kFmtFP8) x = v_scale;
-    vsc[k] = (4 * k + pr < valid) ? x : 0.f;
-  }
-
-  // Weights of this lane's tokens, all heads, as bf16 pairs (t0, t1) and
-  // (t2, t3), each times its V scale.
-  uint32_t w01[G], w23[G];
-  {
-    const float4 p0 = *reinterpret_cast<const float4*>(sp + (0 + pr) * 4);
-    const float4 p1 = *reinterpret_cast<const float4*>(sp + (4 + pr) * 4);
-    const float4 p2 = *reinterpret_cast<const float4*>(sp + (8 + pr) * 4);
-    const float4 p3 = *reinterpret_cast<const float4*>(sp + (12 + pr) * 4);
-    const float a0[4] = {p0.x, p0.y, p0.z, p0.w};
-    const float a1[4] = {p1.x, p1.y, p1.z, p1.w};
-    const float a2[4] = {p2.x, p2.y, p2.z, p2.w};
-    const float a3[4] = {p3.x, p3.y, p3.z, p3.w};
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      if constexpr (F == kFmtBF16) {
-        w01[h] = pack_bf16x2(a0[h], a1[h]);
-        w23[h] = pack_bf16x2(a2[h], a3[h]);
-      } else {
-        w01[h] = pack_bf16x2(a0[h] * vsc[0], a1[h] * vsc[1]);
-        w23[h] = pack_bf16x2(a2[h] * vsc[2], a3[h] * vsc[3]);
-      }
-    }
-  }
-
-  // V as bf16; tokens past the end hold anything (NaN included): zero them.
-  u32x4_t vb[4];
-#pragma unroll
-  for (int k = 0; k < 4; ++k) vb[k] = chunk_to_bf16<F>(b.v[k]);
-  if (valid < kBlockSize) {
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-      if (4 * k + pr >= valid) vb[k] = u32x4_t{0u, 0u, 0u, 0u};
-  }
-  // V pairs: dims (2w, 2w+1) of tokens (t0, t1) and (t2, t3).
-#pragma unroll
-  for (int wd = 0; wd < 4; ++wd) {
-    const uint32_t lo01 = __builtin_amdgcn_perm(vb[1][wd], vb[0][wd], 0x05040100u);
-    const uint32_t hi01 = __builtin_amdgcn_perm(vb[1][wd], vb[0][wd], 0x07060302u);
-    const uint32_t lo23 = __builtin_amdgcn_perm(vb[3][wd], vb[2][wd], 0x05040100u);
-    const uint32_t hi23 = __builtin_amdgcn_perm(vb[3][wd], vb[2][wd], 0x07060302u);
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      st.acc[h][2 * wd] = dot2_bf16(w01[h], lo01, st.acc[h][2 * wd]);
-      st.acc[h][2 * wd] = dot2_bf16(w23[h], lo23, st.acc[h][2 * wd]);
-      st.acc[h][2 * wd + 1] = dot2_bf16(w01[h], hi01, st.acc[h][2 * wd + 1]);
-      st.acc[h][2 * wd + 1] = dot2_bf16(w23[h], hi23, st.acc[h][2 * wd + 1]);
-    }
+    for (int bb = 0; bb < 8; ++bb) st.o[bb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt[bb], pg, st.o[bb], 0, 0, 0);
   }
 }
 
@@ -317,10 +312,10 @@ __global__ __launch_bounds__(kDecodeThreads, kDecodeWGsPerCU) void decode_kernel
   static_assert(G == 1 || G == 2 || G == 4, "group size");
   __shared__ __attribute__((aligned(16))) uint8_t s_k[kWaves][kTileBytes];
   __shared__ __attribute__((aligned(16))) uint8_t s_q[G][kHeadDim * 2];
-  __shared__ __attribute__((aligned(16))) float s_p[kWaves][kBlockSize * 4];
-  __shared__ __attribute__((aligned(16))) float s_alpha[kWaves][4];
   __shared__ __attribute__((aligned(16))) float s_ks[kWaves][kBlockSize * 4];  // q8_0 / q4_0 K scales
-  __shared__ __attribute__((aligned(16))) float s_acc[kWaves][4][G][kHeadDim];
+  __shared__ __attribute__((aligned(16))) uint8_t s_v[kWaves][kTileBytes];
+  __shared__ __attribute__((aligned(16))) float s_vs[kWaves][kBlockSize * 4];    // q8_0 / q4_0 V scales
+  __shared__ __attribute__((aligned(16))) float s_acc[kWaves][G][kHeadDim];
   __shared__ float s_m[kWaves][G];
   __shared__ float s_l[kWaves][G];
   __shared__ int s_last;
@@ -418,22 +413,29 @@ __global__ __launch_bounds__(kDecodeThreads, kDecodeWGsPerCU) void decode_kernel
     st.m_ref = -INFINITY;
     st.l_lane = 0.f;
 #pragma unroll
-    for (int h = 0; h < G; ++h)
+    for (int bb = 0; bb < 8; ++bb) st.o[bb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    // Q^T operand from the staged query (head h keeps chunk c at slot c ^ h);
+    // columns past G get a zero query.
+    {
+      const int qn = lane & 15, qr = lane >> 4;
+      const int qh = min(qn, G - 1);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) st.acc[h][j] = 0.f;
+      for (int sg = 0; sg < 4; ++sg) {
+        const u32x4_t x = *reinterpret_cast<const u32x4_t*>(&s_q[qh][((4 * sg + qr) ^ qh) << 4]);
+        st.qb[sg] = qn < G ? x : u32x4_t{0u, 0u, 0u, 0u};
+      }
+    }
 
     uint8_t* sk = s_k[wave];
-    float* sp = s_p[wave];
-    float* sa = s_alpha[wave];
+    uint8_t* sv = s_v[wave];
     float* sks = s_ks[wave];
-    const uint8_t* sq = &s_q[0][0];
+    float* svs = s_vs[wave];
     // This wave's pages are page0 + 4k for k < cnt; page k lives in ring k % 3.
     // The main loop reissues unconditionally, so the (in-order) load counter
     // sees the same pattern on every trip and each wait leaves the other two
     // pages in flight; the last pages are peeled off.
     auto valid_of = [&](int k) { return min(kBlockSize, n - (page0 + kWaves * k) * kBlockSize); };
-#define PA_CONSUME(RING, K) \
-  consume_page<G, F>(st, RING, sq, sk, sks, sp, sa, valid_of(K), p.scale_log2, p.v_scale, lane)
+#define PA_CONSUME(RING, K) consume_page<G, F>(st, RING, sk, sv, sks, svs, valid_of(K), p.scale_log2, lane)
 #define PA_REISSUE(RING, K)                                          \
   {                                                                  \
     issue_page<F>(RING, p, next_id, g, lane);                        \
@@ -464,21 +466,22 @@ __global__ __launch_bounds__(kDecodeThreads, kDecodeWGsPerCU) void decode_kernel
 #undef PA_CONSUME
 #undef PA_REISSUE
 
-    // Per-wave state -> LDS.
-    const int tq = lane & 15;
-    const int hq = (lane >> 4) % G;
+    // Per-wave state -> LDS.  Column pc's sum is spread over lanes pc + 16 j;
+    // its O^T block values are dims 16 b + 4 pr + i.  FP8's V scale applies
+    // here, once.
     const int pr = lane >> 4;
     const int pc = lane & 15;
-    const float l_sum = row16_sum(st.l_lane);
-    if ((lane >> 4) < G && tq == 0) {
-      s_m[wave][hq] = st.m_ref;
-      s_l[wave][hq] = l_sum;
-    }
+    float l_sum = st.l_lane + other16(st.l_lane);
+    l_sum += other_half(l_sum);
+    const float vs = F == kFmtFP8 ? p.v_scale : 1.f;
+    if (pc < G) {
+      if (pr == 0) {
+        s_m[wave][pc] = st.m_ref;
+        s_l[wave][pc] = l_sum;
+      }
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float4* dst = reinterpret_cast<float4*>(&s_acc[wave][pr][h][pc * 8]);
-      dst[0] = make_float4(st.acc[h][0], st.acc[h][1], st.acc[h][2], st.acc[h][3]);
-      dst[1] = make_float4(st.acc[h][4], st.acc[h][5], st.acc[h][6], st.acc[h][7]);
+      for (int bb = 0; bb < 8; ++bb)
+        *reinterpret_cast<f32x4_t*>(&s_acc[wave][pc][16 * bb + 4 * pr]) = st.o[bb] * vs;
     }
     __syncthreads();
 
@@ -493,15 +496,9 @@ __global__ __launch_bounds__(kDecodeThreads, kDecodeWGsPerCU) void decode_kernel
       for (int w = 0; w < kWaves; ++w) {
         const float sc = fast_exp2(s_m[w][h] - M);  // 0 for a wave with no page
         L = fmaf(sc, s_l[w][h], L);
-        float x0 = 0.f, x1 = 0.f;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float2 v = *reinterpret_cast<const float2*>(&s_acc[w][r][h][d]);
-          x0 += v.x;
-          x1 += v.y;
-        }
-        a0 = fmaf(sc, x0, a0);
-        a1 = fmaf(sc, x1, a1);
+        const float2 v = *reinterpret_cast<const float2*>(&s_acc[w][h][d]);
+        a0 = fmaf(sc, v.x, a0);
+        a1 = fmaf(sc, v.y, a1);
       }
       const float inv = 1.f / L;
       my_o0 = a0 * inv;

@@ -60,44 +60,6 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-// fp32 += two bf16 products (v_dot2c_f32_bf16): products of bf16 are exact
-// in fp32, accumulation is fp32.
-__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
-                                         __builtin_bit_cast(bf16x2_t, b), c, false);
-}
-__device__ __forceinline__ float dot8_bf16(const u32x4_t& a, const u32x4_t& b, float c) {
-  c = dot2_bf16(a.x, b.x, c);
-  c = dot2_bf16(a.y, b.y, c);
-  c = dot2_bf16(a.z, b.z, c);
-  c = dot2_bf16(a.w, b.w, c);
-  return c;
-}
-
-// ---------------------------------------------------------------------------
-// Cross-lane reductions inside one 16-lane DPP row.  row_ror:n rotates the
-// row by n lanes, so after rotations by 8, 4, 2, 1 every lane of the row
-// holds the reduction of all 16.
-// ---------------------------------------------------------------------------
-template <int CTRL>
-__device__ __forceinline__ float dpp_f32(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
-}
-__device__ __forceinline__ float row16_max(float x) {
-  x = fmaxf(x, dpp_f32<0x128>(x));
-  x = fmaxf(x, dpp_f32<0x124>(x));
-  x = fmaxf(x, dpp_f32<0x122>(x));
-  x = fmaxf(x, dpp_f32<0x121>(x));
-  return x;
-}
-__device__ __forceinline__ float row16_sum(float x) {
-  x += dpp_f32<0x128>(x);
-  x += dpp_f32<0x124>(x);
-  x += dpp_f32<0x122>(x);
-  x += dpp_f32<0x121>(x);
-  return x;
-}
-
 // Sum over the whole 64-lane wave (result in every lane).
 __device__ __forceinline__ int wave_sum_i32(int x) {
   for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
@@ -180,6 +142,15 @@ __device__ __forceinline__ float other_half(float v) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   const uint32_t lane = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
   return __uint_as_float(lane < 32 ? r[1] : r[0]);
+}
+
+// The value of lane ^ 16 (v_permlane16_swap; its lane layout was checked on
+// the device: rows 0 and 2 find the partner in the second result, rows 1
+// and 3 in the first).
+__device__ __forceinline__ float other16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  const uint32_t lane = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  return __uint_as_float((lane >> 4) & 1 ? r[0] : r[1]);
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

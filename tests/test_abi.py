@@ -145,10 +145,12 @@ def test_auto_partitions_cover_the_chip(lib):
     s = _shape(num_seqs=16, total_q=16, max_blocks_per_seq=144, max_ctx_len=2303, num_blocks=2592)
     ws, parts = pk.plan(s)
     assert parts == 2
-    # compressed pages prefer the four-way split; the workspace covers both
+    # q8_0 / q4_0 pages prefer the four-way split, FP8 the bf16 one; the
+    # workspace covers both
     lib = pk.load()
     assert lib.pa_num_partitions_kv(ctypes.byref(s), pk.KV_BF16) == 2
-    for fmt in (pk.KV_FP8_E4M3, pk.KV_Q8_0, pk.KV_Q4_0):
+    assert lib.pa_num_partitions_kv(ctypes.byref(s), pk.KV_FP8_E4M3) == 2
+    for fmt in (pk.KV_Q8_0, pk.KV_Q4_0):
         assert lib.pa_num_partitions_kv(ctypes.byref(s), fmt) == 4
     assert lib.pa_num_partitions_kv(ctypes.byref(s), 9) == 0
     assert ws == _ws_bytes(16, 8, 4, 16 * 32)
