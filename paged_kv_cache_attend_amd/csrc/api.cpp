@@ -76,44 +76,36 @@ pa_status check_kv_cache(const pa_kv_cache& c) {
 // the CUs and how much fixed cost (start, merge) each partition carries:
 //  - with at most two resident workgroups per CU for the whole grid, pick
 //    the partition count whose grid fills its last round of CUs best, then
-//    (bf16 pages) the one whose partitions are nearest 64 pages -- long
-//    enough to amortise the workgroup's start and merge, short enough to
-//    keep two workgroups per CU streaming -- or (q8_0 / q4_0 pages) more
-//    partitions;
+//    (bf16 and FP8 pages) the fewest partitions -- the least start and merge
+//    per page -- or (q8_0 / q4_0 pages) the most;
 //  - with more (slot, KV head) pairs than that, the grid is several rounds
 //    anyway; long contexts are cut into partitions of at most 128 pages so
 //    that a batch's longest requests do not finish last on their own.
 // No partition is smaller than 8 pages (two per wave).
 int auto_part_pages(const pa_shape* s, int max_pages, bool grouped) {
-  constexpr int kMinPages = 8, kGoodPages = 64, kLongPages = 128;
+  constexpr int kMinPages = 8, kLongPages = 128;
   const long long pairs = (long long)s->num_seqs * s->num_kv_heads;
   const long long resident = (long long)kDecodeWGsPerCU * kNumCUs;
   if (pairs <= 0 || max_pages <= kMinPages) return kMinPages;
   if (pairs > resident) return std::max(kMinPages, ceil_div(max_pages, ceil_div(max_pages, kLongPages)));
   int best_pp = max_pages;
   double best_fill = -1.0;
-  double best_dist = 0.0;
   for (long long parts = 1; parts * pairs <= resident && parts <= max_pages; ++parts) {
     const int pp = ceil_div(max_pages, (int)parts);
     if (pp < kMinPages) break;
     if (ceil_div(max_pages, pp) != parts) continue;  // same grid as a smaller count
     const double rounds = (double)(pairs * parts) / kNumCUs;
     const double fill = rounds / std::ceil(rounds);
-    // Distance of the partition size from 64 pages (a ratio, >= 1).
-    // q8_0 / q4_0 pages carry fewer bytes for more per-page work (codes and
-    // group scales converted in registers), so more, smaller partitions
-    // (more resident waves per CU) win there (measured on the Qwen3-8B-shaped
-    // batch: 2 -> 4 partitions, 10-15 % faster): every size counts as good
-    // and later (more) partitions win ties.  FP8 pages convert in one
-    // instruction per two values and follow the bf16 rule (2 partitions
-    // measured 7 % faster than 4).
-    const double dist = grouped ? 1.0 : std::max((double)pp / kGoodPages, (double)kGoodPages / pp);
-    // Ties in fill (within 1%) go to the size nearer 64 pages, then to more
-    // partitions.
-    const bool better = fill > best_fill + 0.01 || (fill > best_fill - 0.01 && dist <= best_dist * 1.0001);
+    // Ties in fill (within 1 %): bf16 and FP8 pages keep the fewer, longer
+    // partitions (measured on the shared-prefix batch, 10 x 8447 keys: 3
+    // partitions 34.7 us, 6 37.0 us per layer; FP8 on the Qwen3-8B-shaped
+    // batch: 2 partitions 7 % faster than 4); q8_0 / q4_0 pages carry fewer
+    // bytes for more per-page work (codes and group scales converted in
+    // registers), so there more, smaller partitions -- more resident waves
+    // per CU -- win (2 -> 4 partitions, 10-15 % faster).
+    const bool better = fill > best_fill + 0.01 || (grouped && fill > best_fill - 0.01);
     if (better) {
       best_fill = std::max(best_fill, fill);  // (std::: HIP's unqualified max is the int one)
-      best_dist = dist;
       best_pp = pp;
     }
   }

@@ -157,8 +157,8 @@ def test_auto_partitions_cover_the_chip(lib):
 
 
 @pytest.mark.parametrize("num_seqs,ctx,parts", [
-    (10, 8447, 6),    # 80 pairs: 480 workgroups of 88 pages (3 x 176 fills the CUs as well)
-    (10, 2303, 3),    # 80 pairs: 240 workgroups of 48 pages, nearer 64 pages than 6 x 24
+    (10, 8447, 3),    # 80 pairs: 240 workgroups of 176 pages (6 x 88 fills the CUs as well: fewer wins)
+    (10, 2303, 3),    # 80 pairs: 240 workgroups of 48 pages rather than 480 of 24
     (68, 8355, 5),    # 544 pairs, more than resident: long contexts cut to <= 128 pages
     (1, 32768, 32),   # one request: 32 x 64 pages, one workgroup per CU
     (2, 100, 1),      # 7 pages: never below 8 pages per partition
