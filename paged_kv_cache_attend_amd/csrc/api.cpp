@@ -239,15 +239,18 @@ pa_status attend_impl(const pa_shape* shape, const pa_kv_cache& kv, const void* 
 
 // Prefix-grouped decode: the suffix pass is the decode path with keys
 // starting after each slot's prefix (sized for the longest possible suffix,
-// max_ctx_len - min_prefix_len); the prefix pass gets as many partitions per
-// (group, KV head, row tile) as fill one round of CUs, at most 16 (the
-// partials are merged in one batch per row), with at least one 32-key tile
-// each.  Workspace: [suffix split-KV region][slot prefix lengths]
+// max_ctx_len - min_prefix_len).  The prefix pass splits the longest prefix
+// into partitions of at most kPrefixMaxTiles 32-key tiles (a workgroup holds
+// its whole partition in LDS); when that leaves fewer workgroups than CUs it
+// takes more partitions per (group, KV head, row tile), up to
+// kPrefixFillParts (few enough that the suffix pass merges a row's partials
+// in one batch), never less than one 32-key tile each.
+// Workspace: [suffix split-KV region][slot prefix lengths]
 // [prefix partial LSE][prefix partial out].
-#ifndef PA_PREFIX_MAX_PARTS
-#define PA_PREFIX_MAX_PARTS 16
+#ifndef PA_PREFIX_FILL_PARTS
+#define PA_PREFIX_FILL_PARTS 24
 #endif
-constexpr int kPrefixMaxParts = PA_PREFIX_MAX_PARTS;
+constexpr int kPrefixFillParts = PA_PREFIX_FILL_PARTS;
 
 struct PrefixPlan {
   Plan suffix;
@@ -282,7 +285,9 @@ pa_status make_prefix_plan(const pa_shape* s, const pa_prefix_groups* gr, Prefix
   const long long base = (long long)gr->num_groups * s->num_kv_heads * pp.row_tiles;
   if (base > 0 && max_pages > 0) {
     long long parts = (long long)kNumCUs / base;
-    parts = parts < 1 ? 1 : (parts > kPrefixMaxParts ? kPrefixMaxParts : parts);
+    parts = parts < 1 ? 1 : (parts > kPrefixFillParts ? kPrefixFillParts : parts);
+    const long long need = ceil_div(max_pages, 2 * kPrefixMaxTiles);
+    if (parts < need) parts = need;
     if (parts > ceil_div(max_pages, 2)) parts = ceil_div(max_pages, 2);
     pp.pre_pages = ceil_div(max_pages, (int)parts);
     pp.pre_parts = ceil_div(max_pages, pp.pre_pages);

@@ -184,7 +184,7 @@ __device__ __forceinline__ void merge_fold(MergeState& s, float l, float o0, flo
 // at lse_a[i * rows] and its two dims at out_a[i * rows * 128 + 0, 1]
 // (likewise B).  Device-coherent relaxed loads (partials of this launch may
 // come from workgroups on any XCD), in batches whose loads are all issued
-// before any is used: 8 partials for short merges, else 24 (48 loads in
+// before any is used: 8 partials for short merges, else 28 (56 loads in
 // flight, within the 6-bit load counter).
 template <int kBatch>
 __device__ __forceinline__ void merge_batches(MergeState& s, const float* lse_a, const float* out_a, int na,
@@ -217,7 +217,7 @@ __device__ __forceinline__ void merge_partials(MergeState& s, const float* lse_a
   if (n <= 8)
     merge_batches<8>(s, lse_a, out_a, na, lse_b, out_b, n, rows);
   else
-    merge_batches<24>(s, lse_a, out_a, na, lse_b, out_b, n, rows);
+    merge_batches<28>(s, lse_a, out_a, na, lse_b, out_b, n, rows);
 }
 
 }  // namespace pa

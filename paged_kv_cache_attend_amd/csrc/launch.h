@@ -139,7 +139,9 @@ struct WriteParams {
   int32_t total_q;            // rows of k_new / v_new
 };
 
-// Shared-prefix pass of prefix-grouped decode.
+// Shared-prefix pass of prefix-grouped decode.  A partition is at most
+// kPrefixMaxTiles 32-key tiles (all held in LDS at once).
+constexpr int kPrefixMaxTiles = 8;
 struct PrefixParams {
   const uint16_t* q;
   const uint16_t* k;
@@ -161,7 +163,7 @@ struct PrefixParams {
   int32_t num_groups;
   int32_t row_tiles;           // 64-row tiles of (member, query head) rows per group
   int32_t pre_parts;           // partitions of the prefix
-  int32_t part_pages;          // pages per prefix partition
+  int32_t part_pages;          // pages per prefix partition (<= 2 kPrefixMaxTiles)
   int32_t max_members;         // rows of a group's first max_members slots only
 };
 

@@ -12,16 +12,19 @@
 //
 // Grid: one workgroup per (group, KV head, 64-row tile, prefix partition),
 // plus one set-up workgroup that writes every slot's prefix length for the
-// suffix pass.  Eight waves: wave w takes rows 32 (w % 2) .. +32 of the tile
-// and a quarter (w / 2) of the partition's 32-key tiles; the quarters merge
-// through LDS at the end.  Per tile: the quarter's 128 threads load K and V
-// through the group leader's block-table row two tiles ahead into registers,
-// store K row-major (swizzled) and V transposed (68-byte rows) to a
-// double-buffered LDS area; S^T = K Q^T and O^T += V^T P^T run on
-// v_mfma_f32_32x32x16_bf16 with the softmax mostly in-lane.  Keys past the
-// partition, the prefix or a member's own length get -inf scores.  Output:
-// the normalised fp32 partial and natural-log LSE of every live row, or
-// LSE = -inf when the partition has no visible key.
+// suffix pass.  A partition is at most eight 32-key tiles, and a workgroup
+// requests all of its tiles at once, straight from memory into LDS
+// (global_load_lds_dwordx4: K and V row-major with XOR-swizzled 16-byte
+// chunks, 128 KiB), so the pass costs one memory round trip rather than one
+// per tile.  Eight waves: wave w takes rows 32 (w % 2) .. +32 of the tile
+// and the tiles w / 2, w / 2 + 4 of the partition; the quarters merge
+// through LDS at the end.  S^T = K Q^T and O^T += V^T P^T run on
+// v_mfma_f32_32x32x16_bf16 with the softmax mostly in-lane; the V^T operand
+// comes from the row-major V tile through transposing LDS reads
+// (ds_read_b64_tr_b16).  Keys past the partition, the prefix or a member's
+// own length get -inf scores.  Output: the normalised fp32 partial and
+// natural-log LSE of every live row, or LSE = -inf when the partition has no
+// visible key.
 
 #include "device.h"
 
@@ -30,24 +33,20 @@ namespace pa {
 namespace {
 
 constexpr int kThreads = 512;
-constexpr int kQuarterThreads = 128;
 constexpr int kTileKeys = 32;
-constexpr int kKRowBytes = kHeadDim * 2;          // 256
-constexpr int kVtRowBytes = kTileKeys * 2 + 4;    // 68: padded dim-major row (17 words)
-constexpr int kKBytes = kTileKeys * kKRowBytes;   // 8 KiB
-constexpr int kVtBytes = kHeadDim * kVtRowBytes;  // 8.5 KiB
-constexpr int kStageBytes = kKBytes + kVtBytes;
+constexpr int kRowBytes = kHeadDim * 2;           // 256: one key row of K or V
+constexpr int kTileBytes = kTileKeys * kRowBytes; // 8 KiB (K or V)
 constexpr float kRescaleSlack = 8.0f;             // log2 units
+static_assert(kPrefixMaxTiles == 8, "two tiles per key quarter");
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(const u32x4_t& u) { return __builtin_bit_cast(bf16x8_t, u); }
 
-// A loader thread holds chunk `lc` (dims 8 lc .. +8) of keys 4 lq .. 4 lq + 3
-// of the tile, for K and for V: each load instruction of a wave reads whole
-// 256-byte key rows.
-struct TileRegs {
-  u32x4_t k[4];
-  u32x4_t v[4];
-};
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+
+// Byte offset of dims d .. of key row `key` in a swizzled K or V tile: the
+// 16-byte chunk index is XORed with the key's low four bits.
+__device__ __forceinline__ int swz(int key, int d) { return key * kRowBytes + ((((d >> 3) ^ key) & 15) << 4) + (d & 7) * 2; }
 
 // Set-up workgroup: slot_plen[r] = the prefix length of r's group in whole
 // pages, for a group's first max_members slots (the rows this kernel
@@ -68,14 +67,14 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_kernel(PrefixParams p) {
     write_slot_prefix(p);
     return;
   }
-  __shared__ __attribute__((aligned(16))) uint8_t s_buf[4][2][kStageBytes];
+  // [tile][K | V], filled straight from memory; reused for the final merge.
+  __shared__ __attribute__((aligned(16))) uint8_t s_buf[kPrefixMaxTiles][2][kTileBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int rg = wave & 1;    // row group
   const int kq = wave >> 1;   // key quarter
-  const int lt = tid & (kQuarterThreads - 1);
   const int col = lane & 31;
   const int hh = lane >> 5;
 
@@ -98,71 +97,35 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_kernel(PrefixParams p) {
   // Keys of this partition: pages [part * part_pages, ...) of the prefix.
   const int key0 = part * p.part_pages * kBlockSize;
   const int kv_end = part == p.pre_parts - 1 ? plen : min(plen, (part + 1) * p.part_pages * kBlockSize);
-  const int ntiles = kv_end > key0 ? (kv_end - key0 + kTileKeys - 1) / kTileKeys : 0;
-  const int T = (ntiles + 3) / 4;          // tiles per quarter (all loop T times)
-  const int tile0 = kq * T;
+  const int ntiles = kv_end > key0 ? (kv_end - key0 + kTileKeys - 1) / kTileKeys : 0;  // <= 8
   const int32_t* bt = uniform_ptr(p.block_table + (size_t)s0 * p.max_blocks);
   const int last_page = max(0, (kv_end - 1) >> 4);
 
-  const int lq = lt >> 4;   // keys 4 lq .. 4 lq + 3 of the tile (all in one page)
-  const int lc = lt & 15;   // 16-byte chunk
-
-  auto tile_key = [&](int it) { return key0 + (tile0 + it) * kTileKeys; };
-  // Tiles past the quarter's share or the partition are not loaded; their
-  // registers are never stored (store_tile zeroes keys past kv_end).
-  auto load_tile = [&](TileRegs& t, int it) {
-    if (it >= T || tile0 + it >= ntiles) return;
-    const int page = tile_key(it) >> 4;
-    const int32_t id0 = scalar_load_i32(bt, min(page, last_page));
-    const int32_t id1 = scalar_load_i32(bt, min(page + 1, last_page));
-    const int32_t idp = (lq >> 2) ? id1 : id0;
-    const int slot0 = (4 * lq) & 15;
-    const u32x4_t* ks = reinterpret_cast<const u32x4_t*>(p.k + cache_offset(idp, g, slot0, lc * 8, p.num_kv_heads));
-    const u32x4_t* vs = reinterpret_cast<const u32x4_t*>(p.v + cache_offset(idp, g, slot0, lc * 8, p.num_kv_heads));
+  // Every tile of the partition goes out at once, before anything that
+  // depends on the rows: wave w loads tile w (when it exists), its K and V
+  // rows in eight instructions each (lane l fills LDS chunk slot l % 16 of
+  // row l / 16 of the instruction's four rows, with the global chunk that
+  // the swizzle puts there).  Keys past the partition re-read its last key
+  // (finite), whose scores are masked and whose weights are 0.
+  if (wave < ntiles) {
+    const int t = wave;
+    const int32_t id0 = scalar_load_i32(bt, min((key0 >> 4) + 2 * t, last_page));
+    const int32_t id1 = scalar_load_i32(bt, min((key0 >> 4) + 2 * t + 1, last_page));
+    uint8_t* sk = s_buf[t][0];
+    uint8_t* sv = s_buf[t][1];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) t.k[e] = stream_load(ks + e * (kHeadDim / 8));
-#pragma unroll
-    for (int e = 0; e < 4; ++e) t.v[e] = stream_load(vs + e * (kHeadDim / 8));
-  };
-  auto store_tile = [&](const TileRegs& t, int stage, int it) {
-    uint8_t* sk = s_buf[kq][stage];
-    uint8_t* svt = sk + kKBytes;
-    const int base = tile_key(it) + 4 * lq;
-    const bool tile_ok = it < T;
-    const u32x4_t zero = u32x4_t{0u, 0u, 0u, 0u};
-    u32x4_t kz[4], vz[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const bool ok = tile_ok && base + e < kv_end;
-      kz[e] = ok ? t.k[e] : zero;
-      vz[e] = ok ? t.v[e] : zero;
-      const int key = 4 * lq + e;
-      *reinterpret_cast<u32x4_t*>(sk + key * kKRowBytes + ((lc ^ (key & 15)) << 4)) = kz[e];
+    for (int j = 0; j < 8; ++j) {
+      const int row = 4 * j + (lane >> 4);           // LDS row of this lane
+      const int key = min(key0 + t * kTileKeys + row, kv_end - 1);
+      const int32_t id = (key >> 4) == (key0 >> 4) + 2 * t ? id0 : id1;
+      const int c = (lane & 15) ^ (row & 15);        // global chunk for this slot
+      const size_t off = cache_offset(id, g, key & 15, c * 8, p.num_kv_heads);
+      __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(p.k + off),
+                                       (void __attribute__((address_space(3)))*)(sk + 4 * j * kRowBytes), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(p.v + off),
+                                       (void __attribute__((address_space(3)))*)(sv + 4 * j * kRowBytes), 16, 0, 0);
     }
-    // V^T: dim d's row holds the tile's keys in order; this thread writes the
-    // two words of keys 4 lq .. 4 lq + 3 for each of its 8 dims.
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const uint32_t lo01 = __builtin_amdgcn_perm(vz[1][w], vz[0][w], 0x05040100u);
-      const uint32_t hi01 = __builtin_amdgcn_perm(vz[1][w], vz[0][w], 0x07060302u);
-      const uint32_t lo23 = __builtin_amdgcn_perm(vz[3][w], vz[2][w], 0x05040100u);
-      const uint32_t hi23 = __builtin_amdgcn_perm(vz[3][w], vz[2][w], 0x07060302u);
-      const int d = lc * 8 + 2 * w;
-      uint32_t* r0 = reinterpret_cast<uint32_t*>(svt + d * kVtRowBytes + lq * 8);
-      uint32_t* r1 = reinterpret_cast<uint32_t*>(svt + (d + 1) * kVtRowBytes + lq * 8);
-      r0[0] = lo01;
-      r0[1] = lo23;
-      r1[0] = hi01;
-      r1[1] = hi23;
-    }
-  };
-
-  // The first two tiles go out before anything that depends on the rows.
-  TileRegs ra, rb;
-  load_tile(ra, 0);
-  issue_order_barrier();
-  load_tile(rb, 1);
-  issue_order_barrier();
+  }
 
   // This lane's row: member j, query head hq (of KV head g).  The tile's
   // members start at jf; one load per lane gives their query lengths, a
@@ -206,19 +169,24 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_kernel(PrefixParams p) {
   float m_run = -INFINITY;
   float l_run = 0.f;
 
-  auto compute_tile = [&](int it, int stage) {
-    const uint8_t* sk = s_buf[kq][stage];
-    const uint8_t* svt = sk + kKBytes;
+  // Tile t of the partition (keys key0 + 32 t ..): S^T = K Q^T, online
+  // softmax, O^T += V^T P^T.
+  auto compute_tile = [&](int t) {
+    const uint8_t* sk = s_buf[t][0];
+    const uint8_t* svv = s_buf[t][1];
+    u32x4_t kf[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const int c = hh * 8 + s;
+      kf[s] = *reinterpret_cast<const u32x4_t*>(sk + col * kRowBytes + ((c ^ (col & 15)) << 4));
+    }
     f32x16_t st;
 #pragma unroll
     for (int i = 0; i < 16; ++i) st[i] = 0.f;
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const int c = hh * 8 + s;
-      const u32x4_t kf = *reinterpret_cast<const u32x4_t*>(sk + col * kKRowBytes + ((c ^ (col & 15)) << 4));
-      st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf), as_bf16x8(qf[s]), st, 0, 0, 0);
-    }
-    const int kbase = tile_key(it) + 4 * hh;
+    for (int s = 0; s < 8; ++s)
+      st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf[s]), as_bf16x8(qf[s]), st, 0, 0, 0);
+    const int kbase = key0 + t * kTileKeys + 4 * hh;
     float sv[16];
     float mloc = -INFINITY;
 #pragma unroll
@@ -226,11 +194,11 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_kernel(PrefixParams p) {
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
         const int key = kbase + 8 * a + b;
-        const float x = (it < T && key < kv_end && key <= my_limit) ? st[4 * a + b] * p.scale_log2 : -INFINITY;
+        const float x = (key < kv_end && key <= my_limit) ? st[4 * a + b] * p.scale_log2 : -INFINITY;
         sv[4 * a + b] = x;
         mloc = fmaxf(mloc, x);
       }
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+    mloc = fmaxf(mloc, other_half(mloc));
     const bool raise = mloc > m_run + kRescaleSlack;
     if (__builtin_amdgcn_ballot_w64(raise) != 0) {
       const float m_new = fmaxf(m_run, mloc);
@@ -250,6 +218,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_kernel(PrefixParams p) {
       lsum += sv[i];
     }
     l_run += lsum;
+    // P^T operand for key steps 0 and 1: keys 16 ks + 4 hh + 0..3 and
+    // 16 ks + 8 + 4 hh + 0..3.
     u32x4_t pf[2];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
@@ -258,48 +228,36 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_kernel(PrefixParams p) {
       pf[ks][2] = pack_bf16x2(sv[8 * ks + 4], sv[8 * ks + 5]);
       pf[ks][3] = pack_bf16x2(sv[8 * ks + 6], sv[8 * ks + 7]);
     }
+    // V^T operand (lane: dim 32 mb + l % 32, the same keys) from the
+    // row-major V tile through transposing reads: in each 16-lane group, lane
+    // a points at 4 dims of key a / 4 and lane i receives dim i of the four
+    // keys.  Key + 16 is 4096 bytes further with the same swizzle.
+    const int grp16 = lane >> 4;
+    const int a16 = lane & 15;
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-      const int d = mb * 32 + col;
+    for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        // keys 16 ks + 4 hh + 0..3 and 16 ks + 8 + 4 hh + 0..3 (4-byte reads:
-        // the 68-byte rows keep only 4-byte alignment)
-        const uint32_t* vrow = reinterpret_cast<const uint32_t*>(svt + d * kVtRowBytes + (16 * ks + 4 * hh) * 2);
-        const u32x4_t vf = u32x4_t{vrow[0], vrow[1], vrow[4], vrow[5]};
+        s16x4_t v2[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e)
+          v2[e] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(
+              svv + ks * 4096 + swz(8 * e + 4 * hh + (a16 >> 2), mb * 32 + (grp16 & 1) * 16 + 4 * (a16 & 3))));
+        const u32x2_t l2 = __builtin_bit_cast(u32x2_t, v2[0]);
+        const u32x2_t h2 = __builtin_bit_cast(u32x2_t, v2[1]);
+        const u32x4_t vf = u32x4_t{l2[0], l2[1], h2[0], h2[1]};
         o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vf), as_bf16x8(pf[ks]), o[mb], 0, 0, 0);
       }
-    }
   };
 
-  // Pipeline: tiles it+1, it+2 in registers while
-  // tile it is computed from LDS; double-buffered LDS, one barrier per tile.
-  if (T > 0) {
-    store_tile(ra, 0, 0);
-    issue_order_barrier();
-    load_tile(ra, 2);
-    issue_order_barrier();
-    __syncthreads();
-  }
-  int it = 0;
-  for (; it + 1 < T; it += 2) {
-    store_tile(rb, 1, it + 1);
-    issue_order_barrier();
-    load_tile(rb, it + 3);
-    issue_order_barrier();
-    compute_tile(it, 0);
-    __syncthreads();
-    store_tile(ra, 0, it + 2);
-    issue_order_barrier();
-    load_tile(ra, it + 4);
-    issue_order_barrier();
-    compute_tile(it + 1, 1);
-    __syncthreads();
-  }
-  if (it < T) {
-    compute_tile(it, 0);
-    __syncthreads();
-  }
+  // Every wave's tile loads (and the query) land, then one barrier puts the
+  // whole partition in LDS for every wave.
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), other counters unconstrained
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kPrefixMaxTiles / 4; ++i)
+    if (kq + 4 * i < ntiles) compute_tile(kq + 4 * i);
+  __syncthreads();  // all tiles read before the area is reused
 
   // Merge the quarters into quarter 0 through LDS (the tile area, free
   // now), one accumulator block per round, each round in its own region so

@@ -210,14 +210,21 @@ def test_lse_optional():
 
 
 def test_long_contexts_many_partitions():
-    # 2 slots x 65536 keys on 8 KV heads: 32 partitions of 128 pages, so the
-    # merge folds its partials in two batches (24 + 8); plus a batch of 600
-    # short slots (4800 (slot, KV head) pairs, several rounds of workgroups).
+    # 2 slots x 65536 keys on 8 KV heads: the automatic plan, then 64
+    # partitions of 64 pages, so the merge folds its partials in three
+    # batches (28 + 28 + 8); plus a batch of 600 short slots (4800 (slot, KV
+    # head) pairs, several rounds of workgroups).
     p = _case([65536, 61000], hq=32, hkv=8, seed=91)
     shape = pk.make_shape(p.num_seqs, p.total_q, 32, 8, p.max_blocks_per_seq, 1, p.max_ctx_len, p.num_blocks)
-    assert pk.plan(shape)[1] == 32
-    say("decode 2 x 65536 keys")
-    compare(p, run_gpu(p), run_oracle(p), label="long contexts")
+    assert pk.plan(shape)[1] >= 16
+    shape64 = pk.make_shape(p.num_seqs, p.total_q, 32, 8, p.max_blocks_per_seq, 1, p.max_ctx_len, p.num_blocks,
+                            partition_size=1024)
+    assert pk.plan(shape64)[1] == 64
+    ref = run_oracle(p)
+    say("decode 2 x 65536 keys, automatic partitions")
+    compare(p, run_gpu(p), ref, label="long contexts")
+    say("decode 2 x 65536 keys, 64 partitions")
+    compare(p, run_gpu(p, partition_size=1024), ref, label="long contexts, 64 partitions")
     rng = np.random.default_rng(92)
     q = _case([int(x) for x in rng.integers(1, 300, 600)], hq=32, hkv=8, seed=93)
     say("decode 600 short slots")
