@@ -17,9 +17,10 @@
 // (global_load_lds_dwordx4: K and V row-major with XOR-swizzled 16-byte
 // chunks, 128 KiB), so the pass costs one memory round trip rather than one
 // per tile.  Eight waves: wave w takes rows 32 (w % 2) .. +32 of the tile
-// and the tiles w / 2, w / 2 + 4 of the partition; the quarters merge
-// through LDS at the end.  S^T = K Q^T and O^T += V^T P^T run on
-// v_mfma_f32_32x32x16_bf16 with the softmax mostly in-lane; the V^T operand
+// and the tiles w / 2, w / 2 + 4 of the partition; at the end the quarters
+// merge through LDS, each wave folding and storing one 32-dim block.
+// S^T = K Q^T and O^T += V^T P^T run on v_mfma_f32_32x32x16_bf16 with the
+// softmax mostly in-lane; the V^T operand
 // comes from the row-major V tile through transposing LDS reads
 // (ds_read_b64_tr_b16).  Keys past the partition, the prefix or a member's
 // own length get -inf scores.  Output: the normalised fp32 partial and
@@ -87,6 +88,16 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_kernel(PrefixParams p) {
   const int grp = rest / p.num_kv_heads;
   const int G = p.num_q_heads / p.num_kv_heads;
 
+  // The group's table row is needed before any key can be requested.  The
+  // row is guessed (groups of max_members consecutive slots) and its two
+  // page ids for this wave's tile are requested together with the group's
+  // bounds, saving a memory round trip when the guess holds.
+  const int key0 = part * p.part_pages * kBlockSize;
+  const int page0 = (key0 >> 4) + 2 * wave;  // first page of tile `wave`
+  const int s_guess = min(grp * p.max_members, p.num_seqs - 1);
+  const int32_t* bt_guess = uniform_ptr(p.block_table + (size_t)s_guess * p.max_blocks);
+  int32_t id0 = scalar_load_i32(bt_guess, min(page0, p.max_blocks - 1));
+  int32_t id1 = scalar_load_i32(bt_guess, min(page0 + 1, p.max_blocks - 1));
   const int s0 = scalar_load_i32(p.group_start, grp);
   const int s1 = scalar_load_i32(p.group_start, grp + 1);
   const int plen = scalar_load_i32(p.prefix_len, grp) & ~15;  // whole pages, as the decode pass reads it
@@ -95,7 +106,6 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_kernel(PrefixParams p) {
   if (rows_here <= 0 || plen <= 0) return;
 
   // Keys of this partition: pages [part * part_pages, ...) of the prefix.
-  const int key0 = part * p.part_pages * kBlockSize;
   const int kv_end = part == p.pre_parts - 1 ? plen : min(plen, (part + 1) * p.part_pages * kBlockSize);
   const int ntiles = kv_end > key0 ? (kv_end - key0 + kTileKeys - 1) / kTileKeys : 0;  // <= 8
   const int32_t* bt = uniform_ptr(p.block_table + (size_t)s0 * p.max_blocks);
@@ -109,8 +119,13 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_kernel(PrefixParams p) {
   // (finite), whose scores are masked and whose weights are 0.
   if (wave < ntiles) {
     const int t = wave;
-    const int32_t id0 = scalar_load_i32(bt, min((key0 >> 4) + 2 * t, last_page));
-    const int32_t id1 = scalar_load_i32(bt, min((key0 >> 4) + 2 * t + 1, last_page));
+    if (s0 != s_guess) {
+      id0 = scalar_load_i32(bt, page0);
+      id1 = scalar_load_i32(bt, min(page0 + 1, last_page));
+    }
+    // A tile exists only while its first page is in the partition; past the
+    // prefix the second page is the first again.
+    if (page0 + 1 > last_page) id1 = id0;
     uint8_t* sk = s_buf[t][0];
     uint8_t* sv = s_buf[t][1];
 #pragma unroll
@@ -259,84 +274,69 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_kernel(PrefixParams p) {
     if (kq + 4 * i < ntiles) compute_tile(kq + 4 * i);
   __syncthreads();  // all tiles read before the area is reused
 
-  // Merge the quarters into quarter 0 through LDS (the tile area, free
-  // now), one accumulator block per round, each round in its own region so
-  // one barrier per round suffices: quarters 1-3 write, quarter 0 folds.
-  // Region layout [sender][chunk of 4 floats][lane]: 16-byte accesses by
-  // consecutive lanes.
-  constexpr int kRound = 6 * 4 * 64;  // float4s per round
+  // Merge the four key quarters of each row group through LDS (the tile
+  // area, free now) behind one barrier: wave (rg, kq) folds output block
+  // kq (dims 32 kq .. +32) of its rows from the other three quarters and
+  // stores it, so the folding and the stores are spread over all eight
+  // waves.  Region layout [block][row group][other quarter][chunk of 4
+  // floats][lane]: 16-byte accesses by consecutive lanes.
+  constexpr int kSlot = 4 * 64;  // float4s per (block, row group, quarter)
   float4* xacc = reinterpret_cast<float4*>(&s_buf[0][0][0]);
-  float2* xml = reinterpret_cast<float2*>(xacc + 4 * kRound);  // [sender][lane]: (m, l)
-  static_assert((4 * kRound * sizeof(float4) + 6 * 64 * sizeof(float2)) <= sizeof(s_buf),
+  float2* xml = reinterpret_cast<float2*>(xacc + 4 * 2 * 3 * kSlot);  // [row group][quarter][lane]: (m, l)
+  static_assert(4 * 2 * 3 * kSlot * sizeof(float4) + 2 * 4 * 64 * sizeof(float2) <= sizeof(s_buf),
                 "merge buffer exceeds the tile area");
-  const int sender = (kq - 1) * 2 + rg;
-  float a0 = 0.f, aq[3] = {0.f, 0.f, 0.f};
+  xml[(rg * 4 + kq) * 64 + lane] = make_float2(m_run, l_run);
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb) {
-    float4* rbuf = xacc + mb * kRound;
-    if (kq != 0) {
-      if (mb == 0) xml[sender * 64 + lane] = make_float2(m_run, l_run);
+    if (mb == kq) continue;
+    float4* dst = xacc + ((mb * 2 + rg) * 3 + (kq < mb ? kq : kq - 1)) * kSlot;
 #pragma unroll
-      for (int c = 0; c < 4; ++c)
-        rbuf[(sender * 4 + c) * 64 + lane] =
-            make_float4(o[mb][4 * c], o[mb][4 * c + 1], o[mb][4 * c + 2], o[mb][4 * c + 3]);
-    }
-    __syncthreads();
-    if (kq == 0) {
-      if (mb == 0) {
-        float2 ml[3];
-        float M = m_run;
-#pragma unroll
-        for (int q = 0; q < 3; ++q) {
-          ml[q] = xml[(q * 2 + rg) * 64 + lane];
-          M = fmaxf(M, ml[q].x);
-        }
-        const float Mu = (M == -INFINITY) ? 0.f : M;
-        a0 = fast_exp2(m_run - Mu);
-        float l = l_run * a0;
-#pragma unroll
-        for (int q = 0; q < 3; ++q) {
-          aq[q] = fast_exp2(ml[q].x - Mu);
-          l = fmaf(ml[q].y, aq[q], l);
-        }
-        l_run = l;
-        m_run = M;
-      }
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        float x0 = o[mb][4 * c] * a0, x1 = o[mb][4 * c + 1] * a0;
-        float x2 = o[mb][4 * c + 2] * a0, x3 = o[mb][4 * c + 3] * a0;
-#pragma unroll
-        for (int q = 0; q < 3; ++q) {
-          const float4 y = rbuf[((q * 2 + rg) * 4 + c) * 64 + lane];
-          x0 = fmaf(y.x, aq[q], x0);
-          x1 = fmaf(y.y, aq[q], x1);
-          x2 = fmaf(y.z, aq[q], x2);
-          x3 = fmaf(y.w, aq[q], x3);
-        }
-        o[mb][4 * c] = x0;
-        o[mb][4 * c + 1] = x1;
-        o[mb][4 * c + 2] = x2;
-        o[mb][4 * c + 3] = x3;
-      }
-    }
+    for (int c = 0; c < 4; ++c)
+      dst[c * 64 + lane] = make_float4(o[mb][4 * c], o[mb][4 * c + 1], o[mb][4 * c + 2], o[mb][4 * c + 3]);
   }
-  if (kq != 0 || !row_live) return;
+  __syncthreads();
+  if (!row_live) return;  // both lanes of a row leave together
 
+  float M = -INFINITY;
+  float2 ml[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    ml[q] = xml[(rg * 4 + q) * 64 + lane];
+    M = fmaxf(M, ml[q].x);
+  }
+  const float Mu = (M == -INFINITY) ? 0.f : M;
+  float aw[4];
+  float l = 0.f;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    aw[q] = fast_exp2(ml[q].x - Mu);
+    l = fmaf(ml[q].y, aw[q], l);
+  }
+  const float l_tot = l + __shfl_xor(l, 32, 64);
   const size_t rows = (size_t)p.total_q * p.num_q_heads;
-  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-  if (hh == 0) p.pre_lse[(size_t)part * rows + grow] = l_tot > 0.f ? (m_run + fast_log2(l_tot)) * kLn2 : -INFINITY;
+  if (kq == 0 && hh == 0) p.pre_lse[(size_t)part * rows + grow] = l_tot > 0.f ? (M + fast_log2(l_tot)) * kLn2 : -INFINITY;
   if (l_tot == 0.f) return;  // no visible key in this partition: the output is never read
   const float inv = 1.f / l_tot;
   float* orow = p.pre_out + ((size_t)part * rows + grow) * kHeadDim;
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb)
+  for (int mb = 0; mb < 4; ++mb) {
+    if (mb != kq) continue;
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      const int d = mb * 32 + 8 * a + 4 * hh;
-      *reinterpret_cast<float4*>(orow + d) =
-          make_float4(o[mb][4 * a] * inv, o[mb][4 * a + 1] * inv, o[mb][4 * a + 2] * inv, o[mb][4 * a + 3] * inv);
+    for (int c = 0; c < 4; ++c) {
+      float x0 = o[mb][4 * c] * aw[mb], x1 = o[mb][4 * c + 1] * aw[mb];
+      float x2 = o[mb][4 * c + 2] * aw[mb], x3 = o[mb][4 * c + 3] * aw[mb];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (q == mb) continue;
+        const float4 y = xacc[((mb * 2 + rg) * 3 + (q < mb ? q : q - 1)) * kSlot + c * 64 + lane];
+        x0 = fmaf(y.x, aw[q], x0);
+        x1 = fmaf(y.y, aw[q], x1);
+        x2 = fmaf(y.z, aw[q], x2);
+        x3 = fmaf(y.w, aw[q], x3);
+      }
+      *reinterpret_cast<float4*>(orow + mb * 32 + 8 * c + 4 * hh) = make_float4(x0 * inv, x1 * inv, x2 * inv, x3 * inv);
     }
+  }
 }
 
 }  // namespace
