@@ -50,6 +50,12 @@ CASES = [
     ("mha", dict(groups=[(80, [80, 90, 200])], singles=[33], hq=4, hkv=4)),
     ("gqa2", dict(groups=[(16, [17, 100]), (160, [160, 170, 400])], singles=[], hq=8, hkv=4)),
     ("long_prefix", dict(groups=[(2048, [2048, 2100, 2600])], singles=[700], hq=32, hkv=8)),
+    # 60 prefix pages over 20 partitions of 3 pages: a partition's second
+    # tile reaches into the next partition's first page (masked).
+    ("odd_partition_pages", dict(groups=[(960, [960 + 5 * i for i in range(6)])], singles=[200], hq=32, hkv=8)),
+    # 512 prefix pages need 32 partitions of 16 (eight tiles each): the
+    # suffix merge folds its own partials and the prefix's in two batches.
+    ("very_long_prefix", dict(groups=[(8192, [8192, 8200, 8500])], singles=[], hq=32, hkv=8)),
 ]
 
 
