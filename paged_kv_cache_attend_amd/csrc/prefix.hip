@@ -94,7 +94,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_kernel(PrefixParams p) {
   // bounds, saving a memory round trip when the guess holds.
   const int key0 = part * p.part_pages * kBlockSize;
   const int page0 = (key0 >> 4) + 2 * wave;  // first page of tile `wave`
-  const int s_guess = min(grp * p.max_members, p.num_seqs - 1);
+  const int s_guess = (int)min((long long)grp * p.max_members, (long long)p.num_seqs - 1);
   const int32_t* bt_guess = uniform_ptr(p.block_table + (size_t)s_guess * p.max_blocks);
   int32_t id0 = scalar_load_i32(bt_guess, min(page0, p.max_blocks - 1));
   int32_t id1 = scalar_load_i32(bt_guess, min(page0 + 1, p.max_blocks - 1));
