@@ -340,54 +340,52 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkParams p) {
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   __syncthreads();
 
-  // Merge the key halves: half 1 hands (m, l, o) to half 0 through LDS, in
-  // four rounds of 16 accumulators (16 KiB per round, inside the tile area).
-  float* xbuf = reinterpret_cast<float*>(&s_buf[0][0][0]);  // [rg][18][64] floats
+  // Merge the key halves through LDS (the tile area) behind one barrier:
+  // wave (rg, kh) keeps output blocks 2 kh, 2 kh + 1 (dims 64 kh .. +64) of
+  // its rows, hands the other two to its partner (rg, 1 - kh), folds the two
+  // it receives and stores its 64 dims, so both halves share the folding
+  // and the stores.  Layout [row group][sender half][block][chunk of 4
+  // floats][lane]: 16-byte accesses by consecutive lanes.
+  float4* xacc = reinterpret_cast<float4*>(&s_buf[0][0][0][0]);
+  float2* xml = reinterpret_cast<float2*>(xacc + 4 * 2 * 2 * 4 * 64);  // [row group][half][lane]: (m, l)
+  static_assert(4 * 2 * 2 * 4 * 64 * sizeof(float4) + 4 * 2 * 64 * sizeof(float2) <= sizeof(s_buf),
+                "merge buffer exceeds the tile area");
+  xml[(rg * 2 + kh) * 64 + lane] = make_float2(m_run, l_run);
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb) {
-    if (kh == 1) {
-      float* dst = xbuf + (size_t)rg * 18 * 64;
+    if ((mb >> 1) == kh) continue;
+    float4* dst = xacc + ((rg * 2 + kh) * 2 + (mb & 1)) * 4 * 64;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) dst[i * 64 + lane] = o[mb][i];
-      if (mb == 0) {
-        dst[16 * 64 + lane] = m_run;
-        dst[17 * 64 + lane] = l_run;
-      }
-    }
-    __syncthreads();
-    if (kh == 0) {
-      const float* src = xbuf + (size_t)rg * 18 * 64;
-      const float m1 = src[16 * 64 + lane];
-      const float l1 = src[17 * 64 + lane];
-      const float M = fmaxf(m_run, m1);
-      const float Mu = (M == -INFINITY) ? 0.f : M;
-      const float s0 = fast_exp2(m_run - Mu);
-      const float s1 = fast_exp2(m1 - Mu);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) o[mb][i] = o[mb][i] * s0 + src[i * 64 + lane] * s1;
-      if (mb == 3) {
-        l_run = l_run * s0 + l1 * s1;
-        m_run = M;
-      }
-    }
-    __syncthreads();
+    for (int c = 0; c < 4; ++c)
+      dst[c * 64 + lane] = make_float4(o[mb][4 * c], o[mb][4 * c + 1], o[mb][4 * c + 2], o[mb][4 * c + 3]);
   }
-  if (kh == 1 || !row_live) return;
+  __syncthreads();
+  if (!row_live) return;  // both lanes of a row leave together
 
-  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  const float2 ml = xml[(rg * 2 + (1 - kh)) * 64 + lane];
+  const float M = fmaxf(m_run, ml.x);
+  const float Mu = (M == -INFINITY) ? 0.f : M;
+  const float s0 = fast_exp2(m_run - Mu);
+  const float s1 = fast_exp2(ml.x - Mu);
+  const float l = l_run * s0 + ml.y * s1;
+  const float l_tot = l + __shfl_xor(l, 32, 64);
   const float inv = 1.f / l_tot;
   uint16_t* orow = p.out + ((size_t)(q_row0 + row) * p.num_q_heads + h) * kHeadDim;
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb)
+  for (int mb = 0; mb < 4; ++mb) {
+    if ((mb >> 1) != kh) continue;
+    const float4* src = xacc + ((rg * 2 + (1 - kh)) * 2 + (mb & 1)) * 4 * 64;
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
+      const float4 y = src[a * 64 + lane];
       const int d = mb * 32 + 8 * a + 4 * hh;
       uint2 w;
-      w.x = pack_bf16x2(o[mb][4 * a + 0] * inv, o[mb][4 * a + 1] * inv);
-      w.y = pack_bf16x2(o[mb][4 * a + 2] * inv, o[mb][4 * a + 3] * inv);
+      w.x = pack_bf16x2((o[mb][4 * a + 0] * s0 + y.x * s1) * inv, (o[mb][4 * a + 1] * s0 + y.y * s1) * inv);
+      w.y = pack_bf16x2((o[mb][4 * a + 2] * s0 + y.z * s1) * inv, (o[mb][4 * a + 3] * s0 + y.w * s1) * inv);
       *reinterpret_cast<uint2*>(orow + d) = w;
     }
-  if (hh == 0 && p.lse) p.lse[(size_t)(q_row0 + row) * p.num_q_heads + h] = (m_run + fast_log2(l_tot)) * kLn2;
+  }
+  if (kh == 0 && hh == 0 && p.lse) p.lse[(size_t)(q_row0 + row) * p.num_q_heads + h] = (M + fast_log2(l_tot)) * kLn2;
 }
 
 }  // namespace
