@@ -232,6 +232,8 @@ pa_status attend_impl(const pa_shape* shape, const pa_kv_cache& kv, const void* 
   c.max_blocks = shape->max_blocks_per_seq;
   c.q_tiles = ceil_div(shape->max_q_len, kChunkRows);
   c.causal = (shape->flags & PA_FLAG_CAUSAL) ? 1 : 0;
+  c.max_ctx = shape->max_ctx_len;
+  c.max_q = shape->max_q_len;
   if (launch_chunk(c, plan.grid, s) != hipSuccess) return PA_ERR_LAUNCH;
   return PA_OK;
 }

@@ -70,16 +70,51 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkParams p) {
   const int wh = wave & 3;    // wave within the half (loader role)
   const int col = lane & 31;  // query row within the wave / MFMA column
   const int hh = lane >> 5;   // lane half
+  // The kernel arguments the start needs, fetched together: the index
+  // arithmetic below uses the pinned copies, so the compiler cannot start it
+  // on a first batch of arguments and fetch the rest one round trip later.
+  int grid = gridDim.x, q_tiles = p.q_tiles, hq = p.num_q_heads, hkv = p.num_kv_heads;
+  asm volatile("" : "+s"(grid), "+s"(q_tiles), "+s"(hq), "+s"(hkv)
+               : "s"(p.q_lens), "s"(p.ctx_lens), "s"(p.block_table), "s"(p.max_blocks), "s"(p.max_ctx),
+                 "s"(p.max_q), "s"(p.causal));
 
-  const int wg = xcd_remap(blockIdx.x, gridDim.x);
-  const int qt = wg % p.q_tiles;
-  const int sh = wg / p.q_tiles;
-  const int h = sh % p.num_q_heads;
-  const int seq = sh / p.num_q_heads;
-  const int g = h / (p.num_q_heads / p.num_kv_heads);
+  const int wg = xcd_remap(blockIdx.x, grid);
+  const int qt = wg % q_tiles;
+  const int sh = wg / q_tiles;
+  const int h = sh % hq;
+  const int seq = sh / hq;
+  const int g = h / (hq / hkv);
 
-  const int m = scalar_load_i32(p.q_lens, seq);
-  const int n = scalar_load_i32(p.ctx_lens, seq);
+  // The keys this half needs depend on the slot's lengths.  The page ids of
+  // its first four tiles are requested together with the lengths, for the
+  // tiles the declared maxima (max_ctx_len, max_q_len) give, and requested
+  // again only when the lengths differ: a memory round trip saved before the
+  // first tile request when the slot is full length.
+  const int32_t* bt = p.block_table + (size_t)seq * p.max_blocks;
+  auto half_tiles = [&](int m_, int n_, int& tile0_, int& last_page_, int& kv_end_) {
+    int kv = n_;
+    if (p.causal) {
+      const int last_row = min(m_, (qt + 1) * kChunkRows) - 1;
+      kv = min(n_, n_ - m_ + last_row + 1);
+    }
+    kv_end_ = kv;
+    const int nt = (max(kv, 1) + kTileKeys - 1) / kTileKeys;
+    tile0_ = kh * ((nt + 1) / 2);
+    last_page_ = max(0, (kv - 1) >> 4);
+  };
+  int32_t ids[8];  // pages 2 tile0 .. + 7: tiles 0 .. 3 of this half
+  auto request_ids = [&](int tile0_, int last_page_) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) ids[j] = scalar_load_i32(bt, min(2 * tile0_ + j, last_page_));
+  };
+  int tile0_g, last_page_g, kv_end_g;
+  half_tiles(p.max_q, p.max_ctx, tile0_g, last_page_g, kv_end_g);
+  request_ids(tile0_g, last_page_g);
+  int m = scalar_load_i32(p.q_lens, seq);
+  int n = scalar_load_i32(p.ctx_lens, seq);
+  // (all ten in flight before the first is used)
+  asm volatile("" : "+s"(ids[0]), "+s"(ids[1]), "+s"(ids[2]), "+s"(ids[3]), "+s"(ids[4]), "+s"(ids[5]),
+               "+s"(ids[6]), "+s"(ids[7]), "+s"(m), "+s"(n));
   if (m <= 0 || n <= 0 || qt * kChunkRows >= m) return;
   int q_row0 = 0;  // row offset of the slot, summed once the first tiles are requested
   const int row = qt * kChunkRows + rg * 32 + col;  // row within the slot
@@ -97,18 +132,12 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkParams p) {
   };
 
   // Keys this workgroup needs, split in two halves of whole tiles.
-  int kv_end = n;
-  if (p.causal) {
-    const int last_row = min(m, (qt + 1) * kChunkRows) - 1;
-    kv_end = min(n, n - m + last_row + 1);
-  }
+  int tile0, last_page, kv_end;
+  half_tiles(m, n, tile0, last_page, kv_end);
   const int ntiles = (kv_end + kTileKeys - 1) / kTileKeys;
   const int T = (ntiles + 1) / 2;       // tiles per half (both halves loop T times)
-  const int tile0 = kh * T;             // this half's first tile
   const int my_limit = p.causal ? (n - m + row) : (n - 1);  // last visible key of this row
-
-  const int32_t* bt = p.block_table + (size_t)seq * p.max_blocks;
-  const int last_page = (kv_end - 1) >> 4;
+  if (m != p.max_q || n != p.max_ctx) request_ids(tile0, last_page);
 
   // Loads straight into LDS (global_load_lds_dwordx4: lane l of a wave
   // writes bytes 16 l .. of the instruction's LDS base).  Each of a half's
@@ -117,17 +146,16 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkParams p) {
   // row l / 16 and so loads the global chunk that the swizzle puts there.
   // Keys past the end re-read the last key (finite: tail slots are never
   // read), whose scores are masked and whose probabilities are 0.
-  // Page ids of the next tile to load, read one load ahead.
+  // In the loop, the page ids of the next tile to load are read one load
+  // ahead.
   int32_t nid0 = 0, nid1 = 0;
   auto fetch_ids = [&](int it) {
     const int t = tile0 + it;
     nid0 = scalar_load_i32(bt, min(2 * t, last_page));
     nid1 = scalar_load_i32(bt, min(2 * t + 1, last_page));
   };
-  auto load_tile = [&](int it, int stage) {
+  auto issue_tile = [&](int it, int stage, int32_t id0, int32_t id1) {
     const int t = tile0 + it;
-    const int32_t id0 = nid0, id1 = nid1;
-    fetch_ids(it + 1);
     uint8_t* sk = s_buf[kh][stage][0];
     uint8_t* sv = s_buf[kh][stage][1];
 #pragma unroll
@@ -143,6 +171,11 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkParams p) {
       __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(p.v + off),
                                        (void __attribute__((address_space(3)))*)(sv + lds_off), 16, 0, 0);
     }
+  };
+  auto load_tile = [&](int it, int stage) {
+    const int32_t id0 = nid0, id1 = nid1;
+    fetch_ids(it + 1);
+    issue_tile(it, stage, id0, id1);
   };
 
   f32x16_t o[4];
@@ -306,10 +339,11 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkParams p) {
   // unconditional (a tile index past the half clamps to the last key), so
   // the load counter sees the same pattern on every trip.
   if (T > 0) {
-    fetch_ids(0);
-    load_tile(0, 0);
-    load_tile(1, 1);
-    load_tile(2, 2);
+    issue_tile(0, 0, ids[0], ids[1]);
+    issue_tile(1, 1, ids[2], ids[3]);
+    issue_tile(2, 2, ids[4], ids[5]);
+    nid0 = ids[6];
+    nid1 = ids[7];
   }
   // Sixteen independent scalar loads per batch (indices clamped into the
   // array, the extra ones masked), one wait each: scalar loads leave the

@@ -76,6 +76,8 @@ struct ChunkParams {
   int32_t max_blocks;
   int32_t q_tiles;            // ceil(max_q_len / rows per workgroup)
   int32_t causal;
+  int32_t max_ctx;            // max_ctx_len and max_q_len: the lengths the
+  int32_t max_q;              // first page ids are requested for, unverified
 };
 
 struct CombineParams {
