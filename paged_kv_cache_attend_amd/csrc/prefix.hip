@@ -64,7 +64,15 @@ __device__ void write_slot_prefix(const PrefixParams& p) {
 }
 
 __global__ __launch_bounds__(kThreads, 1) void prefix_kernel(PrefixParams p) {
-  if (blockIdx.x == gridDim.x - 1) {
+  // The kernel arguments the start needs, fetched together: the index
+  // arithmetic below uses the pinned copies, so the compiler cannot start it
+  // on a first batch of arguments and fetch the rest round trips later.
+  int grid = gridDim.x, parts = p.pre_parts, row_tiles = p.row_tiles, hkv = p.num_kv_heads, nhq = p.num_q_heads;
+  int part_pages = p.part_pages, max_members = p.max_members, num_seqs = p.num_seqs, max_blocks = p.max_blocks;
+  asm volatile("" : "+s"(grid), "+s"(parts), "+s"(row_tiles), "+s"(hkv), "+s"(nhq), "+s"(part_pages), "+s"(max_members),
+                    "+s"(num_seqs), "+s"(max_blocks)
+               : "s"(p.block_table), "s"(p.group_start), "s"(p.prefix_len));
+  if (blockIdx.x == grid - 1) {
     write_slot_prefix(p);
     return;
   }
@@ -79,28 +87,31 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_kernel(PrefixParams p) {
   const int col = lane & 31;
   const int hh = lane >> 5;
 
-  const int wg = xcd_remap(blockIdx.x, gridDim.x - 1);
-  const int part = wg % p.pre_parts;
-  int rest = wg / p.pre_parts;
-  const int rt = rest % p.row_tiles;
-  rest /= p.row_tiles;
-  const int g = rest % p.num_kv_heads;
-  const int grp = rest / p.num_kv_heads;
-  const int G = p.num_q_heads / p.num_kv_heads;
+  const int wg = xcd_remap(blockIdx.x, grid - 1);
+  const int part = wg % parts;
+  int rest = wg / parts;
+  const int rt = rest % row_tiles;
+  rest /= row_tiles;
+  const int g = rest % hkv;
+  const int grp = rest / hkv;
+  const int G = nhq / hkv;
 
   // The group's table row is needed before any key can be requested.  The
   // row is guessed (groups of max_members consecutive slots) and its two
   // page ids for this wave's tile are requested together with the group's
   // bounds, saving a memory round trip when the guess holds.
-  const int key0 = part * p.part_pages * kBlockSize;
+  const int key0 = part * part_pages * kBlockSize;
   const int page0 = (key0 >> 4) + 2 * wave;  // first page of tile `wave`
-  const int s_guess = (int)min((long long)grp * p.max_members, (long long)p.num_seqs - 1);
-  const int32_t* bt_guess = uniform_ptr(p.block_table + (size_t)s_guess * p.max_blocks);
-  int32_t id0 = scalar_load_i32(bt_guess, min(page0, p.max_blocks - 1));
-  int32_t id1 = scalar_load_i32(bt_guess, min(page0 + 1, p.max_blocks - 1));
-  const int s0 = scalar_load_i32(p.group_start, grp);
-  const int s1 = scalar_load_i32(p.group_start, grp + 1);
-  const int plen = scalar_load_i32(p.prefix_len, grp) & ~15;  // whole pages, as the decode pass reads it
+  const int s_guess = (int)min((long long)grp * max_members, (long long)num_seqs - 1);
+  const int32_t* bt_guess = uniform_ptr(p.block_table + (size_t)s_guess * max_blocks);
+  int32_t id0 = scalar_load_i32(bt_guess, min(page0, max_blocks - 1));
+  int32_t id1 = scalar_load_i32(bt_guess, min(page0 + 1, max_blocks - 1));
+  int s0 = scalar_load_i32(p.group_start, grp);
+  int s1 = scalar_load_i32(p.group_start, grp + 1);
+  int plen = scalar_load_i32(p.prefix_len, grp);
+  // (all five in flight before the first is used)
+  asm volatile("" : "+s"(id0), "+s"(id1), "+s"(s0), "+s"(s1), "+s"(plen));
+  plen &= ~15;  // whole pages, as the decode pass reads it
   const int members = s1 - s0;
   const int rows_here = members * G - rt * 64;  // rows of this tile that exist
   if (rows_here <= 0 || plen <= 0) return;
