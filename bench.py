@@ -271,10 +271,10 @@ def chunk_secondary(dev, steps, launch="graph"):
                                       float(p.scale), out, lse, max_q_len=p.max_q_len,
                                       max_ctx_len=p.max_ctx_len))
     flops = 4 * int((p.q_lens.astype(np.int64) * p.ctx_lens).sum()) * p.num_q_heads * p.head_dim
-    reps = max(steps, 50)
-    cold_ms, _, _ = time_pass(sets, reps // 16 + 1, 2, launch)
+    passes = max(steps, 640) // 16  # 16 launches per pass; ~20 ms of GPU time per figure
+    cold_ms, _, _ = time_pass(sets, passes, 10, launch)
     cold_ms /= len(sets)
-    warm_ms, _, _ = time_pass(sets[:1] * 16, reps // 16 + 1, 2, launch)
+    warm_ms, _, _ = time_pass(sets[:1] * 16, passes, 10, launch)
     warm_ms /= 16
     return {"workload": "chunked_denoise", "flop_per_call": flops,
             "tflops_cold": flops / (cold_ms * 1e-3) / 1e12, "tflops_warm": flops / (warm_ms * 1e-3) / 1e12,
