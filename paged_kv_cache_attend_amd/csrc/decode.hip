@@ -164,10 +164,14 @@ __device__ __forceinline__ u32x4_t chunk_to_bf16(const T& c) {
     }
     return r;
   } else {
+    // Code n stands for n - 8.  With the top bit of every nibble flipped,
+    // a nibble read as a signed 4-bit field is exactly n - 8, so a signed
+    // bit-field extract (the shift pair) and one conversion give each value.
+    const uint32_t x = c ^ 0x88888888u;
     u32x4_t r;
 #pragma unroll
     for (int w = 0; w < 4; ++w)
-      r[w] = pack_bf16x2((float)(int)((c >> (8 * w)) & 15u) - 8.f, (float)(int)((c >> (8 * w + 4)) & 15u) - 8.f);
+      r[w] = pack_bf16x2((float)((int)(x << (28 - 8 * w)) >> 28), (float)((int)(x << (24 - 8 * w)) >> 28));
     return r;
   }
 }
