@@ -363,3 +363,29 @@ def test_attend_prefix_host_errors(lib):
     assert init(ctypes.byref(s), ctypes.byref(g), None, ctypes.c_size_t(need), None) == pk.Status.ERR_NULL_ARG
     assert init(ctypes.byref(s), ctypes.byref(g), FAKE, ctypes.c_size_t(need - 1), None) == \
         pk.Status.ERR_WORKSPACE_TOO_SMALL
+
+
+def test_prefix_partition_plan():
+    # The prefix pass splits the longest prefix into partitions of at most
+    # eight 32-key tiles (16 pages), more when CUs would sit idle (up to 24
+    # per (group, KV head, row tile)), never under one tile: read back from
+    # the workspace size, whose last region holds one fp32 partial per
+    # partition and row.
+    lib = pk.load()
+    s = _shape(num_seqs=10, total_q=10, max_blocks_per_seq=528, max_ctx_len=8447, num_blocks=6000)
+    rows = 10 * 32
+    size = lambda g: lib.pa_prefix_workspace_size(ctypes.byref(s), ctypes.byref(g))
+    none = size(_groups(num_groups=0, max_members=0, max_prefix_len=0))
+    base = none - (_align(10 * 4) + _align(rows * 4) + rows * 128 * 4)
+
+    def parts(max_prefix_len):
+        ws = size(_groups(num_groups=1, max_members=10, max_prefix_len=max_prefix_len))
+        for p in range(1, 200):
+            if ws == base + _align(10 * 4) + _align(p * rows * 4) + p * rows * 128 * 4:
+                return p
+        raise AssertionError(f"workspace {ws} matches no partition count")
+
+    assert parts(6144) == 24    # 384 pages: 24 partitions of 16 (one group x 8 KV heads = 8 of 256 CUs each)
+    assert parts(8192) == 32    # 512 pages: 16 pages per partition at most
+    assert parts(64) == 2       # 4 pages: one 32-key tile each
+    assert parts(16) == 1
