@@ -109,7 +109,14 @@ typedef struct pa_shape {
  * needs for this shape: one int32 counter per
  * (slot, KV head), then the split-KV partials (fp32 LSE and normalised fp32
  * output per partition and row).  0 when the call needs none.  Returns 0 for
- * a shape pa_attend would reject. */
+ * a shape pa_attend would reject.
+ * Why partials exist: a one-token decode step is too small to occupy the
+ * whole GPU (OpScale page, section 2.1, Figure 7: one-token decode kernels
+ * leave much of the SM allocation unused), so long contexts are cut into
+ * partitions that run side by side and are merged by log-sum-exp.  The
+ * caller allocates this buffer once and reuses it every step (Photon page,
+ * section 3: working buffers are allocated once, at fixed addresses, so that
+ * a step can be captured as a graph and replayed). */
 size_t pa_workspace_size(const pa_shape* shape);
 
 /* Prepare a workspace for this shape: zero its counter region (enqueued on
@@ -143,7 +150,13 @@ pa_status pa_attend(const pa_shape* shape, const void* q, const void* k_cache,
                     void* out, float* lse, void* workspace,
                     size_t workspace_bytes, void* stream);
 
-/* Merge split-KV partials by their log-sum-exp weights.  For each row:
+/* Merge split-KV partials by their log-sum-exp weights.  No page states
+ * this formula: it is the softmax of the definition above regrouped over
+ * disjoint key sets (each partial o_p is the softmax-weighted mean over its
+ * keys, lse_p the log of its sum of exponentials), so merging is exact up to
+ * rounding.  Used for partitions of one request's keys and for a shared
+ * prefix read once for several requests (chapter section 8.3.2).  For each
+ * row:
  *   M = max_p lse_p,  w_p = exp(lse_p - M),
  *   lse = M + ln sum_p w_p,  out = sum_p w_p o_p / sum_p w_p  (bf16, RNE).
  * Partials with lse_p = -inf weigh zero and their outputs are never read; a
@@ -160,7 +173,9 @@ pa_status pa_combine(int32_t num_partials, int32_t rows, int32_t head_dim,
                      void* out, float* lse, void* stream);
 
 /* Copy every active slot's cached K (or V) rows into a dense buffer through
- * the same page addressing the attention kernels use:
+ * the same page addressing the attention kernels use -- the block-table
+ * lookup of section 8.3.1, Fig. 8-10 (logical block j / 16 of a request maps
+ * to whichever physical block its table names):
  *   dst[r][j][g][:] = cache[block_table[r][j / 16]][g][j % 16][:]  for j < n
  * dst is bf16 [num_seqs][max_ctx_len][num_kv_heads][head_dim]; rows j >= n
  * (and all rows of slots with n == 0) are left untouched.  For checking the
@@ -169,16 +184,27 @@ pa_status pa_gather_kv(const pa_shape* shape, const void* cache,
                        const int32_t* block_table, const int32_t* ctx_lens,
                        void* dst, void* stream);
 
-/* Check the device-side preconditions of pa_attend for this shape and data.
- * Writes a bit mask to *error_word (device int32, caller-owned): 0 if all
- * hold, else PA_BAD_* bits below.  Enqueued on `stream`; read the word after
- * the stream passes. */
+/* Check the device-side preconditions of pa_attend for this shape and data,
+ * so that a caller can reject a bad batch before submitting it (the PhyAI
+ * parallel-serving page, failure handling: requests are checked before
+ * submission, and failures are fail-fast with no retry).  Writes a bit mask
+ * to *error_word (device int32, caller-owned): 0 if all hold, else PA_BAD_*
+ * bits below.  `workspace` may be NULL; if given (with its size), the
+ * split-KV counters pa_attend would use for this shape are also checked to
+ * be zero -- a workspace that was not initialised for this shape, or whose
+ * last call did not run to completion, would corrupt the merge silently.
+ * Enqueued on `stream`; read the word after the stream passes.  Errors:
+ * PA_ERR_NULL_ARG, PA_ERR_BAD_SHAPE / PA_ERR_UNSUPPORTED (as pa_attend),
+ * PA_ERR_WORKSPACE_TOO_SMALL (a workspace smaller than its counter region),
+ * PA_ERR_LAUNCH. */
 #define PA_BAD_BLOCK_ID 0x1   /* a table entry in [0, ceil(n/16)) outside [0, num_blocks) */
 #define PA_BAD_CTX_LEN 0x2    /* n < 0, n > max_ctx_len or n > 16 * max_blocks_per_seq */
 #define PA_BAD_Q_LEN 0x4      /* m < 0, m > max_q_len, or m > n while n > 0 */
 #define PA_BAD_TOTAL_Q 0x8    /* sum of q_lens exceeds total_q */
+#define PA_BAD_WORKSPACE 0x10 /* a split-KV counter of this shape is not zero */
 pa_status pa_validate(const pa_shape* shape, const int32_t* block_table,
                       const int32_t* ctx_lens, const int32_t* q_lens,
+                      const void* workspace, size_t workspace_bytes,
                       int32_t* error_word, void* stream);
 
 /* ------------------------------------------------------------------------

@@ -21,6 +21,7 @@ PA_BAD_BLOCK_ID = 0x1
 PA_BAD_CTX_LEN = 0x2
 PA_BAD_Q_LEN = 0x4
 PA_BAD_TOTAL_Q = 0x8
+PA_BAD_WORKSPACE = 0x10
 
 EXPORTS = ("pa_workspace_size", "pa_workspace_init", "pa_num_partitions", "pa_attend", "pa_combine",
            "pa_gather_kv", "pa_validate", "pa_write_kv", "pa_copy_blocks", "pa_pool_create",
@@ -148,7 +149,7 @@ def load():
     lib.pa_combine.restype = ctypes.c_int
     lib.pa_gather_kv.argtypes = [shp, P, P, P, P, P]
     lib.pa_gather_kv.restype = ctypes.c_int
-    lib.pa_validate.argtypes = [shp, P, P, P, P, P]
+    lib.pa_validate.argtypes = [shp, P, P, P, P, ctypes.c_size_t, P, P]
     lib.pa_validate.restype = ctypes.c_int
     lib.pa_write_kv.argtypes = [shp, P, P, P, P, P, P, P, P]
     lib.pa_write_kv.restype = ctypes.c_int
@@ -242,10 +243,34 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def _stream_handle(device, stream):
+def _stream(device, stream):
     torch = _torch()
-    s = torch.cuda.current_stream(device) if stream is None else stream
-    return ctypes.c_void_p(s.cuda_stream)
+    return torch.cuda.current_stream(device) if stream is None else stream
+
+
+def _stream_handle(device, stream):
+    return ctypes.c_void_p(_stream(device, stream).cuda_stream)
+
+
+def _new_workspace(shape: Shape, nbytes: int, device, stream, init=None, wait=False):
+    """A workspace for calls launched on `stream`: allocated from that
+    stream's pool (so the caching allocator reuses it only after the stream
+    has passed the work queued on it) and initialised on that same stream.
+    With ``wait`` the host waits for the initialisation (set-up of prepared
+    calls, which may later be launched on other streams)."""
+    torch = _torch()
+    s = _stream(device, stream)
+    with torch.cuda.stream(s):
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    if init is None:
+        workspace_init(shape, ws, stream=s)
+    else:
+        init(ws, s)
+    if wait:
+        done = torch.cuda.Event()
+        done.record(s)
+        done.synchronize()
+    return ws
 
 
 def _need(t, name, dtype, device, ndim=None):
@@ -297,8 +322,7 @@ def attend(q, k_cache, v_cache, block_table, ctx_lens, q_lens, scale, out, lse=N
                        nb, partition_size, causal, head_dim=d, block_size=bs)
     need = workspace_size(shape)
     if need and workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
-        workspace_init(shape, workspace, stream=stream)
+        workspace = _new_workspace(shape, need, dev, stream)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = load().pa_attend(ctypes.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
                           _ptr(ctx_lens), _ptr(q_lens), ctypes.c_float(float(scale)), _ptr(out), _ptr(lse),
@@ -348,15 +372,18 @@ def gather_kv(cache, block_table, ctx_lens, dst, *, max_ctx_len: int, stream=Non
 
 def validate(block_table, ctx_lens, q_lens, error_word, *, num_blocks: int, total_q: int,
              max_q_len: int, max_ctx_len: int, num_q_heads: int = 1, num_kv_heads: int = 1,
-             stream=None):
-    """``pa_validate``: writes the PA_BAD_* mask into error_word (int32 [1])."""
+             partition_size: int = 0, workspace=None, stream=None):
+    """``pa_validate``: writes the PA_BAD_* mask into error_word (int32 [1]);
+    with ``workspace``, also checks its split-KV counters for this shape."""
     torch = _torch()
     dev = block_table.device
     _need(error_word, "error_word", torch.int32, dev, 1)
     shape = make_shape(block_table.shape[0], total_q, num_q_heads, num_kv_heads, block_table.shape[1],
-                       max_q_len, max_ctx_len, num_blocks)
+                       max_q_len, max_ctx_len, num_blocks, partition_size)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = load().pa_validate(ctypes.byref(shape), _ptr(block_table), _ptr(ctx_lens), _ptr(q_lens),
-                            _ptr(error_word), _stream_handle(dev, stream))
+                            _ptr(workspace), ctypes.c_size_t(ws_bytes), _ptr(error_word),
+                            _stream_handle(dev, stream))
     _check(st, "pa_validate")
     return error_word
 
@@ -438,10 +465,11 @@ def attend_prefix(q, k_cache, v_cache, block_table, ctx_lens, q_lens, scale, out
     if need == 0:
         raise PaError(Status.ERR_BAD_SHAPE, "pa_prefix_workspace_size")
     if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
-        _check(lib.pa_prefix_workspace_init(ctypes.byref(shape), ctypes.byref(groups), _ptr(workspace),
-                                            ctypes.c_size_t(need), _stream_handle(dev, stream)),
-               "pa_prefix_workspace_init")
+        def init(ws, s):
+            _check(lib.pa_prefix_workspace_init(ctypes.byref(shape), ctypes.byref(groups), _ptr(ws),
+                                                ctypes.c_size_t(need), ctypes.c_void_p(s.cuda_stream)),
+                   "pa_prefix_workspace_init")
+        workspace = _new_workspace(shape, need, dev, stream, init, wait=prepared)
     ws_bytes = workspace.numel() * workspace.element_size()
     args = [ctypes.byref(shape), ctypes.byref(groups), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
             _ptr(ctx_lens), _ptr(q_lens), ctypes.c_float(float(scale)), _ptr(out), _ptr(lse), _ptr(workspace),
@@ -545,8 +573,7 @@ def attend_kv(q, cache: QuantCache, block_table, ctx_lens, q_lens, scale, out, l
                        max_ctx_len, cache.num_blocks, partition_size, head_dim=d)
     need = workspace_size(shape)
     if need and workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
-        workspace_init(shape, workspace, stream=stream)
+        workspace = _new_workspace(shape, need, dev, stream, wait=prepared)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     kv = cache.struct()
     args = [ctypes.byref(shape), ctypes.byref(kv), _ptr(q), _ptr(block_table), _ptr(ctx_lens), _ptr(q_lens),
@@ -664,13 +691,15 @@ class PreparedAttend:
     """A ``pa_attend`` call with its arguments marshalled once.
 
     For launch loops (benchmarks, graph capture): ``launch()`` makes the bare
-    C call on the given stream and checks the status.  The tensors must stay
-    alive and in place for as long as the object is used.
+    C call and checks the status.  The workspace is initialised on ``stream``
+    (default: the current stream at construction), and construction waits for
+    that initialisation, so the first launch may go to any stream.  The
+    tensors must stay alive and in place for as long as the object is used.
     """
 
     def __init__(self, q, k_cache, v_cache, block_table, ctx_lens, q_lens, scale, out, lse=None, *,
                  max_q_len: int, max_ctx_len: int, partition_size: int = 0, causal: bool = False,
-                 workspace=None):
+                 workspace=None, stream=None):
         torch = _torch()
         dev = q.device
         for t, name, dt, nd in ((q, "q", torch.bfloat16, 3), (out, "out", torch.bfloat16, 3),
@@ -685,14 +714,19 @@ class PreparedAttend:
         self.shape = make_shape(block_table.shape[0], total_q, hq, hkv, block_table.shape[1], max_q_len,
                                 max_ctx_len, nb, partition_size, causal, head_dim=d, block_size=bs)
         need, self.num_partitions = plan(self.shape)
-        if need and workspace is None:
-            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        self.stream = _stream(dev, stream)
+        if need:
+            if workspace is None:
+                workspace = _new_workspace(self.shape, need, dev, self.stream)
+            else:
+                if workspace.numel() * workspace.element_size() < need:
+                    raise PaError(Status.ERR_WORKSPACE_TOO_SMALL, "PreparedAttend")
+                workspace_init(self.shape, workspace, stream=self.stream)
+            done = torch.cuda.Event()
+            done.record(self.stream)
+            done.synchronize()  # set-up only: launches on any stream see zeroed counters
         self.workspace = workspace
         ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-        if ws_bytes < need:
-            raise PaError(Status.ERR_WORKSPACE_TOO_SMALL, "PreparedAttend")
-        if need:
-            workspace_init(self.shape, workspace)
         self._keep = (q, k_cache, v_cache, block_table, ctx_lens, q_lens, out, lse, workspace)
         self._fn = load().pa_attend
         self._args = [ctypes.byref(self.shape), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
@@ -701,6 +735,8 @@ class PreparedAttend:
         self.device = dev
 
     def launch(self, stream=None):
-        st = self._fn(*self._args, _stream_handle(self.device, stream))
+        """Launch on `stream` (default: the stream given at construction)."""
+        s = self.stream if stream is None else stream
+        st = self._fn(*self._args, ctypes.c_void_p(s.cuda_stream))
         if st:
             raise PaError(st, "pa_attend")

@@ -402,12 +402,22 @@ pa_status pa_gather_kv(const pa_shape* shape, const void* cache, const int32_t* 
 }
 
 pa_status pa_validate(const pa_shape* shape, const int32_t* block_table, const int32_t* ctx_lens,
-                      const int32_t* q_lens, int32_t* error_word, void* stream) {
+                      const int32_t* q_lens, const void* workspace, size_t workspace_bytes,
+                      int32_t* error_word, void* stream) {
   const pa_status st = check_shape(shape);
   if (st != PA_OK) return st;
   if (!error_word) return PA_ERR_NULL_ARG;
   if (shape->num_seqs > 0 && (!block_table || !ctx_lens || !q_lens)) return PA_ERR_NULL_ARG;
   ValidateParams v = {};
+  // The counters sit at the start of the workspace for every page format
+  // and for the suffix pass of pa_attend_prefix: one per (slot, KV head),
+  // present whenever the shape needs a workspace.
+  if (workspace && pa_workspace_size(shape) > 0) {
+    const size_t n = (size_t)shape->num_seqs * (size_t)shape->num_kv_heads;
+    if (workspace_bytes < n * sizeof(int32_t)) return PA_ERR_WORKSPACE_TOO_SMALL;
+    v.counters = static_cast<const int32_t*>(workspace);
+    v.num_counters = (int32_t)n;
+  }
   v.block_table = block_table;
   v.ctx_lens = ctx_lens;
   v.q_lens = q_lens;

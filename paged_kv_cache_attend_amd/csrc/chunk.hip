@@ -30,7 +30,10 @@
 //      the B operand of O^T += V^T P^T (4 x 32 dims, 2 key steps, 8 MFMAs);
 //      the V^T A operand is read from the row-major V tile with transposing
 //      LDS reads (ds_read_b64_tr_b16), issued before the softmax so that they
-//      complete under it.
+//      complete under it.  The output is divided by the sum of those rounded
+//      weights, so it is an exact weighted mean of the V rows under the
+//      weights PV used (a single dominant key comes back exactly); the LSE
+//      takes the sum of the fp32 weights.
 // Keys past the end load the last key (finite) and get -inf scores.
 
 #include "device.h"
@@ -184,7 +187,8 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkParams p) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) o[mb][i] = 0.f;
   float m_run = -INFINITY;  // reference max of this row (log2 domain)
-  float l_run = 0.f;        // this lane's share of the row sum
+  float l_run = 0.f;        // this lane's share of the row sum (fp32 weights)
+  float r_run = 0.f;        // the same over the bf16-rounded weights PV uses
 
   auto compute_tile = [&](int it, int stage) {
     const uint8_t* sk = s_buf[kh][stage][0];
@@ -283,6 +287,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkParams p) {
       const float m_new = fmaxf(m_run, mloc);
       const float alpha = fast_exp2(m_run - ((m_new == -INFINITY) ? 0.f : m_new));
       l_run *= alpha;
+      r_run *= alpha;
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
@@ -307,13 +312,17 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkParams p) {
     l_run += lsum;
     // P^T operand for key steps 0 and 1: keys 16ks + 4hh + 0..3, 16ks + 8 + 4hh + 0..3.
     u32x4_t pf[2];
+    float rsum = 0.f;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       pf[ks][0] = pack_bf16x2(sv[8 * ks + 0], sv[8 * ks + 1]);
       pf[ks][1] = pack_bf16x2(sv[8 * ks + 2], sv[8 * ks + 3]);
       pf[ks][2] = pack_bf16x2(sv[8 * ks + 4], sv[8 * ks + 5]);
       pf[ks][3] = pack_bf16x2(sv[8 * ks + 6], sv[8 * ks + 7]);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) rsum += bf16_lo(pf[ks][w]) + bf16_hi(pf[ks][w]);
     }
+    r_run += rsum;
     // The transposed reads must have landed (the operands pass through this
     // block, so nothing reads them before it).
     asm volatile("s_waitcnt lgkmcnt(0)"
@@ -381,10 +390,10 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkParams p) {
   // and the stores.  Layout [row group][sender half][block][chunk of 4
   // floats][lane]: 16-byte accesses by consecutive lanes.
   float4* xacc = reinterpret_cast<float4*>(&s_buf[0][0][0][0]);
-  float2* xml = reinterpret_cast<float2*>(xacc + 4 * 2 * 2 * 4 * 64);  // [row group][half][lane]: (m, l)
-  static_assert(4 * 2 * 2 * 4 * 64 * sizeof(float4) + 4 * 2 * 64 * sizeof(float2) <= sizeof(s_buf),
+  float4* xml = xacc + 4 * 2 * 2 * 4 * 64;  // [row group][half][lane]: (m, l, rounded l)
+  static_assert(4 * 2 * 2 * 4 * 64 * sizeof(float4) + 4 * 2 * 64 * sizeof(float4) <= sizeof(s_buf),
                 "merge buffer exceeds the tile area");
-  xml[(rg * 2 + kh) * 64 + lane] = make_float2(m_run, l_run);
+  xml[(rg * 2 + kh) * 64 + lane] = make_float4(m_run, l_run, r_run, 0.f);
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb) {
     if ((mb >> 1) == kh) continue;
@@ -396,14 +405,15 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkParams p) {
   __syncthreads();
   if (!row_live) return;  // both lanes of a row leave together
 
-  const float2 ml = xml[(rg * 2 + (1 - kh)) * 64 + lane];
+  const float4 ml = xml[(rg * 2 + (1 - kh)) * 64 + lane];
   const float M = fmaxf(m_run, ml.x);
   const float Mu = (M == -INFINITY) ? 0.f : M;
   const float s0 = fast_exp2(m_run - Mu);
   const float s1 = fast_exp2(ml.x - Mu);
   const float l = l_run * s0 + ml.y * s1;
   const float l_tot = l + __shfl_xor(l, 32, 64);
-  const float inv = 1.f / l_tot;
+  const float r = r_run * s0 + ml.z * s1;
+  const float inv = 1.f / (r + __shfl_xor(r, 32, 64));
   uint16_t* orow = p.out + ((size_t)(q_row0 + row) * p.num_q_heads + h) * kHeadDim;
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb) {

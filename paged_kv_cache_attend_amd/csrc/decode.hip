@@ -42,11 +42,18 @@
 //   than 2^8, which keeps every weight <= 256.
 // * PV: the same lanes hold P^T in exactly the B-operand layout of
 //   v_mfma_f32_16x16x16_bf16, so the weights (times each token's V group
-//   scale, one operand per 32-dim group) are rounded to bf16 and used from
-//   registers; the V^T A operand is read from the V tile with transposing
-//   LDS reads (ds_read_b64_tr_b16), eight 16-dim blocks per page.  Rows past
-//   a slot's end are zeroed in the V tile and get weight 0 by select, since
-//   their stored codes and scales may be anything.
+//   scale, one operand per 32-dim group) are used from registers; the V^T A
+//   operand is read from the V tile with transposing LDS reads
+//   (ds_read_b64_tr_b16), eight 16-dim blocks per page.  The weights reach
+//   PV at close to fp32 accuracy although the operand is bf16: the query
+//   heads also fill columns G .. 2G - 1 of the score tile (columns that would
+//   otherwise hold a zero query), so those lanes compute the same weights w,
+//   and they feed PV the remainder lo = w - hi(w) while lanes of columns < G
+//   feed hi(w), w cut to bf16.  hi + lo is w to 2^-15 of w, and the two
+//   output columns of a head are added once at the end: no extra matrix
+//   product.  Rows past a slot's end are zeroed in the V tile
+//   and get weight 0 by select, since their stored codes and scales may be
+//   anything.
 // * Epilogue: the four waves' (max, sum, acc) merge through LDS.  With one
 //   partition the workgroup writes bf16 out and the LSE.  Otherwise it writes
 //   its normalised fp32 partial and LSE to the workspace, and the last of the
@@ -66,6 +73,10 @@ namespace pa {
 namespace {
 
 constexpr int kWaves = kDecodeWaves;
+#ifndef PA_DECODE_RING
+#define PA_DECODE_RING 3
+#endif
+constexpr int kRing = PA_DECODE_RING;                  // pages per wave in the register ring
 constexpr int kTileBytes = kBlockSize * kHeadDim * 2;  // 4 KiB
 constexpr float kRescaleSlack = 8.0f;                  // log2 units
 
@@ -190,6 +201,17 @@ __device__ __forceinline__ s16x4_t as_s16x4(uint32_t lo, uint32_t hi) {
   return __builtin_bit_cast(s16x4_t, u32x2_t{lo, hi});
 }
 
+// Two fp32 weights as a bf16 pair.  In the lanes of columns < G: hi(w), w
+// truncated to bf16 (its top 16 bits); in the lanes of the duplicate columns:
+// w - hi(w) (exact in fp32), truncated likewise.  hi + lo is w to within 2^-15
+// of w, and both halves come from one byte permute per pair.
+__device__ __forceinline__ uint32_t hi_or_lo(float w0, float w1, uint32_t lo_mask) {
+  const float x0 = w0 - __uint_as_float(__float_as_uint(w0) & lo_mask);
+  const float x1 = w1 - __uint_as_float(__float_as_uint(w1) & lo_mask);
+  // bytes 2, 3 of x0 and 2, 3 of x1 -> (lo half, hi half) of the result
+  return __builtin_amdgcn_perm(__float_as_uint(x1), __float_as_uint(x0), 0x07060302u);
+}
+
 template <int G>
 struct WaveState {
   float m_ref;    // reference max (log2 domain) of head lane % 16
@@ -287,9 +309,11 @@ __device__ __forceinline__ void consume_page(WaveState<G>& st, Page<F>& b, uint8
     vt[bb] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
         (lds_s16x4_t*)(vrow + (((2 * bb + ((pc & 3) >> 1)) ^ tv) << 4)));
 
-  // P^T operand: this lane's tokens 4 pr .. + 4 of column pc, as bf16; with
-  // grouped V scales one operand per 32-dim group (tokens past the end get
-  // weight 0 by select: their stored scales may be anything).
+  // P^T operand: this lane's tokens 4 pr .. + 4 of column pc, as bf16 (hi
+  // in columns < G, lo in columns G .. 2G - 1); with grouped V scales one
+  // operand per 32-dim group (tokens past the end get weight 0 by select:
+  // their stored scales may be anything).
+  const uint32_t lo_mask = pc >= G ? 0xffff0000u : 0u;  // lanes that feed lo subtract hi
   if constexpr (kGrouped) {
     f32x4_t vsc[4];  // V scales of tokens 4 pr + i, groups 0..3
 #pragma unroll
@@ -299,20 +323,23 @@ __device__ __forceinline__ void consume_page(WaveState<G>& st, Page<F>& b, uint8
       float w[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) w[i] = 4 * pr + i < valid ? pw[i] * vsc[i][gr] : 0.f;
-      const s16x4_t pg = as_s16x4(pack_bf16x2(w[0], w[1]), pack_bf16x2(w[2], w[3]));
+      const s16x4_t pg = as_s16x4(hi_or_lo(w[0], w[1], lo_mask), hi_or_lo(w[2], w[3], lo_mask));
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2)
         st.o[2 * gr + h2] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt[2 * gr + h2], pg, st.o[2 * gr + h2], 0, 0, 0);
     }
   } else {
-    const s16x4_t pg = as_s16x4(pack_bf16x2(pw[0], pw[1]), pack_bf16x2(pw[2], pw[3]));
+    const s16x4_t pg = as_s16x4(hi_or_lo(pw[0], pw[1], lo_mask), hi_or_lo(pw[2], pw[3], lo_mask));
 #pragma unroll
     for (int bb = 0; bb < 8; ++bb) st.o[bb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt[bb], pg, st.o[bb], 0, 0, 0);
   }
 }
 
 template <int G, int F>
-__global__ __launch_bounds__(kDecodeThreads, kDecodeWGsPerCU) void decode_kernel(DecodeParams p) {
+#ifndef PA_DECODE_MIN_WGS
+#define PA_DECODE_MIN_WGS kDecodeWGsPerCU
+#endif
+__global__ __launch_bounds__(kDecodeThreads, PA_DECODE_MIN_WGS) void decode_kernel(DecodeParams p) {
   static_assert(G == 1 || G == 2 || G == 4, "group size");
   __shared__ __attribute__((aligned(16))) uint8_t s_k[kWaves][kTileBytes];
   __shared__ __attribute__((aligned(16))) uint8_t s_q[G][kHeadDim * 2];
@@ -352,15 +379,17 @@ __global__ __launch_bounds__(kDecodeThreads, kDecodeWGsPerCU) void decode_kernel
   // whose partials the prefix pass has written; the last partition runs to
   // the slot's end whatever the prefix length.
   const int plen = p.slot_plen ? scalar_load_i32(p.slot_plen, seq) : 0;
-  int32_t sid[4];
+  int32_t sid[kRing + 1];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) sid[k] = scalar_load_i32(bt, min(spage0 + k * kWaves, p.max_blocks - 1));
+  for (int k = 0; k <= kRing; ++k) sid[k] = scalar_load_i32(bt, min(spage0 + k * kWaves, p.max_blocks - 1));
   int qsum = 0;  // this lane's share of the row offset
   for (int i = lane; i < seq; i += 64) qsum += p.q_lens[i];
   // (Keeps the loads above the branch: the compiler would otherwise sink the
   // ones only the working path uses below it, one round trip later.  The
   // wave sum of the row offset waits until the first page is requested.)
-  asm volatile("" : "+s"(sid[0]), "+s"(sid[1]), "+s"(sid[2]), "+s"(sid[3]), "+v"(qsum));
+#pragma unroll
+  for (int k = 0; k <= kRing; ++k) asm volatile("" : "+s"(sid[k]));
+  asm volatile("" : "+v"(qsum));
   if (m <= 0) return;  // no row: nothing to write, no partial to count
   const int npages = (n + kBlockSize - 1) / kBlockSize;
   const int npre = (plen > 0 && n > 0) ? p.pre_parts : 0;
@@ -385,26 +414,26 @@ __global__ __launch_bounds__(kDecodeThreads, kDecodeWGsPerCU) void decode_kernel
   float my_o0 = 0.f, my_o1 = 0.f, my_lse = -INFINITY;  // this workgroup's partial
 
   // Prologue, in issue order: the wave's first page, the query (so that its
-  // wait only covers that first page, needed next anyway), the second and
-  // third pages.  Every load here is unconditional within the workgroup-
-  // uniform has_work branch -- a wave with fewer than three pages re-reads a
-  // valid page -- so the load counter's waits stay exact.
-  Page<F> ring0, ring1, ring2;
+  // wait only covers that first page, needed next anyway), then pages 1 ..
+  // kRing - 1.  Every load here is unconditional within the workgroup-
+  // uniform has_work branch -- a wave with fewer pages than the ring re-reads
+  // a valid page -- so the load counter's waits stay exact.
+  Page<F> ring[kRing];
   const int page0 = pstart + wave;
   const int cnt = (has_work && page0 < pend) ? (pend - page0 + kWaves - 1) / kWaves : 0;
   int32_t next_id = 0;
   int q_row;
   if (has_work) {
-    issue_page<F>(ring0, p, first_id(0), g, lane);
+    issue_page<F>(ring[0], p, first_id(0), g, lane);
     __builtin_amdgcn_sched_barrier(0);  // the first page goes out before the row-offset sum
     q_row = __builtin_amdgcn_readfirstlane(wave_sum_i32(qsum));
     const int qh = (threadIdx.x >> 4) % G, qc = threadIdx.x & 15;
     const u32x4_t qchunk =
         reinterpret_cast<const u32x4_t*>(p.q)[((size_t)q_row * p.num_q_heads + h0 + qh) * 16 + qc];
     issue_order_barrier();
-    issue_page<F>(ring1, p, first_id(1), g, lane);
-    issue_page<F>(ring2, p, first_id(2), g, lane);
-    next_id = first_id(3);
+#pragma unroll
+    for (int r = 1; r < kRing; ++r) issue_page<F>(ring[r], p, first_id(r), g, lane);
+    next_id = first_id(kRing);
     // Query of heads h0 .. h0+G-1 -> LDS, 16-byte chunk c of head h at slot c ^ h.
     if (threadIdx.x < G * 16) *reinterpret_cast<u32x4_t*>(&s_q[qh][(qc ^ qh) << 4]) = qchunk;
     __syncthreads();
@@ -418,15 +447,16 @@ __global__ __launch_bounds__(kDecodeThreads, kDecodeWGsPerCU) void decode_kernel
     st.l_lane = 0.f;
 #pragma unroll
     for (int bb = 0; bb < 8; ++bb) st.o[bb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    // Q^T operand from the staged query (head h keeps chunk c at slot c ^ h);
-    // columns past G get a zero query.
+    // Q^T operand from the staged query (head h keeps chunk c at slot c ^ h):
+    // column n < 2G holds query head n % G (the second copy carries the lo
+    // weights of PV); columns from 2G on get a zero query.
     {
       const int qn = lane & 15, qr = lane >> 4;
-      const int qh = min(qn, G - 1);
+      const int qh = qn & (G - 1);
 #pragma unroll
       for (int sg = 0; sg < 4; ++sg) {
         const u32x4_t x = *reinterpret_cast<const u32x4_t*>(&s_q[qh][((4 * sg + qr) ^ qh) << 4]);
-        st.qb[sg] = qn < G ? x : u32x4_t{0u, 0u, 0u, 0u};
+        st.qb[sg] = qn < 2 * G ? x : u32x4_t{0u, 0u, 0u, 0u};
       }
     }
 
@@ -434,10 +464,11 @@ __global__ __launch_bounds__(kDecodeThreads, kDecodeWGsPerCU) void decode_kernel
     uint8_t* sv = s_v[wave];
     float* sks = s_ks[wave];
     float* svs = s_vs[wave];
-    // This wave's pages are page0 + 4k for k < cnt; page k lives in ring k % 3.
-    // The main loop reissues unconditionally, so the (in-order) load counter
-    // sees the same pattern on every trip and each wait leaves the other two
-    // pages in flight; the last pages are peeled off.
+    // This wave's pages are page0 + 4k for k < cnt; page k lives in ring
+    // slot k % kRing.  The main loop reissues unconditionally, so the
+    // (in-order) load counter sees the same pattern on every trip and each
+    // wait leaves the other kRing - 1 pages in flight; the last pages are
+    // peeled off.
     auto valid_of = [&](int k) { return min(kBlockSize, n - (page0 + kWaves * k) * kBlockSize); };
 #define PA_CONSUME(RING, K) consume_page<G, F>(st, RING, sk, sv, sks, svs, valid_of(K), p.scale_log2, lane)
 #define PA_REISSUE(RING, K)                                          \
@@ -446,38 +477,42 @@ __global__ __launch_bounds__(kDecodeThreads, kDecodeWGsPerCU) void decode_kernel
     next_id = page_id(page0 + kWaves * ((K) + 1));                   \
   }
     int k = 0;
-    for (; k + 5 < cnt; k += 3) {
-      PA_CONSUME(ring0, k);
-      PA_REISSUE(ring0, k + 3);
-      PA_CONSUME(ring1, k + 1);
-      PA_REISSUE(ring1, k + 4);
-      PA_CONSUME(ring2, k + 2);
-      PA_REISSUE(ring2, k + 5);
-    }
-    // At most five pages left: k, k+1, k+2 in rings 0, 1, 2 (if they exist);
-    // k+3 and k+4 still to be issued into rings 0 and 1.
-    if (k < cnt) {
-      PA_CONSUME(ring0, k);
-      if (k + 3 < cnt) PA_REISSUE(ring0, k + 3);
-      if (k + 1 < cnt) {
-        PA_CONSUME(ring1, k + 1);
-        if (k + 4 < cnt) PA_REISSUE(ring1, k + 4);
+    for (; k + 2 * kRing - 1 < cnt; k += kRing) {
+#pragma unroll
+      for (int r = 0; r < kRing; ++r) {
+        PA_CONSUME(ring[r], k + r);
+        PA_REISSUE(ring[r], k + r + kRing);
       }
-      if (k + 2 < cnt) PA_CONSUME(ring2, k + 2);
-      if (k + 3 < cnt) PA_CONSUME(ring0, k + 3);
-      if (k + 4 < cnt) PA_CONSUME(ring1, k + 4);
     }
+    // At most 2 kRing - 1 pages left: k .. k + kRing - 1 in the ring (those
+    // that exist), the rest still to be issued.
+#pragma unroll
+    for (int r = 0; r < kRing; ++r) {
+      if (k + r < cnt) {
+        PA_CONSUME(ring[r], k + r);
+        if (k + r + kRing < cnt) PA_REISSUE(ring[r], k + r + kRing);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < kRing - 1; ++r)
+      if (k + kRing + r < cnt) PA_CONSUME(ring[r], k + kRing + r);
 #undef PA_CONSUME
 #undef PA_REISSUE
 
     // Per-wave state -> LDS.  Column pc's sum is spread over lanes pc + 16 j;
-    // its O^T block values are dims 16 b + 4 pr + i.  FP8's V scale applies
-    // here, once.
+    // its O^T block values are dims 16 b + 4 pr + i, to which the lo column
+    // pc + G (lane ^ G, since pc < G and G is a power of two) is added.
+    // FP8's V scale applies here, once.
     const int pr = lane >> 4;
     const int pc = lane & 15;
     float l_sum = st.l_lane + other16(st.l_lane);
     l_sum += other_half(l_sum);
     const float vs = F == kFmtFP8 ? p.v_scale : 1.f;
+    f32x4_t o_tot[8];
+#pragma unroll
+    for (int bb = 0; bb < 8; ++bb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o_tot[bb][i] = st.o[bb][i] + __shfl_xor(st.o[bb][i], G, 64);
     if (pc < G) {
       if (pr == 0) {
         s_m[wave][pc] = st.m_ref;
@@ -485,7 +520,7 @@ __global__ __launch_bounds__(kDecodeThreads, kDecodeWGsPerCU) void decode_kernel
       }
 #pragma unroll
       for (int bb = 0; bb < 8; ++bb)
-        *reinterpret_cast<f32x4_t*>(&s_acc[wave][pc][16 * bb + 4 * pr]) = st.o[bb] * vs;
+        *reinterpret_cast<f32x4_t*>(&s_acc[wave][pc][16 * bb + 4 * pr]) = o_tot[bb] * vs;
     }
     __syncthreads();
 
@@ -536,11 +571,21 @@ __global__ __launch_bounds__(kDecodeThreads, kDecodeWGsPerCU) void decode_kernel
 
   // Split: publish this partition's partial, count it, and let the last
   // partition of the (slot, KV head) to finish merge them all.  The partials
-  // and the counter are exchanged with relaxed device-scope atomics, which
-  // the compiler emits as cache-coherent (sc1) loads and stores; each thread
-  // waits for its partial stores to complete before the workgroup bumps the
-  // counter.  This avoids device-scope fences, which on this chip write back
-  // and invalidate the whole L2 of the XCD.
+  // and the counter are exchanged with relaxed device-scope atomics; the
+  // ordering that makes the merger see every partial is the hardware's, in
+  // this order (a CPU test checks it on the gfx950 assembly):
+  //   1. each thread's partial stores are device-scope (sc1): written through
+  //      to the point of coherence that every XCD reads;
+  //   2. s_waitcnt vmcnt(0): the stores are acknowledged there (on gfx9 the
+  //      vector-memory counter also counts stores);
+  //   3. s_barrier: every thread of the workgroup has passed step 2;
+  //   4. one thread's counter atomic, whose returned value decides, through
+  //      LDS and a second barrier, whether this workgroup merges;
+  //   5. the merger's loads are device-scope (sc1) and issued after that
+  //      decision, so each reads the point of coherence after every other
+  //      partition's step 2.
+  // This avoids device-scope release/acquire fences, which on this chip
+  // write back and invalidate the whole L2 of the XCD.
   uint64_t* part_out64 = reinterpret_cast<uint64_t*>(p.part_out);
   if (my_out) {
     const size_t prow = (size_t)part * rows + (size_t)q_row * p.num_q_heads + h0 + my_h;

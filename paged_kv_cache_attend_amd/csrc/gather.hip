@@ -63,6 +63,9 @@ __global__ __launch_bounds__(256) void validate_kernel(ValidateParams p) {
       if (b < 0 || (int64_t)b >= p.num_blocks) bits |= PA_BAD_BLOCK_ID;
     }
   }
+  // Split-KV counters: every call that completes leaves them at zero.
+  for (int i = threadIdx.x; i < p.num_counters; i += blockDim.x)
+    if (p.counters[i] != 0) bits |= PA_BAD_WORKSPACE;
   if (bits) atomicOr(&s_bits, bits);
   if (total) atomicAdd(reinterpret_cast<unsigned long long*>(&s_total), (unsigned long long)total);
   __syncthreads();

@@ -106,6 +106,8 @@ struct ValidateParams {
   const int32_t* block_table;
   const int32_t* ctx_lens;
   const int32_t* q_lens;
+  const int32_t* counters;    // split-KV counters to check for zero, or null
+  int32_t num_counters;
   int32_t* error_word;
   int64_t num_blocks;
   int32_t num_seqs;

@@ -193,7 +193,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_kernel(PrefixParams p) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) o[mb][i] = 0.f;
   float m_run = -INFINITY;
-  float l_run = 0.f;
+  float l_run = 0.f;  // this lane's share of the row sum (fp32 weights)
+  float r_run = 0.f;  // the same over the bf16-rounded weights PV uses
 
   // Tile t of the partition (keys key0 + 32 t ..): S^T = K Q^T, online
   // softmax, O^T += V^T P^T.
@@ -230,6 +231,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_kernel(PrefixParams p) {
       const float m_new = fmaxf(m_run, mloc);
       const float alpha = fast_exp2(m_run - ((m_new == -INFINITY) ? 0.f : m_new));
       l_run *= alpha;
+      r_run *= alpha;
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
@@ -245,15 +247,20 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_kernel(PrefixParams p) {
     }
     l_run += lsum;
     // P^T operand for key steps 0 and 1: keys 16 ks + 4 hh + 0..3 and
-    // 16 ks + 8 + 4 hh + 0..3.
+    // 16 ks + 8 + 4 hh + 0..3.  The output is normalised by the sum of these
+    // rounded weights, the LSE by the sum of the fp32 ones.
     u32x4_t pf[2];
+    float rsum = 0.f;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       pf[ks][0] = pack_bf16x2(sv[8 * ks + 0], sv[8 * ks + 1]);
       pf[ks][1] = pack_bf16x2(sv[8 * ks + 2], sv[8 * ks + 3]);
       pf[ks][2] = pack_bf16x2(sv[8 * ks + 4], sv[8 * ks + 5]);
       pf[ks][3] = pack_bf16x2(sv[8 * ks + 6], sv[8 * ks + 7]);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) rsum += bf16_lo(pf[ks][w]) + bf16_hi(pf[ks][w]);
     }
+    r_run += rsum;
     // V^T operand (lane: dim 32 mb + l % 32, the same keys) from the
     // row-major V tile through transposing reads: in each 16-lane group, lane
     // a points at 4 dims of key a / 4 and lane i receives dim i of the four
@@ -293,10 +300,10 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_kernel(PrefixParams p) {
   // floats][lane]: 16-byte accesses by consecutive lanes.
   constexpr int kSlot = 4 * 64;  // float4s per (block, row group, quarter)
   float4* xacc = reinterpret_cast<float4*>(&s_buf[0][0][0]);
-  float2* xml = reinterpret_cast<float2*>(xacc + 4 * 2 * 3 * kSlot);  // [row group][quarter][lane]: (m, l)
-  static_assert(4 * 2 * 3 * kSlot * sizeof(float4) + 2 * 4 * 64 * sizeof(float2) <= sizeof(s_buf),
+  float4* xml = xacc + 4 * 2 * 3 * kSlot;  // [row group][quarter][lane]: (m, l, rounded l)
+  static_assert(4 * 2 * 3 * kSlot * sizeof(float4) + 2 * 4 * 64 * sizeof(float4) <= sizeof(s_buf),
                 "merge buffer exceeds the tile area");
-  xml[(rg * 4 + kq) * 64 + lane] = make_float2(m_run, l_run);
+  xml[(rg * 4 + kq) * 64 + lane] = make_float4(m_run, l_run, r_run, 0.f);
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb) {
     if (mb == kq) continue;
@@ -309,7 +316,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_kernel(PrefixParams p) {
   if (!row_live) return;  // both lanes of a row leave together
 
   float M = -INFINITY;
-  float2 ml[4];
+  float4 ml[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     ml[q] = xml[(rg * 4 + q) * 64 + lane];
@@ -317,17 +324,19 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_kernel(PrefixParams p) {
   }
   const float Mu = (M == -INFINITY) ? 0.f : M;
   float aw[4];
-  float l = 0.f;
+  float l = 0.f, lr = 0.f;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     aw[q] = fast_exp2(ml[q].x - Mu);
     l = fmaf(ml[q].y, aw[q], l);
+    lr = fmaf(ml[q].z, aw[q], lr);
   }
   const float l_tot = l + __shfl_xor(l, 32, 64);
+  const float r_tot = lr + __shfl_xor(lr, 32, 64);
   const size_t rows = (size_t)p.total_q * p.num_q_heads;
   if (kq == 0 && hh == 0) p.pre_lse[(size_t)part * rows + grow] = l_tot > 0.f ? (M + fast_log2(l_tot)) * kLn2 : -INFINITY;
   if (l_tot == 0.f) return;  // no visible key in this partition: the output is never read
-  const float inv = 1.f / l_tot;
+  const float inv = 1.f / r_tot;
   float* orow = p.pre_out + ((size_t)part * rows + grow) * kHeadDim;
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb) {

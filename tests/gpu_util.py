@@ -15,20 +15,27 @@ from paged_kv_cache_attend_amd import inputs
 DEV = torch.device("cuda:0")
 
 # Tolerances on the output and the LSE (natural log), from the accuracy
-# budget of bf16 storage with fp32 accumulation: half a bf16 ulp at |o| < 2 is
-# at most 2^-8 ~ 0.004, inside the max bound; the mean stays near 2^-10.
-# Where the exact output itself is 2 or more in magnitude, its bf16 spacing
-# alone reaches the bound (half an ulp is 0.0078 on [2, 4), 0.0156 on
-# [4, 8)), so there the max bound scales with it: TOL_MAX * |o| / 2, a 0.5 %
-# relative bound (half an ulp is at most 0.39 % of |o|).
+# budget of bf16 storage with fp32 accumulation: the benchmark spec-style absolute
+# bounds, max |dout| <= 1e-2, mean |dout| <= 1e-3, max |dlse| <= 1e-3.  Below
+# |o| = 4 half a bf16 ulp of the output is at most 2^-8 ~ 0.0039 and the max
+# bound is the absolute 1e-2.  From |o| = 4 on, half an ulp alone is 2^-6 =
+# 0.0156 or more, above 1e-2 before any arithmetic, so there the bound is that
+# half ulp plus the same 1e-2 as the margin for the arithmetic.
 TOL_MAX = 1e-2
 TOL_MEAN = 1e-3
 TOL_LSE = 1e-3
 
 
+def half_ulp_bf16(x: np.ndarray) -> np.ndarray:
+    """Half the bf16 spacing at |x| (8 significant bits): 2^(floor(log2|x|) - 8)."""
+    a = np.maximum(np.abs(np.asarray(x, dtype=np.float64)), np.finfo(np.float64).tiny)
+    return np.exp2(np.floor(np.log2(a)) - 8.0)
+
+
 def out_bound(exact: np.ndarray) -> np.ndarray:
     """Per-element bound on |out - exact| for exact outputs `exact`."""
-    return TOL_MAX * np.maximum(1.0, np.abs(exact) / 2.0)
+    a = np.abs(exact)
+    return np.where(a < 4.0, TOL_MAX, half_ulp_bf16(a) + TOL_MAX)
 
 OUT_SENTINEL = 0x7F81         # a bf16 NaN pattern no kernel produces
 LSE_SENTINEL = 0x7FC12345     # an fp32 NaN pattern no kernel produces
@@ -85,11 +92,15 @@ def compare(problem, gpu, ref, *, label=""):
     emax = float(err.max()) if err.size else 0.0
     emean = float(err.mean()) if err.size else 0.0
     ratio = float((err / out_bound(out[written])).max()) if err.size else 0.0
-    assert ratio <= 1.0, f"{label}: max |dout| {emax:.3e} ({ratio:.3f} of its bound)"
-    assert emean <= TOL_MEAN, f"{label}: mean |dout| {emean:.3e}"
+    lmax = None
     if lb is not None:
         el = np.abs(lb[written].astype(np.float64) - lse[written])
         lmax = float(el.max()) if el.size else 0.0
+    say(f"  {label}: max |dout| {emax:.3e} ({ratio:.3f} of its bound), mean |dout| {emean:.3e}, "
+        f"max |dlse| {lmax if lmax is None else f'{lmax:.3e}'}")
+    assert ratio <= 1.0, f"{label}: max |dout| {emax:.3e} ({ratio:.3f} of its bound)"
+    assert emean <= TOL_MEAN, f"{label}: mean |dout| {emean:.3e}"
+    if lb is not None:
         assert lmax <= TOL_LSE, f"{label}: max |dlse| {lmax:.3e}"
         assert (lb[~written].view(np.uint32) == np.uint32(LSE_SENTINEL)).all(), f"{label}: lse of an inactive row written"
     assert (ob[~written] == OUT_SENTINEL).all(), f"{label}: out of an inactive row written"

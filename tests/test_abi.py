@@ -210,9 +210,21 @@ def test_gather_and_validate_argument_checks(lib):
     s = _shape()
     assert lib.pa_gather_kv(ctypes.byref(s), None, FAKE, FAKE, FAKE, None) == pk.Status.ERR_NULL_ARG
     assert lib.pa_gather_kv(None, FAKE, FAKE, FAKE, FAKE, None) == pk.Status.ERR_NULL_ARG
-    assert lib.pa_validate(ctypes.byref(s), FAKE, FAKE, FAKE, None, None) == pk.Status.ERR_NULL_ARG
+    assert lib.pa_validate(ctypes.byref(s), FAKE, FAKE, FAKE, None, 0, None, None) == pk.Status.ERR_NULL_ARG
     bad = _shape(head_dim=96)
     assert lib.pa_gather_kv(ctypes.byref(bad), FAKE, FAKE, FAKE, FAKE, None) == pk.Status.ERR_UNSUPPORTED
+
+
+def test_validate_workspace_counter_region_checked_on_host(lib):
+    # 4 slots x 8 KV heads with a split: 32 counters (128 bytes) at the
+    # workspace start.  A workspace too small for them is rejected before any
+    # launch; NULL skips the counter check (and, here, fails on the NULL word).
+    s = _shape(max_ctx_len=160, partition_size=16)
+    assert pk.workspace_size(s) > 0
+    assert lib.pa_validate(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, 127, FAKE, None) \
+        == pk.Status.ERR_WORKSPACE_TOO_SMALL
+    assert lib.pa_validate(ctypes.byref(s), FAKE, FAKE, FAKE, None, 0, None, None) == pk.Status.ERR_NULL_ARG
+    assert _lib.PA_BAD_WORKSPACE == 0x10
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

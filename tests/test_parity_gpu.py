@@ -1,8 +1,9 @@
 """GPU parity: the HIP path (through the C ABI) against the FP64 oracle.
 
-Tolerances: output max |d| <= 1e-2 (scaled by |o| / 2 where the exact output
-is 2 or more in magnitude: its bf16 spacing alone reaches 1e-2 there), mean
-|d| <= 1e-3, LSE max |d| <= 1e-3 on every written row; rows of inactive slots keep their sentinel bytes exactly.
+Tolerances: output max |d| <= 1e-2 (where the exact output is 4 or more in
+magnitude, half its bf16 spacing plus 1e-2: half an ulp alone exceeds 1e-2
+there), mean |d| <= 1e-3, LSE max |d| <= 1e-3 on every written row; rows of
+inactive slots keep their sentinel bytes exactly.
 Bit-exact checks: page gather, page placement, shared-versus-copied prefix,
 single-key output, repeat determinism.
 """
@@ -17,7 +18,8 @@ import oracle
 import paged_kv_cache_attend_amd as pk
 from paged_kv_cache_attend_amd import inputs
 
-from gpu_util import DEV, LSE_SENTINEL, OUT_SENTINEL, bf16_to_f64, compare, run_gpu, run_oracle, say
+from gpu_util import (DEV, LSE_SENTINEL, OUT_SENTINEL, TOL_MEAN, bf16_to_f64, compare, out_bound, run_gpu,
+                      run_oracle, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -338,7 +340,10 @@ def test_combine_matches_oracle_merge():
     lb = lse.cpu().numpy()
     o = bf16_to_f64(ob)
     assert not touched[5] and (ob[5] == OUT_SENTINEL).all() and lb[5:6].view(np.uint32)[0] == LSE_SENTINEL
-    assert np.abs(o[touched] - ref_o[touched]).max() <= 2e-2
+    err = np.abs(o[touched] - ref_o[touched])
+    say(f"combine: max |dout| {err.max():.3e}, mean {err.mean():.3e}")
+    assert (err <= out_bound(ref_o[touched])).all(), float((err / out_bound(ref_o[touched])).max())
+    assert err.mean() <= TOL_MEAN
     assert np.abs(lb[touched] - ref_l[touched]).max() <= 1e-4
 
 
@@ -365,3 +370,61 @@ def test_validate_flags_bad_data():
     ql2 = ql.clone()
     ql2[0] = 40
     assert check(bt, cl, ql2, max_q_len=64, total_q=64) == pk._lib.PA_BAD_Q_LEN
+
+
+def test_validate_flags_unzeroed_workspace_counters():
+    # A split shape (3 slots x 2 KV heads, 16-token partitions): the counters
+    # are zero after pa_workspace_init and after a completed call, and a
+    # non-zero one (a workspace not initialised for the shape) is flagged.
+    p = _case([37, 100, 0], ql=[1, 1, 1], seed=59)
+    t = inputs.to_device(p, *p.layer(0), DEV)
+    kw = dict(num_blocks=p.num_blocks, total_q=p.total_q, max_q_len=1, max_ctx_len=p.max_ctx_len,
+              num_q_heads=p.num_q_heads, num_kv_heads=p.num_kv_heads, partition_size=16)
+    shape = pk.make_shape(p.num_seqs, p.total_q, p.num_q_heads, p.num_kv_heads, p.max_blocks_per_seq, 1,
+                          p.max_ctx_len, p.num_blocks, 16)
+    ws = torch.full((pk.workspace_size(shape),), 0x5A, dtype=torch.uint8, device=DEV)
+    word = torch.full((1,), -1, dtype=torch.int32, device=DEV)
+
+    def check():
+        pk.validate(t["block_table"], t["ctx_lens"], t["q_lens"], word, workspace=ws, **kw)
+        torch.cuda.synchronize()
+        return int(word.item())
+
+    assert check() == pk._lib.PA_BAD_WORKSPACE
+    pk.workspace_init(shape, ws)
+    assert check() == 0
+    out = torch.empty_like(t["q"])
+    pk.attend(t["q"], t["k"], t["v"], t["block_table"], t["ctx_lens"], t["q_lens"], float(p.scale), out,
+              max_q_len=1, max_ctx_len=p.max_ctx_len, partition_size=16, workspace=ws)
+    assert check() == 0
+    ws[:4].view(torch.int32).fill_(1)
+    assert check() == pk._lib.PA_BAD_WORKSPACE
+
+
+def test_binding_on_a_non_current_stream():
+    # attend() allocates its workspace from the launch stream's pool and zeroes
+    # its counters there; PreparedAttend zeroes on its construction stream
+    # and waits, so a launch on any other stream sees zeroed counters.
+    p = _case([300, 1000, 37, 2000], hq=32, hkv=8, seed=61)
+    ref = run_oracle(p)
+    t = inputs.to_device(p, *p.layer(0), DEV)
+    side = torch.cuda.Stream(device=DEV)
+    for _ in range(3):
+        out = torch.full(t["q"].shape, OUT_SENTINEL, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+        lse = torch.full(t["q"].shape[:2], LSE_SENTINEL, dtype=torch.int32, device=DEV).view(torch.float32)
+        torch.cuda.synchronize()
+        pk.attend(t["q"], t["k"], t["v"], t["block_table"], t["ctx_lens"], t["q_lens"], float(p.scale), out, lse,
+                  max_q_len=1, max_ctx_len=p.max_ctx_len, partition_size=64, stream=side)
+        side.synchronize()
+        compare(p, (out.view(torch.int16).cpu().numpy().view(np.uint16), lse.cpu().numpy()), ref,
+                label="attend on a side stream")
+    out = torch.full(t["q"].shape, OUT_SENTINEL, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+    lse = torch.full(t["q"].shape[:2], LSE_SENTINEL, dtype=torch.int32, device=DEV).view(torch.float32)
+    torch.cuda.synchronize()
+    call = pk.PreparedAttend(t["q"], t["k"], t["v"], t["block_table"], t["ctx_lens"], t["q_lens"],
+                             float(p.scale), out, lse, max_q_len=1, max_ctx_len=p.max_ctx_len, partition_size=64)
+    assert call.num_partitions > 1
+    call.launch(side)
+    side.synchronize()
+    compare(p, (out.view(torch.int16).cpu().numpy().view(np.uint16), lse.cpu().numpy()), ref,
+            label="prepared call launched on a side stream")

@@ -143,7 +143,8 @@ def test_prefix_full_size_shared_prefix_decode():
     assert np.abs(lb[rows] - lse[rows]).max() <= 1e-3
     base = run_gpu(p)
     d = np.abs(inputs_bf16(ob) - inputs_bf16(base[0]))
-    assert d.max() <= 2e-2 and d.mean() <= 2e-3, (d.max(), d.mean())
+    # two results each within out_bound of the exact one
+    assert (d <= 2 * out_bound(inputs_bf16(base[0]))).all() and d.mean() <= 2e-3, (d.max(), d.mean())
     assert np.abs(lb - base[1]).max() <= 2e-3
 
 
