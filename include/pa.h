@@ -79,7 +79,9 @@ typedef enum pa_status {
   PA_ERR_UNSUPPORTED = 3,         /* valid but not implemented (e.g. head_dim != 128) */
   PA_ERR_WORKSPACE_TOO_SMALL = 4, /* workspace_bytes < pa_workspace_size() */
   PA_ERR_LAUNCH = 5,              /* the HIP runtime rejected a kernel launch */
-  PA_ERR_OUT_OF_BLOCKS = 6        /* the block pool has too few free blocks; nothing changed */
+  PA_ERR_OUT_OF_BLOCKS = 6,       /* the block pool has too few free blocks; nothing changed */
+  PA_ERR_SCRATCH_LIMIT = 7        /* pa_attend_noalloc: the call needs more scratch than
+                                     PA_NOALLOC_SCRATCH_BYTES; nothing launched */
 } pa_status;
 
 /* Request rows may only see keys up to their own position (chunked prefill,
@@ -427,6 +429,32 @@ pa_status pa_pool_get_stats(const pa_pool* pool, pa_pool_stats* stats);
 
 /* Static, NUL-terminated description of a status code. */
 const char* pa_status_string(pa_status status);
+
+/* ------------------------------------------------------------------------
+ * pa_attend without a caller workspace
+ * ------------------------------------------------------------------------
+ * For callers that cannot allocate device memory or pass a workspace: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments, result, errors and kernels as pa_attend, minus
+ * the workspace: the split-KV counters and partials live in a buffer built
+ * into the library, PA_NOALLOC_SCRATCH_BYTES of device memory on every GPU
+ * the library runs on, held until the process ends.  A call whose shape
+ * needs more (pa_workspace_size(shape) > PA_NOALLOC_SCRATCH_BYTES) returns
+ * PA_ERR_SCRATCH_LIMIT and launches nothing.  Nothing here allocates: the
+ * first call on a device looks up that device's copy of the buffer and
+ * enqueues a kernel that zeroes its counters; every later call finds them
+ * zero again, since each completed call leaves them so.
+ * The device is the current one (hipGetDevice), and `stream` must belong to
+ * it.  All calls on one GPU share the buffer: two calls that can run at the
+ * same time on one GPU (different streams, overlapping graph launches) race
+ * on it and give wrong results; order them on one stream.  Errors as for
+ * pa_attend, plus PA_ERR_SCRATCH_LIMIT, and PA_ERR_LAUNCH when the buffer's
+ * address cannot be obtained. */
+#define PA_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+pa_status pa_attend_noalloc(const pa_shape* shape, const void* q, const void* k_cache,
+                            const void* v_cache, const int32_t* block_table,
+                            const int32_t* ctx_lens, const int32_t* q_lens, float scale,
+                            void* out, float* lse, void* stream);
 
 #ifdef __cplusplus
 }

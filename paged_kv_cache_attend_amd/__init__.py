@@ -12,7 +12,8 @@ _BINDING = ("PaError", "Shape", "Status", "attend", "combine", "gather_kv", "val
             "lib_path", "load", "make_shape", "plan", "status_string", "workspace_size",
             "EXPORTS", "PreparedAttend", "workspace_init", "write_kv", "copy_blocks", "Pool",
             "PoolStats", "KVCache", "QuantCache", "attend_kv", "write_kv_cache", "KV_BF16",
-            "KV_FP8_E4M3", "KV_Q8_0", "KV_Q4_0", "PrefixGroups", "attend_prefix")
+            "KV_FP8_E4M3", "KV_Q8_0", "KV_Q4_0", "PrefixGroups", "attend_prefix", "attend_noalloc",
+            "NOALLOC_SCRATCH_BYTES")
 
 
 def __getattr__(name):

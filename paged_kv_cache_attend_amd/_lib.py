@@ -28,7 +28,9 @@ EXPORTS = ("pa_workspace_size", "pa_workspace_init", "pa_num_partitions", "pa_at
            "pa_pool_destroy", "pa_pool_append", "pa_pool_fork", "pa_pool_release", "pa_pool_retire",
            "pa_pool_length", "pa_pool_block_table", "pa_pool_refcount", "pa_pool_get_stats",
            "pa_attend_kv", "pa_write_kv_cache", "pa_num_partitions_kv", "pa_prefix_workspace_size",
-           "pa_prefix_workspace_init", "pa_attend_prefix", "pa_status_string")
+           "pa_prefix_workspace_init", "pa_attend_prefix", "pa_attend_noalloc", "pa_status_string")
+
+NOALLOC_SCRATCH_BYTES = 32 << 20   # PA_NOALLOC_SCRATCH_BYTES
 
 # pa_kv_format
 KV_BF16 = 0
@@ -45,6 +47,7 @@ class Status(enum.IntEnum):
     ERR_WORKSPACE_TOO_SMALL = 4
     ERR_LAUNCH = 5
     ERR_OUT_OF_BLOCKS = 6
+    ERR_SCRATCH_LIMIT = 7
 
 
 class PaError(RuntimeError):
@@ -145,6 +148,8 @@ def load():
     lib.pa_num_partitions_kv.restype = ctypes.c_int32
     lib.pa_attend.argtypes = [shp, P, P, P, P, P, P, ctypes.c_float, P, P, P, ctypes.c_size_t, P]
     lib.pa_attend.restype = ctypes.c_int
+    lib.pa_attend_noalloc.argtypes = [shp, P, P, P, P, P, P, ctypes.c_float, P, P, P]
+    lib.pa_attend_noalloc.restype = ctypes.c_int
     lib.pa_combine.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P, P, P, P, P]
     lib.pa_combine.restype = ctypes.c_int
     lib.pa_gather_kv.argtypes = [shp, P, P, P, P, P]
@@ -328,6 +333,41 @@ def attend(q, k_cache, v_cache, block_table, ctx_lens, q_lens, scale, out, lse=N
                           _ptr(ctx_lens), _ptr(q_lens), ctypes.c_float(float(scale)), _ptr(out), _ptr(lse),
                           _ptr(workspace), ctypes.c_size_t(ws_bytes), _stream_handle(dev, stream))
     _check(st, "pa_attend")
+    return out, lse
+
+
+def attend_noalloc(q, k_cache, v_cache, block_table, ctx_lens, q_lens, scale, out, lse=None, *,
+                   max_q_len: int, max_ctx_len: int, partition_size: int = 0, causal: bool = False,
+                   stream=None):
+    """``pa_attend_noalloc``: ``attend`` without a workspace; the library's
+    built-in scratch buffer holds the split-KV partials (no allocation here
+    or in the library)."""
+    torch = _torch()
+    dev = q.device
+    _need(q, "q", torch.bfloat16, dev, 3)
+    _need(out, "out", torch.bfloat16, dev, 3)
+    _need(k_cache, "k_cache", torch.bfloat16, dev, 4)
+    _need(v_cache, "v_cache", torch.bfloat16, dev, 4)
+    _need(block_table, "block_table", torch.int32, dev, 2)
+    _need(ctx_lens, "ctx_lens", torch.int32, dev, 1)
+    _need(q_lens, "q_lens", torch.int32, dev, 1)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, dev, 2)
+    total_q, hq, d = q.shape
+    nb, hkv, bs, d2 = k_cache.shape
+    if tuple(out.shape) != tuple(q.shape) or tuple(v_cache.shape) != tuple(k_cache.shape) or d2 != d:
+        raise ValueError("shape mismatch between q/out or k_cache/v_cache")
+    if lse is not None and tuple(lse.shape) != (total_q, hq):
+        raise ValueError("lse must be [total_q, Hq]")
+    num_seqs = block_table.shape[0]
+    if ctx_lens.shape[0] != num_seqs or q_lens.shape[0] != num_seqs:
+        raise ValueError("ctx_lens / q_lens must have one entry per block-table row")
+    shape = make_shape(num_seqs, total_q, hq, hkv, block_table.shape[1], max_q_len, max_ctx_len,
+                       nb, partition_size, causal, head_dim=d, block_size=bs)
+    st = load().pa_attend_noalloc(ctypes.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+                                  _ptr(ctx_lens), _ptr(q_lens), ctypes.c_float(float(scale)), _ptr(out),
+                                  _ptr(lse), _stream_handle(dev, stream))
+    _check(st, "pa_attend_noalloc")
     return out, lse
 
 

@@ -21,7 +21,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpa.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["api.cpp", "pool.cpp", "decode.hip", "combine.hip", "chunk.hip", "gather.hip", "write.hip", "prefix.hip"]
+SOURCES = ["api.cpp", "pool.cpp", "decode.hip", "combine.hip", "chunk.hip", "gather.hip", "write.hip", "prefix.hip",
+           "noalloc.hip"]
 
 COMMON = [
     "--offload-arch=gfx950",

@@ -307,6 +307,24 @@ pa_status make_prefix_plan(const pa_shape* s, const pa_prefix_groups* gr, Prefix
 
 }  // namespace
 
+namespace pa {
+
+// pa_attend with the workspace given by the caller of this function (the
+// library's own scratch buffer, for pa_attend_noalloc).
+pa_status attend_bf16(const pa_shape* shape, const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_table, const int32_t* ctx_lens, const int32_t* q_lens,
+                      float scale, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  pa_kv_cache kv = {};
+  kv.format = kFmtBF16;
+  kv.k_codes = const_cast<void*>(k_cache);
+  kv.v_codes = const_cast<void*>(v_cache);
+  return attend_impl(shape, kv, q, block_table, ctx_lens, q_lens, scale, out, lse, workspace,
+                     workspace_bytes, stream);
+}
+
+}  // namespace pa
+
 extern "C" {
 
 size_t pa_workspace_size(const pa_shape* shape) {
@@ -613,6 +631,7 @@ const char* pa_status_string(pa_status status) {
     case PA_ERR_WORKSPACE_TOO_SMALL: return "workspace smaller than pa_workspace_size()";
     case PA_ERR_LAUNCH: return "kernel launch failed";
     case PA_ERR_OUT_OF_BLOCKS: return "the block pool has too few free blocks";
+    case PA_ERR_SCRATCH_LIMIT: return "the call needs more scratch than pa_attend_noalloc's built-in buffer";
   }
   return "unknown status";
 }

@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "pa.h"
+
 namespace pa {
 
 constexpr int kHeadDim = 128;    // only head size built
@@ -196,5 +198,11 @@ hipError_t launch_copy_blocks(const CopyParams& p, hipStream_t s);
 hipError_t launch_write_kv_quant(const WriteQuantParams& p, int format, hipStream_t s);
 hipError_t launch_prefix(const PrefixParams& p, unsigned grid, hipStream_t s);
 hipError_t launch_validate(const ValidateParams& p, hipStream_t s);
+
+// pa_attend on bf16 pages with an explicit workspace (api.cpp).
+pa_status attend_bf16(const pa_shape* shape, const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_table, const int32_t* ctx_lens, const int32_t* q_lens,
+                      float scale, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                      void* stream);
 
 }  // namespace pa
