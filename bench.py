@@ -47,11 +47,12 @@ def parse():
     ap.add_argument("--no-chunk", action="store_true", help="skip the secondary chunk-path measurement")
     ap.add_argument("--no-append", action="store_true", help="skip the secondary K/V-append measurement")
     ap.add_argument("--no-quant", action="store_true", help="skip the secondary quantised-KV decode measurement")
-    ap.add_argument("--no-prefix", action="store_true", help="skip the secondary prefix-grouped decode measurement")
+    ap.add_argument("--no-prefix", action="store_true", help="skip the shared-prefix workload (pa_attend and pa_attend_prefix)")
+    ap.add_argument("--no-ragged", action="store_true", help="skip the ragged mixed decode workload")
     ap.add_argument("--cpu-budget-s", type=float, default=25.0)
     ap.add_argument("--mode", choices=["bench", "copy"], default="bench",
                     help="copy: time a plain 1 GiB device copy (counter calibration for rocprofv3)")
-    ap.add_argument("--quick", action="store_true", help="skip the eager and per-launch re-timings")
+    ap.add_argument("--quick", action="store_true", help="skip the eager and per-launch re-timings and the ceilings")
     return ap.parse_args()
 
 
@@ -183,8 +184,11 @@ def prepare_calls(problem, layers, partition_size):
     return calls, outs, lses
 
 
-def time_pass(calls, steps, warmup, launch):
-    """Time `steps` passes; returns (ms per pass from events, wall ms per pass)."""
+def time_pass(calls, steps, warmup, launch, trials=5):
+    """Time `trials` runs of exactly `steps` passes each (a pass = every call
+    once, in order), each bracketed by a synchronisation on both sides.
+    Returns (median ms per pass, best ms per pass, wall ms per pass of the
+    median trial, per-trial ms list)."""
     import torch
     stream = torch.cuda.current_stream()
 
@@ -205,16 +209,22 @@ def time_pass(calls, steps, warmup, launch):
     for _ in range(warmup):
         run()
     torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    e0.record(stream)
-    for _ in range(steps):
-        run()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    wall = (time.perf_counter() - t0) * 1e3 / steps
-    return e0.elapsed_time(e1) / steps, wall, graph
+    per, walls = [], []
+    for _ in range(trials):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        e0.record(stream)
+        for _ in range(steps):
+            run()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        walls.append((time.perf_counter() - t0) * 1e3 / steps)
+        per.append(e0.elapsed_time(e1) / steps)
+    order = sorted(range(trials), key=lambda i: per[i])
+    med = order[trials // 2]
+    return per[med], per[order[0]], walls[med], per
 
 
 def time_kernel_launches(calls, reps):
@@ -257,7 +267,105 @@ def parity(problem, outs, lses, ref):
             "pass": bool(worst <= 1.0 and emean <= 1e-3 and lmax <= 1e-3)}
 
 
-def chunk_secondary(dev, steps, launch="graph"):
+def device_layers(problem, dev, num_layers, seed):
+    """Per-layer device tensors for a workload's structure, with values drawn
+    on the device (N(0, 1) rounded to bf16): for timing runs whose parity the
+    GPU tests check on the host-drawn inputs."""
+    import torch
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed)
+    bt = torch.from_numpy(problem.block_table.astype(np.int32)).to(dev)
+    cl = torch.from_numpy(problem.ctx_lens.astype(np.int32)).to(dev)
+    ql = torch.from_numpy(problem.q_lens.astype(np.int32)).to(dev)
+    hd = problem.head_dim
+    layers = []
+    for _ in range(num_layers):
+        shape = (problem.num_blocks, problem.num_kv_heads, problem.block_size, hd)
+        layers.append(dict(
+            q=torch.randn((problem.total_q, problem.num_q_heads, hd), generator=g, device=dev).bfloat16(),
+            k=torch.randn(shape, generator=g, device=dev).bfloat16(),
+            v=torch.randn(shape, generator=g, device=dev).bfloat16(),
+            block_table=bt, ctx_lens=cl, q_lens=ql))
+    return layers
+
+
+def hbm_roofline(bytes_per_launch, us, kernel, ceiling_gbs=None, **extra):
+    gbs = bytes_per_launch / (us * 1e-6) / 1e9
+    r = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+         "algorithmic_bytes_per_launch": bytes_per_launch, "avg_launch_us": us, "kernel": kernel}
+    if ceiling_gbs:
+        r["frac_of_measured_read_ceiling"] = gbs / ceiling_gbs
+    r.update(extra)
+    return r
+
+
+def read_ceiling(problem, layers, steps, launch):
+    """The measured streaming ceiling for a decode workload: the same K/V
+    tiles (each (slot, page, KV head) once) of every layer, read with the
+    decode kernel's loads and nothing else, one launch per layer as the
+    decode pass does; for 72 tiles per workgroup (the decode grid at two
+    partitions) and for finer grids.  GB/s over the same algorithmic bytes."""
+    import torch
+    import paged_kv_cache_attend_amd as pk
+    dev = layers[0]["k"].device
+    tl = []
+    hkv = problem.num_kv_heads
+    for r in range(problem.num_seqs):
+        n = int(problem.ctx_lens[r])
+        for j in range(-(-n // problem.block_size)):
+            phys = int(problem.block_table[r][j])
+            tl.extend(phys * hkv + g for g in range(hkv))
+    tiles = torch.tensor(tl, dtype=torch.int32, device=dev)
+    bytes_per_launch = len(tl) * 2 * problem.block_size * problem.head_dim * 2
+    res = {}
+    for tpw in (72, 36, 18):
+        sink = torch.zeros(-(-len(tl) // tpw), dtype=torch.int32, device=dev)
+
+        class _C:
+            def __init__(self, t):
+                self.t = t
+
+            def launch(self, s):
+                pk.measure_read_tiles(self.t["k"], self.t["v"], tiles, sink, tiles_per_wg=tpw, stream=s)
+
+        calls = [_C(t) for t in layers]
+        ms, best, _, _ = time_pass(calls, max(steps // 4, 20), 3, launch)
+        us = ms * 1e3 / len(calls)
+        res[f"tiles_per_workgroup_{tpw}"] = {"us_per_launch": us, "gbs": bytes_per_launch / (us * 1e-6) / 1e9}
+    best_gbs = max(v["gbs"] for v in res.values())
+    return {"gbs": best_gbs, "frac_of_hbm_peak": best_gbs / HBM_PEAK_GBS, "bytes_per_launch": bytes_per_launch,
+            "kernel": "pa_measure_read_tiles (same tiles and loads as the decode kernel, no arithmetic), "
+                      "one launch per layer in a graph", "variants": res}
+
+
+def mfma_ceiling():
+    """Measured bf16 matrix-core throughput (v_mfma_f32_32x32x16_bf16, four
+    independent chains per wave, 2 and 4 workgroups of 4 waves per CU)."""
+    import torch
+    import paged_kv_cache_attend_amd as pk
+    best = 0.0
+    res = {}
+    for wgs in (512, 1024):
+        sink = torch.zeros(wgs * 4, dtype=torch.float32, device="cuda:0")
+        iters = 4000
+        flop = pk.measure_mfma_bf16(wgs, iters, sink)  # warm-up
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(5):
+            pk.measure_mfma_bf16(wgs, iters, sink)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        tf = flop * 5 / (e0.elapsed_time(e1) * 1e-3) / 1e12
+        res[f"workgroups_{wgs}"] = tf
+        best = max(best, tf)
+    return {"tflops": best, "frac_of_spec": best / BF16_PEAK_TFLOPS,
+            "kernel": "pa_measure_mfma_bf16 (v_mfma_f32_32x32x16_bf16, 4 chains per wave)", "variants": res}
+
+
+def chunk_secondary(dev, steps, launch="graph", mfma_tflops=None):
     """TFLOP/s of the chunked-denoising workload (4 x 24 heads x 256 rows x 1024 keys)."""
     import torch
     import paged_kv_cache_attend_amd as pk
@@ -274,18 +382,30 @@ def chunk_secondary(dev, steps, launch="graph"):
                                       max_ctx_len=p.max_ctx_len))
     flops = 4 * int((p.q_lens.astype(np.int64) * p.ctx_lens).sum()) * p.num_q_heads * p.head_dim
     passes = max(steps, 640) // 16  # 16 launches per pass; ~20 ms of GPU time per figure
-    cold_ms, _, _ = time_pass(sets, passes, 10, launch)
+    cold_ms, cold_best, _, _ = time_pass(sets, passes, 10, launch)
     cold_ms /= len(sets)
-    warm_ms, _, _ = time_pass(sets[:1] * 16, passes, 10, launch)
+    cold_best /= len(sets)
+    warm_ms, warm_best, _, _ = time_pass(sets[:1] * 16, passes, 10, launch)
     warm_ms /= 16
+    warm_best /= 16
+    warm_tf = flops / (warm_ms * 1e-3) / 1e12
+    cold_tf = flops / (cold_ms * 1e-3) / 1e12
+    moved = 63012864  # q + K/V pages + out + lse of one call
+    roof = {"bound": "mfma", "achieved": warm_tf, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": warm_tf / BF16_PEAK_TFLOPS, "algorithmic_flops_per_launch": flops,
+            "avg_launch_us": warm_ms * 1e3, "kernel": "chunk_kernel (warm: inputs resident in the Infinity Cache)",
+            "traffic": None}
+    if mfma_tflops:
+        roof["measured_peak_tflops"] = mfma_tflops
+        roof["frac_of_measured_peak"] = warm_tf / mfma_tflops
     return {"workload": "chunked_denoise", "flop_per_call": flops,
-            "tflops_cold": flops / (cold_ms * 1e-3) / 1e12, "tflops_warm": flops / (warm_ms * 1e-3) / 1e12,
-            "ms_cold": cold_ms, "ms_warm": warm_ms,
-            "frac_of_bf16_peak_warm": flops / (warm_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+            "tflops_cold": cold_tf, "tflops_warm": warm_tf, "ms_cold": cold_ms, "ms_warm": warm_ms,
+            "ms_cold_best": cold_best, "ms_warm_best": warm_best,
+            "frac_of_bf16_peak_warm": warm_tf / BF16_PEAK_TFLOPS,
             # the call reads and writes 63,012,864 B: AI = 204.5 FLOP/B, so cold
             # it is capped at min(peak, AI x 8 TB/s) = 1,636 TFLOP/s
-            "frac_of_roofline_cold": flops / (cold_ms * 1e-3) / 1e12
-            / min(BF16_PEAK_TFLOPS, flops / 63012864 * HBM_PEAK_GBS / 1e3)}
+            "frac_of_roofline_cold": cold_tf / min(BF16_PEAK_TFLOPS, flops / moved * HBM_PEAK_GBS / 1e3),
+            "roofline": roof}
 
 
 class _WriteCall:
@@ -320,8 +440,8 @@ def append_secondary(dev, steps, launch="graph"):
     prefill = _WriteCall(kn, vn, table, ctx, ctx, kc, vc, int(p.ctx_lens.max()))
     decode = _WriteCall(kn[:p.num_seqs], vn[:p.num_seqs], table, ctx, ones, kc, vc, 1)
     reps = max(steps // 4, 20)
-    pre_ms, _, _ = time_pass([prefill], reps, 2, launch)
-    dec_ms, _, _ = time_pass([decode] * 36, reps, 2, launch)
+    pre_ms, _, _, _ = time_pass([prefill], reps, 2, launch)
+    dec_ms, _, _, _ = time_pass([decode] * 36, reps, 2, launch)
     moved = 4 * rows * hkv * d * 2  # K and V: read the new row, write the page slot
     return {"workload": "qwen3_8b_short_decode prompt and decode appends (one layer per call)",
             "prompt_rows": rows, "prompt_bytes_moved": moved, "prompt_us": pre_ms * 1e3,
@@ -333,9 +453,10 @@ def append_secondary(dev, steps, launch="graph"):
 
 def quant_secondary(dev, steps, launch, bf16_us_per_layer):
     """Decode of the Qwen3-8B-shaped batch (16 x 2303 keys, 32/8 heads) over
-    FP8, q8_0 and q4_0 pages: microseconds per layer, GB/s over the bytes the
-    format reads (codes + group scales), and the trade of section 8.4.2,
-    Delta T = Delta D / beta - T_c, against the bf16 time measured above."""
+    FP8, q8_0 and q4_0 pages, 36 distinct layers of random codes: microseconds
+    per layer, GB/s over the bytes the format reads (codes + group scales),
+    and the trade of section 8.4.2, Delta T = Delta D / beta - T_c, against the
+    bf16 time measured above."""
     import torch
     import paged_kv_cache_attend_amd as pk
     from paged_kv_cache_attend_amd import inputs
@@ -354,7 +475,7 @@ def quant_secondary(dev, steps, launch, bf16_us_per_layer):
     pk.workspace_init(shape, ws)
     tokens = int(p.ctx_lens.sum())
     bf16_bytes = tokens * hkv * 512
-    distinct = 12  # 12 distinct layers of pages (over 500 MB even for q4_0), cycled to 36 launches
+    distinct = 36
     res = {}
     for name, fmt, per_tok in (("fp8", pk.KV_FP8_E4M3, 256), ("q8_0", pk.KV_Q8_0, 272),
                                ("q4_0", pk.KV_Q4_0, 144)):
@@ -379,34 +500,35 @@ def quant_secondary(dev, steps, launch, bf16_us_per_layer):
             keep.append(c)
             calls.append(pk.attend_kv(q, c, table, ctx, ql, float(p.scale), out, lse, max_q_len=1,
                                       max_ctx_len=p.max_ctx_len, workspace=ws, prepared=True))
-        ms, _, _ = time_pass(calls * 3, max(steps // 4, 20), 3, launch)
-        us = ms * 1e3 / (3 * distinct)
+        ms, best, _, _ = time_pass(calls, max(steps // 4, 20), 3, launch)
+        us = ms * 1e3 / distinct
         moved = tokens * hkv * per_tok
         beta = bf16_bytes / (bf16_us_per_layer * 1e-6)          # bf16's achieved read rate
         saved_read_us = (bf16_bytes - moved) / beta * 1e6       # Delta D / beta
-        res[name] = {"us_per_layer": us, "bytes_per_layer": moved, "gbs": moved / (us * 1e-6) / 1e9,
-                     "frac_of_hbm_peak": moved / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+        res[name] = {"us_per_layer": us, "us_per_layer_best": best * 1e3 / distinct, "bytes_per_layer": moved,
+                     "gbs": moved / (us * 1e-6) / 1e9, "frac_of_hbm_peak": moved / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
                      "speedup_vs_bf16": bf16_us_per_layer / us,
                      "delta_T_us": bf16_us_per_layer - us, "delta_D_over_beta_us": saved_read_us,
-                     "T_c_us": saved_read_us - (bf16_us_per_layer - us)}
+                     "T_c_us": saved_read_us - (bf16_us_per_layer - us),
+                     "partitions": calls[0].num_partitions}
         del calls, keep
         torch.cuda.empty_cache()
-    res["workload"] = "qwen3_8b_short_decode, 12 distinct layers of random codes cycled to 36 launches"
+    res["workload"] = "qwen3_8b_short_decode, 36 distinct layers of random codes (drawn on the device)"
     res["parity"] = "against the FP64 oracle over decoded pages in the GPU tests"
     return res
 
 
-def prefix_secondary(dev, steps, launch="graph"):
-    """The shared-prefix batch (10 slots x 8447 keys, the first 6144 one
-    shared copy; 32/8 heads) through pa_attend and through prefix-grouped
-    decode, pa_attend_prefix: microseconds per layer each, and GB/s over the
-    distinct bytes a layer reads (the shared pages counted once)."""
+def shared_prefix_config(dev, steps, launch, ceiling_gbs=None):
+    """The shared-prefix long decode (10 slots x 8447 keys, the first 6144
+    one physical copy, 32/8 heads), 36 distinct layers, through pa_attend and
+    through prefix-grouped decode (pa_attend_prefix).  The headline figure is
+    GB/s over the distinct bytes a layer must read (shared pages once)."""
     import torch
     import paged_kv_cache_attend_amd as pk
     from paged_kv_cache_attend_amd import inputs
-    nl = 12  # 12 distinct layers (about 1.4 GB of pages), cycled to 36 launches
+    nl = 36
     p = inputs.qwen3_shared_prefix_decode(num_layers=nl)
-    layers = [inputs.to_device(p, *p.layer(l), dev) for l in range(nl)]
+    layers = device_layers(p, dev, nl, inputs.SEED_BASE + 3300)
     plen = p.shared_prefix_blocks * p.block_size
     gs = torch.tensor([0, p.num_seqs], dtype=torch.int32, device=dev)
     pl = torch.tensor([plen], dtype=torch.int32, device=dev)
@@ -426,19 +548,86 @@ def prefix_secondary(dev, steps, launch="graph"):
         ws_g = g.keep[-1]
         grouped.append(g)
     reps = max(steps // 4, 20)
-    b_ms, _, _ = time_pass(base * 3, reps, 3, launch)
-    g_ms, _, _ = time_pass(grouped * 3, reps, 3, launch)
-    b_us, g_us = b_ms * 1e3 / (3 * nl), g_ms * 1e3 / (3 * nl)
+    b_ms, b_best, _, _ = time_pass(base, reps, 3, launch)
+    g_ms, g_best, _, _ = time_pass(grouped, reps, 3, launch)
+    b_us, g_us = b_ms * 1e3 / nl, g_ms * 1e3 / nl
     unique = p.kv_bytes_unique()
-    return {"workload": "qwen3_8b_shared_prefix_decode, 12 distinct layers cycled to 36 launches",
-            "unique_bytes_per_layer": unique, "bytes_read_per_layer_unshared": p.kv_bytes_read(),
-            "pa_attend_us_per_layer": b_us, "pa_attend_prefix_us_per_layer": g_us,
+    logical = p.kv_bytes_read()
+    best = min(b_us, g_us)
+    return {"workload": "qwen3_8b_shared_prefix_decode: 36 distinct layers (values drawn on the device), "
+                        "10 slots x 8447 keys, 6144 shared, 32/8 heads",
+            "unique_bytes_per_layer": unique, "logical_bytes_per_layer": logical,
+            "pa_attend_us_per_layer": b_us, "pa_attend_us_per_layer_best": b_best * 1e3 / nl,
+            "pa_attend_prefix_us_per_layer": g_us, "pa_attend_prefix_us_per_layer_best": g_best * 1e3 / nl,
             "pa_attend_gbs_unique": unique / (b_us * 1e-6) / 1e9,
             "pa_attend_prefix_gbs_unique": unique / (g_us * 1e-6) / 1e9,
-            "pa_attend_effective_gbs": p.kv_bytes_read() / (b_us * 1e-6) / 1e9,
-            "pa_attend_prefix_effective_gbs": p.kv_bytes_read() / (g_us * 1e-6) / 1e9,
-            "speedup": b_us / g_us,
-            "parity": "against the FP64 oracle and pa_attend in the GPU tests"}
+            "pa_attend_effective_gbs": logical / (b_us * 1e-6) / 1e9,
+            "speedup_prefix_vs_attend": b_us / g_us,
+            "partitions": base[0].num_partitions,
+            "roofline": hbm_roofline(unique, best, "the faster of pa_attend and pa_attend_prefix per layer "
+                                     "(graph replay of 36 layers), on unique bytes", ceiling_gbs,
+                                     path="pa_attend_prefix" if g_us < b_us else "pa_attend"),
+            "parity": "against the FP64 oracle (layer 7 and sampled slots) and pa_attend in the GPU tests"}
+
+
+def ragged_config(dev, steps, launch, ceiling_gbs=None):
+    """The ragged mixed decode batch (64 slots of U[1, 8447] keys + 4 zombie
+    slots, 32/8 heads, 512-token partitions): one layer (about 1.2 GB of
+    pages, far beyond the Infinity Cache) per launch.  The split and its
+    merge run in one launch (the last partition of each (slot, KV head)
+    merges); the merge alone is also timed as the stand-alone pa_combine over
+    the same partials, which is what a separate merge pass would cost."""
+    import torch
+    import paged_kv_cache_attend_amd as pk
+    from paged_kv_cache_attend_amd import inputs
+    p = inputs.ragged_mixed_decode()
+    t = device_layers(p, dev, 1, inputs.SEED_BASE + 4400)[0]
+    out = torch.empty_like(t["q"])
+    lse = torch.empty(t["q"].shape[:2], dtype=torch.float32, device=dev)
+    c = pk.PreparedAttend(t["q"], t["k"], t["v"], t["block_table"], t["ctx_lens"], t["q_lens"],
+                          float(p.scale), out, lse, max_q_len=1, max_ctx_len=p.max_ctx_len,
+                          partition_size=p.partition_size)
+    reps = max(steps // 2, 40)
+    ms, best, _, _ = time_pass([c], reps, 3, launch)
+    c_auto = pk.PreparedAttend(t["q"], t["k"], t["v"], t["block_table"], t["ctx_lens"], t["q_lens"],
+                               float(p.scale), out, lse, max_q_len=1, max_ctx_len=p.max_ctx_len)
+    ms_auto, _, _, _ = time_pass([c_auto], reps, 3, launch)
+    P = c.num_partitions
+    rows = p.total_q * p.num_q_heads
+    po = torch.zeros((P, rows, p.head_dim), dtype=torch.float32, device=dev)
+    plse = torch.randn((P, rows), dtype=torch.float32, device=dev)
+    cout = torch.empty((rows, p.head_dim), dtype=torch.bfloat16, device=dev)
+    clse = torch.empty(rows, dtype=torch.float32, device=dev)
+
+    class _Comb:
+        def launch(self, s):
+            pk.combine(po, plse, cout, clse, stream=s)
+
+    comb_ms, _, _, _ = time_pass([_Comb()], reps, 3, launch)
+    kv = p.kv_bytes_read()
+    us = ms * 1e3
+    return {"workload": "ragged_mixed_decode: 64 slots U[1, 8447] + 4 zombies, 32/8 heads, "
+                        "512-token partitions (values drawn on the device)",
+            "kv_bytes": kv, "partitions": P, "split_and_merge_us": us, "split_and_merge_us_best": best * 1e3,
+            "gbs": kv / (us * 1e-6) / 1e9, "auto_partition_us": ms_auto * 1e3,
+            "auto_partitions": c_auto.num_partitions,
+            "merge_alone_us": comb_ms * 1e3,
+            "merge_alone_note": f"pa_combine over {P} partials x {rows} rows x 128 (the same partials the fused "
+                                "merge reads), launched by itself",
+            "partial_bytes": P * rows * (p.head_dim + 1) * 4,
+            "roofline": hbm_roofline(kv, us, "decode_kernel<4> with the fused merge, one launch", ceiling_gbs),
+            "parity": "against the FP64 oracle in full in the GPU tests (test_ragged_mixed_decode_full_size)"}
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
 
 
 def main():
@@ -470,16 +659,23 @@ def main():
     log(f"setup {time.perf_counter() - t_setup:.1f}s; partitions per slot {calls[0].num_partitions}")
 
     decode = problem.max_q_len == 1
-    ms, wall_ms, _ = time_pass(calls, args.steps, args.warmup, args.launch)
+    ms, best_ms, wall_ms, trials = time_pass(calls, args.steps, args.warmup, args.launch)
+    log(f"timed: {ms * 1e3 / len(calls):.2f} us per layer (median of {len(trials)} trials)")
     eager_ms = None
     if args.launch == "graph" and not args.quick:
-        eager_ms, _, _ = time_pass(calls, max(10, args.steps // 4), 2, "eager")
+        eager_ms, _, _, _ = time_pass(calls, max(10, args.steps // 4), 2, "eager", trials=1)
     per_call_ms = ms / len(calls) if args.quick else time_kernel_launches(calls, max(5, args.steps // 10))
 
     kv_read = problem.kv_bytes_read() * problem.num_layers
     kv_unique = problem.kv_bytes_unique() * problem.num_layers
     flops = 4 * int((problem.q_lens.astype(np.int64) * problem.ctx_lens).sum()) * problem.num_q_heads \
         * problem.head_dim * problem.num_layers
+    ceiling = mfma = None
+    if not args.quick:
+        mfma = mfma_ceiling()
+        if decode:
+            ceiling = read_ceiling(problem, layers, args.steps, args.launch)
+            log(f"read ceiling {ceiling['gbs']:.0f} GB/s; MFMA {mfma['tflops']:.0f} TFLOP/s")
     if decode:
         headline_bytes = kv_unique  # each distinct byte read once (equals kv_read without sharing)
         value = headline_bytes / (ms * 1e-3) / 1e9
@@ -497,6 +693,9 @@ def main():
                     "kernel": kname + " (split-KV decode with the LSE merge fused), one launch per layer",
                     "avg_launch_us": per_call_ms * 1e3,
                     "timing": "HIP events around back-to-back launches on the launch stream"}
+        if ceiling:
+            roofline["measured_read_ceiling_gbs"] = ceiling["gbs"]
+            roofline["frac_of_measured_read_ceiling"] = achieved / ceiling["gbs"]
     else:
         value = flops / (ms * 1e-3) / 1e12
         unit = "TFLOP/s"
@@ -507,6 +706,9 @@ def main():
                     "traffic": None if tr is None else tr[0] + tr[1],
                     "algorithmic_flops_per_launch": flops / len(calls), "kernel": "chunk_kernel",
                     "avg_launch_us": per_call_ms * 1e3}
+        if mfma:
+            roofline["measured_peak_tflops"] = mfma["tflops"]
+            roofline["frac_of_measured_peak"] = achieved / mfma["tflops"]
 
     par = parity(problem, outs, lses, ref) if ref else None
     cpu = None
@@ -519,21 +721,33 @@ def main():
         else:
             cpu = {"value": flops / problem.num_layers * len(ref) / cpu_s / 1e12, "unit": "TFLOP/s",
                    "cores": ncores, "kind": "oracle", "sample": f"{len(ref)} call(s), 1 BLAS thread, {cpu_s:.1f}s"}
-        cpu["cpu_model"] = platform.processor() or platform.machine()
+        cpu["cpu_model"] = cpu_model()
+        cpu["host_cpus_available"] = len(os.sched_getaffinity(0))
 
-    ceiling = copy_ceiling(dev) if decode and not args.quick else None
+    main_workload = decode and problem.name == "qwen3_8b_short_decode"
+    del layers
+    calls_keep = calls
     secondary = None
-    if decode and not args.no_chunk:
-        secondary = chunk_secondary(dev, args.steps, args.launch)
+    if main_workload and not args.no_chunk:
+        log("chunk workload")
+        secondary = chunk_secondary(dev, args.steps, args.launch, mfma["tflops"] if mfma else None)
+    configs = {}
+    if main_workload and not args.no_prefix:
+        log("shared-prefix workload")
+        configs["shared_prefix"] = shared_prefix_config(dev, args.steps, args.launch,
+                                                        ceiling["gbs"] if ceiling else None)
+        torch.cuda.empty_cache()
+    if main_workload and not args.no_ragged:
+        log("ragged workload")
+        configs["ragged"] = ragged_config(dev, args.steps, args.launch, ceiling["gbs"] if ceiling else None)
+        torch.cuda.empty_cache()
     append = None
-    if decode and not args.no_append:
+    if main_workload and not args.no_append:
         append = append_secondary(dev, args.steps, args.launch)
     quant = None
-    if decode and not args.no_quant and problem.name == "qwen3_8b_short_decode":
-        quant = quant_secondary(dev, args.steps, args.launch, ms / len(calls) * 1e3)
-    prefix = None
-    if decode and not args.no_prefix and problem.name == "qwen3_8b_short_decode":
-        prefix = prefix_secondary(dev, args.steps, args.launch)
+    if main_workload and not args.no_quant:
+        log("quantised pages")
+        quant = quant_secondary(dev, args.steps, args.launch, ms / len(calls_keep) * 1e3)
 
     line = {
         "metric": METRIC,
@@ -558,13 +772,17 @@ def main():
             "head_dim": problem.head_dim,
             "block_size": problem.block_size,
             "partition_size": ps,
-            "partitions": calls[0].num_partitions,
+            "partitions": calls_keep[0].num_partitions,
             "launch": args.launch,
             "accumulate": "fp32",
+            "pv_weights": ("bf16 hi + lo pair per softmax weight (the fp32 weight to 2^-15)" if decode
+                           else "bf16 softmax weights, output divided by their sum"),
         },
+        "timing": {"trials": len(trials), "steps_per_trial": args.steps, "ms_per_step_median": ms,
+                   "ms_per_step_best": best_ms, "ms_per_step_trials": trials},
         "frac_of_hbm_peak": (value / HBM_PEAK_GBS) if decode else None,
-        "copy_ceiling_gbs": ceiling,
-        "frac_of_copy_ceiling": (value / ceiling) if ceiling else None,
+        "measured_read_ceiling": ceiling,
+        "measured_mfma_ceiling": mfma,
         "kv_bytes_per_step": kv_read if decode else None,
         "kv_unique_bytes_per_step": kv_unique if decode else None,
         "effective_gbs": (kv_read / (ms * 1e-3) / 1e9) if decode else None,
@@ -574,9 +792,9 @@ def main():
         "cpu_baseline": cpu,
         "parity": par,
         "chunk": secondary,
+        "configs": configs or None,
         "append": append,
         "quantised": quant,
-        "prefix_grouped": prefix,
         "source_hash": kernel_source_hash(),
     }
     print(json.dumps(line), flush=True)

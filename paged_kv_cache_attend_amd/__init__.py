@@ -13,7 +13,7 @@ _BINDING = ("PaError", "Shape", "Status", "attend", "combine", "gather_kv", "val
             "EXPORTS", "PreparedAttend", "workspace_init", "write_kv", "copy_blocks", "Pool",
             "PoolStats", "KVCache", "QuantCache", "attend_kv", "write_kv_cache", "KV_BF16",
             "KV_FP8_E4M3", "KV_Q8_0", "KV_Q4_0", "PrefixGroups", "attend_prefix", "attend_noalloc",
-            "NOALLOC_SCRATCH_BYTES")
+            "NOALLOC_SCRATCH_BYTES", "measure_read_tiles", "measure_mfma_bf16")
 
 
 def __getattr__(name):

@@ -28,7 +28,8 @@ EXPORTS = ("pa_workspace_size", "pa_workspace_init", "pa_num_partitions", "pa_at
            "pa_pool_destroy", "pa_pool_append", "pa_pool_fork", "pa_pool_release", "pa_pool_retire",
            "pa_pool_length", "pa_pool_block_table", "pa_pool_refcount", "pa_pool_get_stats",
            "pa_attend_kv", "pa_write_kv_cache", "pa_num_partitions_kv", "pa_prefix_workspace_size",
-           "pa_prefix_workspace_init", "pa_attend_prefix", "pa_attend_noalloc", "pa_status_string")
+           "pa_prefix_workspace_init", "pa_attend_prefix", "pa_attend_noalloc", "pa_status_string",
+           "pa_measure_read_tiles", "pa_measure_mfma_bf16")
 
 NOALLOC_SCRATCH_BYTES = 32 << 20   # PA_NOALLOC_SCRATCH_BYTES
 
@@ -148,6 +149,10 @@ def load():
     lib.pa_num_partitions_kv.restype = ctypes.c_int32
     lib.pa_attend.argtypes = [shp, P, P, P, P, P, P, ctypes.c_float, P, P, P, ctypes.c_size_t, P]
     lib.pa_attend.restype = ctypes.c_int
+    lib.pa_measure_read_tiles.argtypes = [P, P, P, ctypes.c_int64, ctypes.c_int32, P, P]
+    lib.pa_measure_read_tiles.restype = ctypes.c_int
+    lib.pa_measure_mfma_bf16.argtypes = [ctypes.c_int32, ctypes.c_int32, P, P]
+    lib.pa_measure_mfma_bf16.restype = ctypes.c_int
     lib.pa_attend_noalloc.argtypes = [shp, P, P, P, P, P, P, ctypes.c_float, P, P, P]
     lib.pa_attend_noalloc.restype = ctypes.c_int
     lib.pa_combine.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P, P, P, P, P]
@@ -369,6 +374,32 @@ def attend_noalloc(q, k_cache, v_cache, block_table, ctx_lens, q_lens, scale, ou
                                   _ptr(lse), _stream_handle(dev, stream))
     _check(st, "pa_attend_noalloc")
     return out, lse
+
+
+def measure_read_tiles(k_cache, v_cache, tiles, sink, *, tiles_per_wg: int, stream=None):
+    """``pa_measure_read_tiles``: stream tiles (int32 tile indices) of both
+    caches; sink uint32 [ceil(len(tiles) / tiles_per_wg)]."""
+    torch = _torch()
+    dev = k_cache.device
+    _need(tiles, "tiles", torch.int32, dev, 1)
+    _need(sink, "sink", torch.int32, dev, 1)
+    n = int(tiles.shape[0])
+    if sink.shape[0] < -(-n // tiles_per_wg):
+        raise ValueError("sink too small")
+    st = load().pa_measure_read_tiles(_ptr(k_cache), _ptr(v_cache), _ptr(tiles), ctypes.c_int64(n),
+                                      ctypes.c_int32(tiles_per_wg), _ptr(sink), _stream_handle(dev, stream))
+    _check(st, "pa_measure_read_tiles")
+
+
+def measure_mfma_bf16(workgroups: int, iters: int, sink, *, stream=None):
+    """``pa_measure_mfma_bf16``: sink float32 [workgroups * 4]; returns FLOP per call."""
+    torch = _torch()
+    _need(sink, "sink", torch.float32, sink.device, 1)
+    if sink.shape[0] < workgroups * 4:
+        raise ValueError("sink too small")
+    st = load().pa_measure_mfma_bf16(int(workgroups), int(iters), _ptr(sink), _stream_handle(sink.device, stream))
+    _check(st, "pa_measure_mfma_bf16")
+    return workgroups * 4 * iters * 4 * 32768
 
 
 def combine(partial_out, partial_lse, out, lse=None, *, stream=None):

@@ -22,7 +22,7 @@ LIB = os.path.join(PKG, "libpa.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["api.cpp", "pool.cpp", "decode.hip", "combine.hip", "chunk.hip", "gather.hip", "write.hip", "prefix.hip",
-           "noalloc.hip"]
+           "noalloc.hip", "measure.hip"]
 
 COMMON = [
     "--offload-arch=gfx950",

@@ -15,7 +15,8 @@ import paged_kv_cache_attend_amd as pk
 from paged_kv_cache_attend_amd import _lib
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "pa.h")
+HEADERS = sorted(os.path.join(ROOT, "include", f) for f in os.listdir(os.path.join(ROOT, "include"))
+                 if f.endswith(".h"))
 
 
 @pytest.fixture(scope="module")
@@ -27,7 +28,7 @@ def lib():
 
 
 def _declared():
-    text = open(HEADER).read()
+    text = "\n".join(open(h).read() for h in HEADERS)
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(pa_[a-z_0-9]+)\s*\(", text)))
 
@@ -225,6 +226,16 @@ def test_validate_workspace_counter_region_checked_on_host(lib):
         == pk.Status.ERR_WORKSPACE_TOO_SMALL
     assert lib.pa_validate(ctypes.byref(s), FAKE, FAKE, FAKE, None, 0, None, None) == pk.Status.ERR_NULL_ARG
     assert _lib.PA_BAD_WORKSPACE == 0x10
+
+
+def test_measure_entry_points_check_arguments_on_the_host(lib):
+    assert lib.pa_measure_read_tiles(FAKE, FAKE, FAKE, -1, 4, FAKE, None) == pk.Status.ERR_BAD_SHAPE
+    assert lib.pa_measure_read_tiles(FAKE, FAKE, FAKE, 10, 0, FAKE, None) == pk.Status.ERR_BAD_SHAPE
+    assert lib.pa_measure_read_tiles(None, FAKE, FAKE, 10, 4, FAKE, None) == pk.Status.ERR_NULL_ARG
+    assert lib.pa_measure_read_tiles(FAKE, FAKE, FAKE, 0, 4, FAKE, None) == pk.Status.OK  # nothing to do
+    assert lib.pa_measure_mfma_bf16(0, 10, FAKE, None) == pk.Status.ERR_BAD_SHAPE
+    assert lib.pa_measure_mfma_bf16(4, 0, FAKE, None) == pk.Status.ERR_BAD_SHAPE
+    assert lib.pa_measure_mfma_bf16(4, 10, None, None) == pk.Status.ERR_NULL_ARG
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
