@@ -430,11 +430,13 @@ pa_status pa_validate(const pa_shape* shape, const int32_t* block_table, const i
   // The counters sit at the start of the workspace for every page format
   // and for the suffix pass of pa_attend_prefix: one per (slot, KV head),
   // present whenever the shape needs a workspace.
-  if (workspace && pa_workspace_size(shape) > 0) {
-    const size_t n = (size_t)shape->num_seqs * (size_t)shape->num_kv_heads;
-    if (workspace_bytes < n * sizeof(int32_t)) return PA_ERR_WORKSPACE_TOO_SMALL;
+  Plan plan, comp;
+  if (workspace && make_plan(shape, &plan) == PA_OK && make_plan(shape, &comp, true) == PA_OK &&
+      std::max(plan.ws_bytes, comp.ws_bytes) > 0) {
+    const size_t bytes = std::max(plan.counters_bytes, comp.counters_bytes);
+    if (workspace_bytes < bytes) return PA_ERR_WORKSPACE_TOO_SMALL;
     v.counters = static_cast<const int32_t*>(workspace);
-    v.num_counters = (int32_t)n;
+    v.num_counters = (int32_t)(bytes / sizeof(int32_t));
   }
   v.block_table = block_table;
   v.ctx_lens = ctx_lens;

@@ -57,9 +57,13 @@ extern "C" pa_status pa_attend_noalloc(const pa_shape* shape, const void* q, con
   // attend_bf16 then returns the precise status).
   const size_t need = pa_workspace_size(shape);
   if (need > PA_NOALLOC_SCRATCH_BYTES) return PA_ERR_SCRATCH_LIMIT;
-  if ((size_t)shape->num_seqs * (size_t)(shape->num_kv_heads > 0 ? shape->num_kv_heads : 0) > ((size_t)1 << 20) &&
-      need > 0)
-    return PA_ERR_SCRATCH_LIMIT;  // more counters than the zeroed region holds
+  // Counters: one per (slot, KV head) on the decode path, one per 128-row
+  // tile of a (slot, query head) on the chunk path; bounded by slots x query
+  // heads x row tiles either way.
+  const size_t counters = (size_t)(shape->num_seqs > 0 ? shape->num_seqs : 0) *
+                          (size_t)(shape->num_q_heads > 0 ? shape->num_q_heads : 0) *
+                          (size_t)((shape->max_q_len + 127) / 128 > 1 ? (shape->max_q_len + 127) / 128 : 1);
+  if (need > 0 && counters > ((size_t)1 << 20)) return PA_ERR_SCRATCH_LIMIT;  // beyond the zeroed region
   void* ws = nullptr;
   if (need > 0) {
     int dev = 0;
