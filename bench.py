@@ -49,6 +49,7 @@ def parse():
     ap.add_argument("--no-quant", action="store_true", help="skip the secondary quantised-KV decode measurement")
     ap.add_argument("--no-prefix", action="store_true", help="skip the shared-prefix workload (pa_attend and pa_attend_prefix)")
     ap.add_argument("--no-ragged", action="store_true", help="skip the ragged mixed decode workload")
+    ap.add_argument("--no-causal", action="store_true", help="skip chunked prefill and speculative verification")
     ap.add_argument("--cpu-budget-s", type=float, default=25.0)
     ap.add_argument("--mode", choices=["bench", "copy"], default="bench",
                     help="copy: time a plain 1 GiB device copy (counter calibration for rocprofv3)")
@@ -619,6 +620,62 @@ def ragged_config(dev, steps, launch, ceiling_gbs=None):
             "parity": "against the FP64 oracle in full in the GPU tests (test_ragged_mixed_decode_full_size)"}
 
 
+def causal_secondary(dev, steps, launch, bf16_decode_us=None):
+    """Causal multi-token queries (section 8.2.3 and 8.5 of the chapter):
+    - the page's chunked-prefill example, the last 512-token chunk of an
+      8192-token prompt, 32/8 heads: TFLOP/s on the visible (query, key)
+      pairs (4 D FLOP per pair and query head), 16 resident copies rotated;
+    - speculative verification of 5 and 8 tokens per request on the
+      Qwen3-8B short-decode batch (16 x 2303 keys), 36 distinct layers:
+      microseconds per layer and GB/s over the pages read."""
+    import torch
+    import paged_kv_cache_attend_amd as pk
+    from paged_kv_cache_attend_amd import inputs
+    res = {}
+    p = inputs.chunked_prefill()
+    m, n = int(p.q_lens[0]), int(p.ctx_lens[0])
+    pairs = m * (n - m) + m * (m + 1) // 2
+    flops = 4 * p.head_dim * p.num_q_heads * pairs
+    sets = []
+    for t in device_layers(p, dev, 16, inputs.SEED_BASE + 6600):
+        out = torch.empty_like(t["q"])
+        lse = torch.empty(t["q"].shape[:2], dtype=torch.float32, device=dev)
+        sets.append(pk.PreparedAttend(t["q"], t["k"], t["v"], t["block_table"], t["ctx_lens"], t["q_lens"],
+                                      float(p.scale), out, lse, max_q_len=m, max_ctx_len=n, causal=True))
+    ms, best, _, _ = time_pass(sets, max(steps // 8, 20), 3, launch)
+    us = ms * 1e3 / len(sets)
+    res["chunked_prefill"] = {"workload": "chunked_prefill_c512_h7680: 1 request, 512 new tokens after 7680 "
+                                          "cached, 32/8 heads, causal (values drawn on the device)",
+                              "pairs": pairs, "flop_per_call": flops, "us_per_call": us,
+                              "us_per_call_best": best * 1e3 / len(sets),
+                              "tflops": flops / (us * 1e-6) / 1e12,
+                              "frac_of_bf16_peak": flops / (us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS}
+    del sets
+    torch.cuda.empty_cache()
+    for mt in (5, 8):
+        p = inputs.speculative_verify(mt)
+        calls = []
+        for t in device_layers(p, dev, 36, inputs.SEED_BASE + 6700 + mt):
+            out = torch.empty_like(t["q"])
+            lse = torch.empty(t["q"].shape[:2], dtype=torch.float32, device=dev)
+            calls.append(pk.PreparedAttend(t["q"], t["k"], t["v"], t["block_table"], t["ctx_lens"], t["q_lens"],
+                                           float(p.scale), out, lse, max_q_len=mt, max_ctx_len=p.max_ctx_len,
+                                           causal=True))
+        ms, best, _, _ = time_pass(calls, max(steps // 4, 20), 3, launch)
+        us = ms * 1e3 / len(calls)
+        kv = p.kv_bytes_read()
+        res[f"speculative_verify_m{mt}"] = {
+            "workload": f"16 requests x 2303 keys, {mt} new tokens each, 32/8 heads, causal, 36 distinct layers",
+            "us_per_layer": us, "us_per_layer_best": best * 1e3 / len(calls),
+            "kv_gbs": kv / (us * 1e-6) / 1e9, "frac_of_hbm_peak": kv / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+            "vs_one_token_decode": (us / bf16_decode_us) if bf16_decode_us else None}
+        del calls
+        torch.cuda.empty_cache()
+    res["parity"] = "against the FP64 oracle in the GPU tests (test_chunked_prefill_page_example_full_size, " \
+                    "test_speculative_verification)"
+    return res
+
+
 def cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
@@ -741,6 +798,10 @@ def main():
         log("ragged workload")
         configs["ragged"] = ragged_config(dev, args.steps, args.launch, ceiling["gbs"] if ceiling else None)
         torch.cuda.empty_cache()
+    causal = None
+    if main_workload and not args.no_causal:
+        log("causal multi-token workloads")
+        causal = causal_secondary(dev, args.steps, args.launch, ms / len(calls_keep) * 1e3)
     append = None
     if main_workload and not args.no_append:
         append = append_secondary(dev, args.steps, args.launch)
@@ -793,6 +854,7 @@ def main():
         "parity": par,
         "chunk": secondary,
         "configs": configs or None,
+        "causal": causal,
         "append": append,
         "quantised": quant,
         "source_hash": kernel_source_hash(),

@@ -138,8 +138,10 @@ pa_status make_plan(const pa_shape* s, Plan* plan, bool grouped = false) {
       p.ws_bytes = p.out_offset + (size_t)p.num_parts * p.rows * kHeadDim * sizeof(float);
     }
   } else {
-    const int q_tiles = ceil_div(s->max_q_len, kChunkRows);
-    const long long grid = (long long)s->num_seqs * s->num_q_heads * q_tiles;
+    // One workgroup per 128 packed (token, query head of the group) rows of
+    // a (slot, KV head).
+    const int q_tiles = ceil_div(s->max_q_len * p.group, kChunkRows);
+    const long long grid = (long long)s->num_seqs * s->num_kv_heads * q_tiles;
     if (grid > INT_MAX) return PA_ERR_UNSUPPORTED;
     p.grid = (unsigned)grid;
   }
@@ -230,7 +232,7 @@ pa_status attend_impl(const pa_shape* shape, const pa_kv_cache& kv, const void* 
   c.num_q_heads = shape->num_q_heads;
   c.num_kv_heads = shape->num_kv_heads;
   c.max_blocks = shape->max_blocks_per_seq;
-  c.q_tiles = ceil_div(shape->max_q_len, kChunkRows);
+  c.q_tiles = ceil_div(shape->max_q_len * plan.group, kChunkRows);
   c.causal = (shape->flags & PA_FLAG_CAUSAL) ? 1 : 0;
   c.max_ctx = shape->max_ctx_len;
   c.max_q = shape->max_q_len;

@@ -8,7 +8,15 @@
 // section 8.2.3).  Both products are dense contractions, so they run on the
 // matrix cores: v_mfma_f32_32x32x16_bf16 with fp32 accumulation.
 //
-// Workgroup: 8 waves over 128 query rows of one (slot, query head).  Wave w
+// Rows: the (new token, query head) pairs of one KV head of a slot, token
+// major -- packed row j is token j / G of query head g G + j % G, G being the
+// query heads per KV head -- so the G heads that share a KV head read its
+// pages once, and a few tokens with grouped heads (speculative verification:
+// 5 to 8 tokens times 4 heads) fill a tile instead of leaving most of it
+// idle.  With one query head per KV head (the denoising workload) a row is a
+// token.
+//
+// Workgroup: 8 waves over 128 packed rows of one (slot, KV head).  Wave w
 // takes rows 32 (w % 4) .. +32 and one half of the keys (w / 4); the two
 // halves merge through LDS at the end.  Each half walks its keys in 32-key
 // tiles (two 16-token pages):
@@ -83,10 +91,10 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkParams p) {
 
   const int wg = xcd_remap(blockIdx.x, grid);
   const int qt = wg % q_tiles;
-  const int sh = wg / q_tiles;
-  const int h = sh % hq;
-  const int seq = sh / hq;
-  const int g = h / (hq / hkv);
+  const int sg = wg / q_tiles;
+  const int g = sg % hkv;
+  const int seq = sg / hkv;
+  const int G = hq / hkv;
 
   // The keys this half needs depend on the slot's lengths.  The page ids of
   // its first four tiles are requested together with the lengths, for the
@@ -97,8 +105,8 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkParams p) {
   auto half_tiles = [&](int m_, int n_, int& tile0_, int& last_page_, int& kv_end_) {
     int kv = n_;
     if (p.causal) {
-      const int last_row = min(m_, (qt + 1) * kChunkRows) - 1;
-      kv = min(n_, n_ - m_ + last_row + 1);
+      const int last_token = (min(m_ * G, (qt + 1) * kChunkRows) - 1) / G;  // of the tile's last live row
+      kv = min(n_, n_ - m_ + last_token + 1);
     }
     kv_end_ = kv;
     const int nt = (max(kv, 1) + kTileKeys - 1) / kTileKeys;
@@ -118,18 +126,19 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkParams p) {
   // (all ten in flight before the first is used)
   asm volatile("" : "+s"(ids[0]), "+s"(ids[1]), "+s"(ids[2]), "+s"(ids[3]), "+s"(ids[4]), "+s"(ids[5]),
                "+s"(ids[6]), "+s"(ids[7]), "+s"(m), "+s"(n));
-  if (m <= 0 || n <= 0 || qt * kChunkRows >= m) return;
+  if (m <= 0 || n <= 0 || qt * kChunkRows >= m * G) return;
   int q_row0 = 0;  // row offset of the slot, summed once the first tiles are requested
-  const int row = qt * kChunkRows + rg * 32 + col;  // row within the slot
-  const bool row_live = row < m;
+  const int prow = qt * kChunkRows + rg * 32 + col;  // packed row within the slot
+  const bool row_live = prow < m * G;
+  const int tok = row_live ? prow / G : 0;           // its token; rows past the end use token 0 of
+  const int h = g * G + (row_live ? prow % G : 0);   // head g G (their results are never written)
 
   // Q^T operand: lane (row, half) holds dims (hh*8 + s)*8 .. +8 for step s
-  // (loaded after the first tiles are requested, below).  Rows past m read
-  // row 0's query (their results are never written).
+  // (loaded after the first tiles are requested, below).
   u32x4_t qf[8];
   auto load_q = [&]() {
     const u32x4_t* qp = reinterpret_cast<const u32x4_t*>(p.q) +
-                        ((size_t)(q_row0 + (row_live ? row : 0)) * p.num_q_heads + h) * (kHeadDim / 8);
+                        ((size_t)(q_row0 + tok) * p.num_q_heads + h) * (kHeadDim / 8);
 #pragma unroll
     for (int s = 0; s < 8; ++s) qf[s] = qp[hh * 8 + s];
   };
@@ -139,7 +148,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkParams p) {
   half_tiles(m, n, tile0, last_page, kv_end);
   const int ntiles = (kv_end + kTileKeys - 1) / kTileKeys;
   const int T = (ntiles + 1) / 2;       // tiles per half (both halves loop T times)
-  const int my_limit = p.causal ? (n - m + row) : (n - 1);  // last visible key of this row
+  const int my_limit = p.causal ? (n - m + tok) : (n - 1);  // last visible key of this row
   if (m != p.max_q || n != p.max_ctx) request_ids(tile0, last_page);
 
   // Loads straight into LDS (global_load_lds_dwordx4: lane l of a wave
@@ -414,7 +423,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkParams p) {
   const float l_tot = l + __shfl_xor(l, 32, 64);
   const float r = r_run * s0 + ml.z * s1;
   const float inv = 1.f / (r + __shfl_xor(r, 32, 64));
-  uint16_t* orow = p.out + ((size_t)(q_row0 + row) * p.num_q_heads + h) * kHeadDim;
+  uint16_t* orow = p.out + ((size_t)(q_row0 + tok) * p.num_q_heads + h) * kHeadDim;
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb) {
     if ((mb >> 1) != kh) continue;
@@ -429,7 +438,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkParams p) {
       *reinterpret_cast<uint2*>(orow + d) = w;
     }
   }
-  if (kh == 0 && hh == 0 && p.lse) p.lse[(size_t)(q_row0 + row) * p.num_q_heads + h] = (M + fast_log2(l_tot)) * kLn2;
+  if (kh == 0 && hh == 0 && p.lse) p.lse[(size_t)(q_row0 + tok) * p.num_q_heads + h] = (M + fast_log2(l_tot)) * kLn2;
 }
 
 }  // namespace

@@ -394,6 +394,25 @@ def chunked_denoise() -> PagedProblem:
     return make_problem("chunked_denoise", SEED_BASE + 5, [1024] * 4, [256] * 4, 24, 24)
 
 
+def chunked_prefill(num_seqs: int = 1) -> PagedProblem:
+    """The last 512-token chunk of an 8192-token prompt (7680 tokens already
+    cached), Qwen3-8B heads (32 query / 8 KV), causal: the chunked-prefill
+    example of the inference-optimisation chapter (section 8.2.3), whose last
+    chunk covers 512 x 7680 + 512 x 513 / 2 = 4,063,488 query-key pairs."""
+    return make_problem("chunked_prefill_c512_h7680", SEED_BASE + 6, [8192] * num_seqs, [512] * num_seqs,
+                        32, 8, causal=True)
+
+
+def speculative_verify(num_tokens: int = 8) -> PagedProblem:
+    """Verification of `num_tokens` proposed tokens per request at once
+    (section 8.5 of the same chapter: a draft proposes several tokens, the
+    target model checks them in one step): the Qwen3-8B short decode batch
+    (16 requests, 2303 keys each including the new tokens, 32/8 heads),
+    causal over the new tokens."""
+    return make_problem(f"speculative_verify_m{num_tokens}", SEED_BASE + 7 + num_tokens, [2303] * 16,
+                        [num_tokens] * 16, 32, 8, causal=True)
+
+
 CONFIGS = {
     "tiny_decode": tiny_decode,
     "qwen3_8b_short_decode": qwen3_short_decode,

@@ -295,6 +295,25 @@ def test_chunk_path_many_slots(num_seqs):
     compare(p, run_gpu(p), run_oracle(p), label=f"chunk {num_seqs} slots")
 
 
+def test_chunked_prefill_page_example_full_size():
+    # section 8.2.3: the last 512-token chunk of an 8192-token prompt, causal,
+    # Qwen3-8B heads; 4,063,488 visible (query, key) pairs per head
+    p = inputs.chunked_prefill()
+    m, n = int(p.q_lens[0]), int(p.ctx_lens[0])
+    assert m * (n - m) + m * (m + 1) // 2 == 4_063_488
+    say("chunked prefill c=512 h=7680")
+    compare(p, run_gpu(p), run_oracle(p), label="chunked prefill c512 h7680")
+
+
+@pytest.mark.parametrize("num_tokens", [5, 8])
+def test_speculative_verification(num_tokens):
+    # 16 requests x 2303 keys, 5 or 8 new tokens each, causal over them, 32/8
+    # heads: (token, query head) rows of a KV head packed into one tile
+    p = inputs.speculative_verify(num_tokens)
+    say(f"speculative verification m={num_tokens}")
+    compare(p, run_gpu(p), run_oracle(p), label=f"spec verify m={num_tokens}")
+
+
 def test_chunk_path_handles_group_sizes_without_decode_kernel():
     # 8 query heads per KV head with one row each takes the MFMA path
     p = _case([37, 100, 1000], hq=64, hkv=8, seed=43)
