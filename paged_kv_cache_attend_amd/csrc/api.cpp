@@ -25,6 +25,7 @@ struct Plan {
   bool empty = true;      // nothing to launch
   bool decode = false;    // split-KV decode path, else chunk path
   int group = 1;          // query heads per KV head
+  int tokens = 1;         // decode: new tokens per slot the kernel is built for
   int part_pages = 0;     // pages per partition (decode)
   int num_parts = 1;      // partitions (decode)
   size_t rows = 0;        // total_q * num_q_heads
@@ -123,7 +124,11 @@ pa_status make_plan(const pa_shape* s, Plan* plan, bool grouped = false) {
     return PA_OK;
   }
   p.empty = false;
-  p.decode = (s->max_q_len == 1) && decode_supports_group(p.group);
+  // Up to 8 new tokens per slot (tokens x group <= 32) stream the pages like
+  // a one-token decode, the (token, query head) pairs as matrix columns;
+  // longer chunks take the chunk path.
+  p.tokens = decode_tokens_per_slot(p.group, s->max_q_len);
+  p.decode = p.tokens > 0 && (p.tokens == 1 || !grouped);
   if (p.decode) {
     const int max_pages = ceil_div(s->max_ctx_len, kBlockSize);
     p.part_pages = s->partition_size > 0 ? s->partition_size / kBlockSize : auto_part_pages(s, max_pages, grouped);
@@ -182,6 +187,7 @@ DecodeParams decode_params(const pa_shape* shape, const Plan& plan, const pa_kv_
   d.k_scales = static_cast<const uint16_t*>(kv.k_scales);
   d.v_scales = static_cast<const uint16_t*>(kv.v_scales);
   d.v_scale = kv.format == kFmtFP8 ? kv.v_scale : 1.f;
+  d.causal = (shape->flags & PA_FLAG_CAUSAL) ? 1 : 0;
   return d;
 }
 
@@ -202,7 +208,7 @@ pa_status attend_impl(const pa_shape* shape, const pa_kv_cache& kv, const void* 
   if (!q || !k_cache || !v_cache || !block_table || !ctx_lens || !q_lens || !out)
     return PA_ERR_NULL_ARG;
   if (grouped && (!kv.k_scales || !kv.v_scales)) return PA_ERR_NULL_ARG;
-  if (kv.format != kFmtBF16 && !plan.decode) return PA_ERR_UNSUPPORTED;
+  if (kv.format != kFmtBF16 && (!plan.decode || plan.tokens > 1)) return PA_ERR_UNSUPPORTED;
   if (plan.ws_bytes > 0) {
     if (!workspace) return PA_ERR_NULL_ARG;
     if (workspace_bytes < plan.ws_bytes) return PA_ERR_WORKSPACE_TOO_SMALL;
@@ -214,7 +220,7 @@ pa_status attend_impl(const pa_shape* shape, const pa_kv_cache& kv, const void* 
   if (plan.decode) {
     const DecodeParams d = decode_params(shape, plan, kv, q, block_table, ctx_lens, q_lens, scale_log2,
                                          out, lse, static_cast<char*>(workspace));
-    if (launch_decode(d, plan.group, kv.format, plan.grid, s) != hipSuccess) return PA_ERR_LAUNCH;
+    if (launch_decode(d, plan.group, kv.format, plan.tokens, plan.grid, s) != hipSuccess) return PA_ERR_LAUNCH;
     return PA_OK;
   }
 
@@ -622,7 +628,7 @@ pa_status pa_attend_prefix(const pa_shape* shape, const pa_prefix_groups* groups
   d.pre_out = pr.pre_out;
   d.pre_lse = pr.pre_lse;
   d.pre_parts = pp.pre_grid > 0 ? pp.pre_parts : 0;
-  if (launch_decode(d, pp.suffix.group, kFmtBF16, pp.suffix.grid, s) != hipSuccess) return PA_ERR_LAUNCH;
+  if (launch_decode(d, pp.suffix.group, kFmtBF16, 1, pp.suffix.grid, s) != hipSuccess) return PA_ERR_LAUNCH;
   return PA_OK;
 }
 

@@ -17,8 +17,8 @@
 // token.
 //
 // Workgroup: 8 waves over 128 packed rows of one (slot, KV head).  Wave w
-// takes rows 32 (w % 4) .. +32 and one half of the keys (w / 4); the two
-// halves merge through LDS at the end.  Each half walks its keys in 32-key
+// takes the rows r with r % 4 == w % 4 (32 of them) and one half of the
+// keys (w / 4); the two halves merge through LDS at the end.  Each half walks its keys in 32-key
 // tiles (two 16-token pages):
 //   1. the tile's K and V rows go straight from memory into LDS
 //      (global_load_lds_dwordx4), row-major with XOR-swizzled 16-byte
@@ -128,7 +128,11 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkParams p) {
                "+s"(ids[6]), "+s"(ids[7]), "+s"(m), "+s"(n));
   if (m <= 0 || n <= 0 || qt * kChunkRows >= m * G) return;
   int q_row0 = 0;  // row offset of the slot, summed once the first tiles are requested
-  const int prow = qt * kChunkRows + rg * 32 + col;  // packed row within the slot
+  // Packed row within the slot: the tile's rows are dealt to the four row
+  // groups in turn (row 4 c + rg is column c of row group rg), so a tile
+  // with few live rows (a few tokens' grouped heads) still keeps every SIMD
+  // busy instead of leaving three row groups idle.
+  const int prow = qt * kChunkRows + 4 * col + rg;
   const bool row_live = prow < m * G;
   const int tok = row_live ? prow / G : 0;           // its token; rows past the end use token 0 of
   const int h = g * G + (row_live ? prow % G : 0);   // head g G (their results are never written)

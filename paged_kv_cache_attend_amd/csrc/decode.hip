@@ -212,22 +212,45 @@ __device__ __forceinline__ uint32_t hi_or_lo(float w0, float w1, uint32_t lo_mas
   return __builtin_amdgcn_perm(__float_as_uint(x1), __float_as_uint(x0), 0x07060302u);
 }
 
-template <int G>
+// Columns of the score tile.  A slot's (token, query head) pairs of one KV
+// head, token major -- column c is token c / G of query head g G + c % G --
+// for up to M tokens per slot: C = G M real columns.  When two copies fit in
+// a 16-column tile (2C <= 16, always so for one token with up to 8 heads per
+// KV head), columns C .. 2C - 1 repeat the queries and carry the lo halves of
+// the weights (see hi_or_lo); otherwise NT = ceil(C / 16) tiles of 16
+// columns take the bf16-rounded weights, and a column's output is divided by
+// the sum of those same rounded weights.
+template <int G, int M>
+struct Cols {
+  static constexpr int C = G * M;
+  static constexpr bool HL = 2 * C <= 16;
+  static constexpr int NT = HL ? 1 : (C + 15) / 16;
+  static constexpr int J = (C * kHeadDim / 2 + kDecodeThreads - 1) / kDecodeThreads;  // epilogue pairs per thread
+};
+
+template <int NT>
 struct WaveState {
-  float m_ref;    // reference max (log2 domain) of head lane % 16
-  float l_lane;   // this lane's share (tokens 4 (lane / 16) .. + 4 of each page) of that head's sum
-  f32x4_t o[8];   // O^T block b: dims 16 b + 4 (lane / 16) + i of head lane % 16
-  u32x4_t qb[4];  // Q^T operand of step s: dims 32 s + 8 (lane / 16) .. + 8 of head lane % 16
+  float m_ref[NT];    // reference max (log2 domain) of column 16 ct + lane % 16
+  float l_lane[NT];   // this lane's share (tokens 4 (lane / 16) .. + 4 of each page) of that column's sum
+  float r_lane[NT];   // the same over the bf16-rounded weights (tiles without lo columns)
+  f32x4_t o[NT][8];   // O^T block b: dims 16 b + 4 (lane / 16) + i of that column
+  u32x4_t qb[NT][4];  // Q^T operand of step s: dims 32 s + 8 (lane / 16) .. + 8 of that column
 };
 
 // `sk` / `sv` are this wave's 4 KiB LDS tiles, `sks` / `svs` its 16 x 4
-// group scales (q8_0, q4_0).
-template <int G, int F>
-__device__ __forceinline__ void consume_page(WaveState<G>& st, Page<F>& b, uint8_t* sk, uint8_t* sv,
-                                               float* sks, float* svs, int valid, float scale_log2, int lane) {
+// group scales (q8_0, q4_0).  `kbase` is the page's first key index and
+// lim[ct] the last key this lane's column of tile ct may see (several tokens
+// per slot only).
+template <int G, int F, int M>
+__device__ __forceinline__ void consume_page(WaveState<Cols<G, M>::NT>& st, Page<F>& b, uint8_t* sk, uint8_t* sv,
+                                               float* sks, float* svs, int valid, float scale_log2, int lane,
+                                               int kbase, const int* lim) {
+  using CS = Cols<G, M>;
+  constexpr int NT = CS::NT;
   const int pr = lane >> 4;
   const int pc = lane & 15;
   constexpr bool kGrouped = F == kFmtQ8 || F == kFmtQ4;
+  static_assert(!kGrouped || M == 1, "grouped page formats decode one token per slot");
 
   // K and V tiles -> LDS as bf16, row t keeping its 16-byte chunk c at slot
   // c ^ t.  V rows past the end are zeroed: their codes may decode to
@@ -248,7 +271,9 @@ __device__ __forceinline__ void consume_page(WaveState<G>& st, Page<F>& b, uint8
   // Scores: A = K (row = token pc, dims 32 s + 8 pr .. + 8 of step s), B = Q^T.
   // A group of 32 dims is one step, so grouped scales weight each step's
   // product (its own accumulator) before the sum.
-  f32x4_t s4 = {0.f, 0.f, 0.f, 0.f};
+  f32x4_t s4[NT];
+#pragma unroll
+  for (int ct = 0; ct < NT; ++ct) s4[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   if constexpr (kGrouped) {
     f32x4_t ksc[4];  // K scales of this lane's tokens 4 pr + i, groups 0..3
 #pragma unroll
@@ -256,46 +281,19 @@ __device__ __forceinline__ void consume_page(WaveState<G>& st, Page<F>& b, uint8
 #pragma unroll
     for (int sg = 0; sg < 4; ++sg) {
       const u32x4_t kf = *reinterpret_cast<const u32x4_t*>(sk + pc * 256 + (((4 * sg + pr) ^ pc) << 4));
-      const f32x4_t part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf), as_bf16x8(st.qb[sg]),
+      const f32x4_t part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf), as_bf16x8(st.qb[0][sg]),
                                                                    f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) s4[i] = fmaf(ksc[i][sg], part[i], s4[i]);
+      for (int i = 0; i < 4; ++i) s4[0][i] = fmaf(ksc[i][sg], part[i], s4[0][i]);
     }
   } else {
 #pragma unroll
     for (int sg = 0; sg < 4; ++sg) {
       const u32x4_t kf = *reinterpret_cast<const u32x4_t*>(sk + pc * 256 + (((4 * sg + pr) ^ pc) << 4));
-      s4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf), as_bf16x8(st.qb[sg]), s4, 0, 0, 0);
+#pragma unroll
+      for (int ct = 0; ct < NT; ++ct)
+        s4[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf), as_bf16x8(st.qb[ct][sg]), s4[ct], 0, 0, 0);
     }
-  }
-
-  // Online softmax of column pc over the page's 16 tokens (this lane holds
-  // tokens 4 pr .. + 4; the others sit in lanes ^ 16 and ^ 32).
-  float sl[4];
-  float mloc = -INFINITY;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    sl[i] = 4 * pr + i < valid ? s4[i] * scale_log2 : -INFINITY;
-    mloc = fmaxf(mloc, sl[i]);
-  }
-  mloc = fmaxf(mloc, other16(mloc));
-  mloc = fmaxf(mloc, other_half(mloc));
-  const bool raise = mloc > st.m_ref + kRescaleSlack;
-  if (__builtin_amdgcn_ballot_w64(raise) != 0) {
-    const float m_new = fmaxf(st.m_ref, mloc);
-    const float alpha = fast_exp2(st.m_ref - m_new);  // 0 on the first page (m_ref = -inf)
-    st.m_ref = m_new;
-    st.l_lane *= alpha;
-#pragma unroll
-    for (int bb = 0; bb < 8; ++bb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) st.o[bb][i] *= alpha;
-  }
-  float pw[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    pw[i] = fast_exp2(sl[i] - st.m_ref);  // 0 past the end
-    st.l_lane += pw[i];
   }
 
   // V^T operand of block bb (dims 16 bb .. + 16, tokens 4 pr .. + 4): lane a
@@ -309,46 +307,104 @@ __device__ __forceinline__ void consume_page(WaveState<G>& st, Page<F>& b, uint8
     vt[bb] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
         (lds_s16x4_t*)(vrow + (((2 * bb + ((pc & 3) >> 1)) ^ tv) << 4)));
 
-  // P^T operand: this lane's tokens 4 pr .. + 4 of column pc, as bf16 (hi
-  // in columns < G, lo in columns G .. 2G - 1); with grouped V scales one
-  // operand per 32-dim group (tokens past the end get weight 0 by select:
-  // their stored scales may be anything).
-  const uint32_t lo_mask = pc >= G ? 0xffff0000u : 0u;  // lanes that feed lo subtract hi
-  if constexpr (kGrouped) {
-    f32x4_t vsc[4];  // V scales of tokens 4 pr + i, groups 0..3
 #pragma unroll
-    for (int i = 0; i < 4; ++i) vsc[i] = *reinterpret_cast<const f32x4_t*>(svs + (4 * pr + i) * 4);
+  for (int ct = 0; ct < NT; ++ct) {
+    // Online softmax of column 16 ct + pc over the page's 16 tokens (this
+    // lane holds tokens 4 pr .. + 4; the others sit in lanes ^ 16 and ^ 32).
+    float sl[4];
+    float mloc = -INFINITY;
 #pragma unroll
-    for (int gr = 0; gr < 4; ++gr) {
-      float w[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) w[i] = 4 * pr + i < valid ? pw[i] * vsc[i][gr] : 0.f;
-      const s16x4_t pg = as_s16x4(hi_or_lo(w[0], w[1], lo_mask), hi_or_lo(w[2], w[3], lo_mask));
-#pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2)
-        st.o[2 * gr + h2] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt[2 * gr + h2], pg, st.o[2 * gr + h2], 0, 0, 0);
+    for (int i = 0; i < 4; ++i) {
+      const bool vis = 4 * pr + i < valid && (M == 1 || kbase + 4 * pr + i <= lim[ct]);
+      sl[i] = vis ? s4[ct][i] * scale_log2 : -INFINITY;
+      mloc = fmaxf(mloc, sl[i]);
     }
-  } else {
-    const s16x4_t pg = as_s16x4(hi_or_lo(pw[0], pw[1], lo_mask), hi_or_lo(pw[2], pw[3], lo_mask));
+    mloc = fmaxf(mloc, other16(mloc));
+    mloc = fmaxf(mloc, other_half(mloc));
+    const bool raise = mloc > st.m_ref[ct] + kRescaleSlack;
+    if (__builtin_amdgcn_ballot_w64(raise) != 0) {
+      const float m_new = fmaxf(st.m_ref[ct], mloc);
+      // 0 on the first page (m_ref = -inf).  With several tokens, a column
+      // that has seen no visible key yet keeps m = -inf (its sums are 0)
+      // while another column raises: guard -inf - -inf.
+      const float alpha = fast_exp2(st.m_ref[ct] - ((M > 1 && m_new == -INFINITY) ? 0.f : m_new));
+      st.m_ref[ct] = m_new;
+      st.l_lane[ct] *= alpha;
+      st.r_lane[ct] *= alpha;
 #pragma unroll
-    for (int bb = 0; bb < 8; ++bb) st.o[bb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt[bb], pg, st.o[bb], 0, 0, 0);
+      for (int bb = 0; bb < 8; ++bb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) st.o[ct][bb][i] *= alpha;
+    }
+    // With several tokens a column can meet a page with no visible key
+    // before any visible one (its reference max still -inf): weight 0.
+    const float m_use = (M > 1 && st.m_ref[ct] == -INFINITY) ? 0.f : st.m_ref[ct];
+    float pw[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      pw[i] = fast_exp2(sl[i] - m_use);  // 0 past the end
+      st.l_lane[ct] += pw[i];
+    }
+
+    // P^T operand: this lane's tokens 4 pr .. + 4 of its column, as bf16 (hi
+    // in columns < C and lo in columns C .. 2C - 1 when the tile holds both
+    // copies, else rounded to nearest); with grouped V scales one operand per
+    // 32-dim group (tokens past the end get weight 0 by select: their stored
+    // scales may be anything).
+    if constexpr (kGrouped) {
+      const uint32_t lo_mask = pc >= CS::C ? 0xffff0000u : 0u;  // lanes that feed lo subtract hi
+      f32x4_t vsc[4];  // V scales of tokens 4 pr + i, groups 0..3
+#pragma unroll
+      for (int i = 0; i < 4; ++i) vsc[i] = *reinterpret_cast<const f32x4_t*>(svs + (4 * pr + i) * 4);
+#pragma unroll
+      for (int gr = 0; gr < 4; ++gr) {
+        float w[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[i] = 4 * pr + i < valid ? pw[i] * vsc[i][gr] : 0.f;
+        const s16x4_t pg = as_s16x4(hi_or_lo(w[0], w[1], lo_mask), hi_or_lo(w[2], w[3], lo_mask));
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2)
+          st.o[0][2 * gr + h2] =
+              __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt[2 * gr + h2], pg, st.o[0][2 * gr + h2], 0, 0, 0);
+      }
+    } else {
+      s16x4_t pg;
+      if constexpr (CS::HL) {
+        const uint32_t lo_mask = pc >= CS::C ? 0xffff0000u : 0u;  // lanes that feed lo subtract hi
+        pg = as_s16x4(hi_or_lo(pw[0], pw[1], lo_mask), hi_or_lo(pw[2], pw[3], lo_mask));
+      } else {
+        const uint32_t w01 = pack_bf16x2(pw[0], pw[1]);
+        const uint32_t w23 = pack_bf16x2(pw[2], pw[3]);
+        st.r_lane[ct] += (bf16_lo(w01) + bf16_hi(w01)) + (bf16_lo(w23) + bf16_hi(w23));
+        pg = as_s16x4(w01, w23);
+      }
+#pragma unroll
+      for (int bb = 0; bb < 8; ++bb)
+        st.o[ct][bb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt[bb], pg, st.o[ct][bb], 0, 0, 0);
+    }
   }
 }
 
-template <int G, int F>
 #ifndef PA_DECODE_MIN_WGS
 #define PA_DECODE_MIN_WGS kDecodeWGsPerCU
 #endif
-__global__ __launch_bounds__(kDecodeThreads, PA_DECODE_MIN_WGS) void decode_kernel(DecodeParams p) {
-  static_assert(G == 1 || G == 2 || G == 4, "group size");
+template <int G, int F, int M>
+__global__ __launch_bounds__(kDecodeThreads, (Cols<G, M>::NT > 1 ? 1 : PA_DECODE_MIN_WGS)) void decode_kernel(
+    DecodeParams p) {
+  static_assert(G == 1 || G == 2 || G == 4 || G == 8, "group size");
+  using CS = Cols<G, M>;
+  constexpr int C = CS::C;
+  constexpr int NT = CS::NT;
+  static_assert(C <= 32, "at most two 16-column tiles");
   __shared__ __attribute__((aligned(16))) uint8_t s_k[kWaves][kTileBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t s_q[G][kHeadDim * 2];
+  __shared__ __attribute__((aligned(16))) uint8_t s_q[C][kHeadDim * 2];
   __shared__ __attribute__((aligned(16))) float s_ks[kWaves][kBlockSize * 4];  // q8_0 / q4_0 K scales
   __shared__ __attribute__((aligned(16))) uint8_t s_v[kWaves][kTileBytes];
   __shared__ __attribute__((aligned(16))) float s_vs[kWaves][kBlockSize * 4];    // q8_0 / q4_0 V scales
-  __shared__ __attribute__((aligned(16))) float s_acc[kWaves][G][kHeadDim];
-  __shared__ float s_m[kWaves][G];
-  __shared__ float s_l[kWaves][G];
+  __shared__ __attribute__((aligned(16))) float s_acc[kWaves][C][kHeadDim];
+  __shared__ float s_m[kWaves][C];
+  __shared__ float s_l[kWaves][C];
+  __shared__ float s_r[kWaves][C];
   __shared__ int s_last;
 
   const int lane = threadIdx.x & 63;
@@ -367,8 +423,8 @@ __global__ __launch_bounds__(kDecodeThreads, PA_DECODE_MIN_WGS) void decode_kern
 
   // Everything the start needs comes in one round trip, issued before the
   // first branch: the lengths, the prefix length, the slot's row offset (a
-  // vector load and a wave sum) and the page ids of this wave's first four
-  // pages as they are when the slot has no prefix (checked below, reloaded
+  // vector load and a wave sum) and the page ids of this wave's first pages
+  // as they are when the slot has no prefix (checked below, reloaded
   // otherwise).  Lengths and page ids are wave-uniform scalar loads, which do
   // not share the (in-order) vector load counter with the page stream.
   const int32_t* bt = p.block_table + (size_t)seq * p.max_blocks;
@@ -392,7 +448,7 @@ __global__ __launch_bounds__(kDecodeThreads, PA_DECODE_MIN_WGS) void decode_kern
   asm volatile("" : "+v"(qsum));
   if (m <= 0) return;  // no row: nothing to write, no partial to count
   const int npages = (n + kBlockSize - 1) / kBlockSize;
-  const int npre = (plen > 0 && n > 0) ? p.pre_parts : 0;
+  const int npre = (M == 1 && plen > 0 && n > 0) ? p.pre_parts : 0;
   const int pstart = plen / kBlockSize + part * p.part_pages;
   const int pend = part == P - 1 ? npages : min(npages, pstart + p.part_pages);
   const bool has_work = n > 0 && pstart < pend;
@@ -408,10 +464,6 @@ __global__ __launch_bounds__(kDecodeThreads, PA_DECODE_MIN_WGS) void decode_kern
 
   const int h0 = g * G;
   const size_t rows = (size_t)p.total_q * p.num_q_heads;
-  const int my_h = (threadIdx.x * 2) / kHeadDim;  // epilogue role: 2 dims of one head
-  const int my_d = (threadIdx.x * 2) % kHeadDim;
-  const bool my_out = threadIdx.x * 2 < G * kHeadDim;
-  float my_o0 = 0.f, my_o1 = 0.f, my_lse = -INFINITY;  // this workgroup's partial
 
   // Prologue, in issue order: the wave's first page, the query (so that its
   // wait only covers that first page, needed next anyway), then pages 1 ..
@@ -427,36 +479,65 @@ __global__ __launch_bounds__(kDecodeThreads, PA_DECODE_MIN_WGS) void decode_kern
     issue_page<F>(ring[0], p, first_id(0), g, lane);
     __builtin_amdgcn_sched_barrier(0);  // the first page goes out before the row-offset sum
     q_row = __builtin_amdgcn_readfirstlane(wave_sum_i32(qsum));
-    const int qh = (threadIdx.x >> 4) % G, qc = threadIdx.x & 15;
-    const u32x4_t qchunk =
-        reinterpret_cast<const u32x4_t*>(p.q)[((size_t)q_row * p.num_q_heads + h0 + qh) * 16 + qc];
+    // The queries of the C columns: 16-byte chunk qc of column c; tokens
+    // past the slot's m read its last token (their columns are zeroed below).
+    constexpr int kQChunks = (C * 16 + kDecodeThreads - 1) / kDecodeThreads;
+    u32x4_t qchunk[kQChunks];
+#pragma unroll
+    for (int j = 0; j < kQChunks; ++j) {
+      const int idx = threadIdx.x + j * kDecodeThreads;
+      const int c = min(idx >> 4, C - 1), qc = idx & 15;
+      const int tok = min(c / G, m - 1);
+      qchunk[j] = reinterpret_cast<const u32x4_t*>(p.q)[((size_t)(q_row + tok) * p.num_q_heads + h0 + c % G) * 16 + qc];
+    }
     issue_order_barrier();
 #pragma unroll
     for (int r = 1; r < kRing; ++r) issue_page<F>(ring[r], p, first_id(r), g, lane);
     next_id = first_id(kRing);
-    // Query of heads h0 .. h0+G-1 -> LDS, 16-byte chunk c of head h at slot c ^ h.
-    if (threadIdx.x < G * 16) *reinterpret_cast<u32x4_t*>(&s_q[qh][(qc ^ qh) << 4]) = qchunk;
+    // Queries -> LDS, 16-byte chunk qc of column c at slot qc ^ (c % 16).
+#pragma unroll
+    for (int j = 0; j < kQChunks; ++j) {
+      const int idx = threadIdx.x + j * kDecodeThreads;
+      const int c = idx >> 4, qc = idx & 15;
+      if (c < C) *reinterpret_cast<u32x4_t*>(&s_q[c][(qc ^ (c & 15)) << 4]) = qchunk[j];
+    }
     __syncthreads();
   } else {
     q_row = __builtin_amdgcn_readfirstlane(wave_sum_i32(qsum));
   }
 
-  if (has_work) {
-    WaveState<G> st;
-    st.m_ref = -INFINITY;
-    st.l_lane = 0.f;
+  // This lane's column per tile: its real column (the lo copy maps back to
+  // the hi one), whether that column is a live token, and the last key it
+  // may see (causal: token t of m sees keys up to n - m + t).
+  const int pr = lane >> 4;
+  const int pc = lane & 15;
+  int col[NT];
+  bool col_live[NT];
+  int lim[NT];
 #pragma unroll
-    for (int bb = 0; bb < 8; ++bb) st.o[bb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    // Q^T operand from the staged query (head h keeps chunk c at slot c ^ h):
-    // column n < 2G holds query head n % G (the second copy carries the lo
-    // weights of PV); columns from 2G on get a zero query.
-    {
-      const int qn = lane & 15, qr = lane >> 4;
-      const int qh = qn & (G - 1);
+  for (int ct = 0; ct < NT; ++ct) {
+    const int n16 = ct * 16 + pc;
+    col[ct] = CS::HL ? (n16 & (C - 1)) : n16;
+    const bool in_tile = CS::HL ? n16 < 2 * C : n16 < C;
+    col_live[ct] = in_tile && col[ct] / G < m;
+    lim[ct] = p.causal ? n - m + col[ct] / G : n - 1;
+  }
+
+  if (has_work) {
+    WaveState<NT> st;
+#pragma unroll
+    for (int ct = 0; ct < NT; ++ct) {
+      st.m_ref[ct] = -INFINITY;
+      st.l_lane[ct] = 0.f;
+      st.r_lane[ct] = 0.f;
+#pragma unroll
+      for (int bb = 0; bb < 8; ++bb) st.o[ct][bb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      // Q^T operand from the staged queries; dead columns get a zero query.
+      const int c = min(col[ct], C - 1);
 #pragma unroll
       for (int sg = 0; sg < 4; ++sg) {
-        const u32x4_t x = *reinterpret_cast<const u32x4_t*>(&s_q[qh][((4 * sg + qr) ^ qh) << 4]);
-        st.qb[sg] = qn < 2 * G ? x : u32x4_t{0u, 0u, 0u, 0u};
+        const u32x4_t x = *reinterpret_cast<const u32x4_t*>(&s_q[c][((4 * sg + pr) ^ (c & 15)) << 4]);
+        st.qb[ct][sg] = col_live[ct] ? x : u32x4_t{0u, 0u, 0u, 0u};
       }
     }
 
@@ -470,7 +551,9 @@ __global__ __launch_bounds__(kDecodeThreads, PA_DECODE_MIN_WGS) void decode_kern
     // wait leaves the other kRing - 1 pages in flight; the last pages are
     // peeled off.
     auto valid_of = [&](int k) { return min(kBlockSize, n - (page0 + kWaves * k) * kBlockSize); };
-#define PA_CONSUME(RING, K) consume_page<G, F>(st, RING, sk, sv, sks, svs, valid_of(K), p.scale_log2, lane)
+#define PA_CONSUME(RING, K)                                                                            \
+  consume_page<G, F, M>(st, RING, sk, sv, sks, svs, valid_of(K), p.scale_log2, lane,                   \
+                        (page0 + kWaves * (K)) * kBlockSize, lim)
 #define PA_REISSUE(RING, K)                                          \
   {                                                                  \
     issue_page<F>(RING, p, next_id, g, lane);                        \
@@ -499,72 +582,105 @@ __global__ __launch_bounds__(kDecodeThreads, PA_DECODE_MIN_WGS) void decode_kern
 #undef PA_CONSUME
 #undef PA_REISSUE
 
-    // Per-wave state -> LDS.  Column pc's sum is spread over lanes pc + 16 j;
+    // Per-wave state -> LDS.  A column's sum is spread over lanes pc + 16 j;
     // its O^T block values are dims 16 b + 4 pr + i, to which the lo column
-    // pc + G (lane ^ G, since pc < G and G is a power of two) is added.
-    // FP8's V scale applies here, once.
-    const int pr = lane >> 4;
-    const int pc = lane & 15;
-    float l_sum = st.l_lane + other16(st.l_lane);
-    l_sum += other_half(l_sum);
+    // (lane ^ C, since pc < C and C is a power of two) is added when the tile
+    // holds one.  FP8's V scale applies here, once.
     const float vs = F == kFmtFP8 ? p.v_scale : 1.f;
-    f32x4_t o_tot[8];
 #pragma unroll
-    for (int bb = 0; bb < 8; ++bb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) o_tot[bb][i] = st.o[bb][i] + __shfl_xor(st.o[bb][i], G, 64);
-    if (pc < G) {
-      if (pr == 0) {
-        s_m[wave][pc] = st.m_ref;
-        s_l[wave][pc] = l_sum;
-      }
+    for (int ct = 0; ct < NT; ++ct) {
+      float l_sum = st.l_lane[ct] + other16(st.l_lane[ct]);
+      l_sum += other_half(l_sum);
+      float r_sum = st.r_lane[ct] + other16(st.r_lane[ct]);
+      r_sum += other_half(r_sum);
+      f32x4_t o_tot[8];
 #pragma unroll
       for (int bb = 0; bb < 8; ++bb)
-        *reinterpret_cast<f32x4_t*>(&s_acc[wave][pc][16 * bb + 4 * pr]) = o_tot[bb] * vs;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          o_tot[bb][i] = CS::HL ? st.o[ct][bb][i] + __shfl_xor(st.o[ct][bb][i], C, 64) : st.o[ct][bb][i];
+      const int c = ct * 16 + pc;
+      if (c < C) {
+        if (pr == 0) {
+          s_m[wave][c] = st.m_ref[ct];
+          s_l[wave][c] = l_sum;
+          s_r[wave][c] = CS::HL ? l_sum : r_sum;
+        }
+#pragma unroll
+        for (int bb = 0; bb < 8; ++bb)
+          *reinterpret_cast<f32x4_t*>(&s_acc[wave][c][16 * bb + 4 * pr]) = o_tot[bb] * vs;
+      }
     }
     __syncthreads();
-
-    // Merge the waves: two adjacent dims of one head per thread.
-    if (my_out) {
-      const int h = my_h, d = my_d;
-      float M = -INFINITY;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_m[w][h]);
-      float L = 0.f, a0 = 0.f, a1 = 0.f;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        const float sc = fast_exp2(s_m[w][h] - M);  // 0 for a wave with no page
-        L = fmaf(sc, s_l[w][h], L);
-        const float2 v = *reinterpret_cast<const float2*>(&s_acc[w][h][d]);
-        a0 = fmaf(sc, v.x, a0);
-        a1 = fmaf(sc, v.y, a1);
-      }
-      const float inv = 1.f / L;
-      my_o0 = a0 * inv;
-      my_o1 = a1 * inv;
-      my_lse = (M + fast_log2(L)) * kLn2;  // natural log
-    }
   }
 
-  if (P == 1) {
-    if (!my_out) return;
-    const size_t row = (size_t)q_row * p.num_q_heads + h0 + my_h;
-    if (npre == 0) {
-      if (has_work) {
-        reinterpret_cast<uint32_t*>(p.out)[(row * kHeadDim + my_d) / 2] = pack_bf16x2(my_o0, my_o1);
-        if (my_d == 0 && p.lse) p.lse[row] = my_lse;
+  // Epilogue: each thread takes J (column, dim pair) outputs: pair i covers
+  // dims 2 (i % 64) .. + 2 of column i / 64, token c / G, head h0 + c % G.
+  constexpr int J = CS::J;
+  float my_o0[J], my_o1[J], my_lse[J];
+  int my_c[J], my_d[J];
+  bool my_out[J];
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int i = threadIdx.x + j * kDecodeThreads;
+    my_c[j] = min(i >> 6, C - 1);
+    my_d[j] = (i & 63) * 2;
+    my_out[j] = i < C * 64 && my_c[j] / G < m;
+    my_o0[j] = 0.f;
+    my_o1[j] = 0.f;
+    my_lse[j] = -INFINITY;
+    if (has_work && my_out[j]) {
+      // Merge the waves (a wave with no page, or whose keys this column
+      // cannot see, has max -inf and weight 0).
+      const int c = my_c[j], d = my_d[j];
+      float Mx = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) Mx = fmaxf(Mx, s_m[w][c]);
+      if (Mx != -INFINITY) {
+        float L = 0.f, R = 0.f, a0 = 0.f, a1 = 0.f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+          const float sc = fast_exp2(s_m[w][c] - Mx);
+          L = fmaf(sc, s_l[w][c], L);
+          R = fmaf(sc, s_r[w][c], R);
+          const float2 v = *reinterpret_cast<const float2*>(&s_acc[w][c][d]);
+          a0 = fmaf(sc, v.x, a0);
+          a1 = fmaf(sc, v.y, a1);
+        }
+        const float inv = 1.f / R;
+        my_o0[j] = a0 * inv;
+        my_o1[j] = a1 * inv;
+        my_lse[j] = (Mx + fast_log2(L)) * kLn2;  // natural log
       }
-      return;
     }
-    // Own result and the prefix pass's partials of this row (written by the
-    // previous launch).
-    MergeState ms;
-    if (has_work) merge_fold(ms, my_lse, my_o0, my_o1);
-    merge_partials(ms, nullptr, nullptr, 0, p.pre_lse + row, p.pre_out + row * kHeadDim + my_d, npre, rows);
-    if (ms.M != -INFINITY) {
-      const float inv = 1.f / ms.W;
-      reinterpret_cast<uint32_t*>(p.out)[(row * kHeadDim + my_d) / 2] = pack_bf16x2(ms.a0 * inv, ms.a1 * inv);
-      if (my_d == 0 && p.lse) p.lse[row] = ms.M + fast_log2(ms.W) * kLn2;
+  }
+  auto row_of = [&](int j) -> size_t {
+    return (size_t)(q_row + my_c[j] / G) * p.num_q_heads + h0 + my_c[j] % G;
+  };
+
+  if (P == 1) {
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      if (!my_out[j]) continue;
+      const size_t row = row_of(j);
+      const int d = my_d[j];
+      if (npre == 0) {
+        if (my_lse[j] != -INFINITY) {
+          reinterpret_cast<uint32_t*>(p.out)[(row * kHeadDim + d) / 2] = pack_bf16x2(my_o0[j], my_o1[j]);
+          if (d == 0 && p.lse) p.lse[row] = my_lse[j];
+        }
+        continue;
+      }
+      // Own result and the prefix pass's partials of this row (written by the
+      // previous launch).
+      MergeState ms;
+      if (has_work) merge_fold(ms, my_lse[j], my_o0[j], my_o1[j]);
+      merge_partials(ms, nullptr, nullptr, 0, p.pre_lse + row, p.pre_out + row * kHeadDim + d, npre, rows);
+      if (ms.M != -INFINITY) {
+        const float inv = 1.f / ms.W;
+        reinterpret_cast<uint32_t*>(p.out)[(row * kHeadDim + d) / 2] = pack_bf16x2(ms.a0 * inv, ms.a1 * inv);
+        if (d == 0 && p.lse) p.lse[row] = ms.M + fast_log2(ms.W) * kLn2;
+      }
     }
     return;
   }
@@ -587,13 +703,16 @@ __global__ __launch_bounds__(kDecodeThreads, PA_DECODE_MIN_WGS) void decode_kern
   // This avoids device-scope release/acquire fences, which on this chip
   // write back and invalidate the whole L2 of the XCD.
   uint64_t* part_out64 = reinterpret_cast<uint64_t*>(p.part_out);
-  if (my_out) {
-    const size_t prow = (size_t)part * rows + (size_t)q_row * p.num_q_heads + h0 + my_h;
-    if (has_work) {
-      const uint64_t bits = (uint64_t)__float_as_uint(my_o0) | ((uint64_t)__float_as_uint(my_o1) << 32);
-      __hip_atomic_store(part_out64 + (prow * kHeadDim + my_d) / 2, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    if (!my_out[j]) continue;
+    const size_t prow = (size_t)part * rows + row_of(j);
+    if (my_lse[j] != -INFINITY) {
+      const uint64_t bits = (uint64_t)__float_as_uint(my_o0[j]) | ((uint64_t)__float_as_uint(my_o1[j]) << 32);
+      __hip_atomic_store(part_out64 + (prow * kHeadDim + my_d[j]) / 2, bits, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
     }
-    if (my_d == 0) __hip_atomic_store(p.part_lse + prow, my_lse, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (my_d[j] == 0) __hip_atomic_store(p.part_lse + prow, my_lse[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   wait_vm_stores();
   __syncthreads();
@@ -607,15 +726,18 @@ __global__ __launch_bounds__(kDecodeThreads, PA_DECODE_MIN_WGS) void decode_kern
   // prefix, the prefix pass's npre, their loads issued in batches before any
   // is used; a partial with LSE = -inf (empty) gets weight 0 without its
   // output being read.
-  if (my_out) {
-    const size_t row = (size_t)q_row * p.num_q_heads + h0 + my_h;
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    if (!my_out[j]) continue;
+    const size_t row = row_of(j);
+    const int d = my_d[j];
     MergeState ms;
-    merge_partials(ms, p.part_lse + row, p.part_out + row * kHeadDim + my_d, P,
-                   p.pre_lse + row, p.pre_out + row * kHeadDim + my_d, npre, rows);
+    merge_partials(ms, p.part_lse + row, p.part_out + row * kHeadDim + d, P, p.pre_lse + row,
+                   p.pre_out + row * kHeadDim + d, npre, rows);
     if (ms.M != -INFINITY) {
       const float inv = 1.f / ms.W;
-      reinterpret_cast<uint32_t*>(p.out)[(row * kHeadDim + my_d) / 2] = pack_bf16x2(ms.a0 * inv, ms.a1 * inv);
-      if (my_d == 0 && p.lse) p.lse[row] = ms.M + fast_log2(ms.W) * kLn2;
+      reinterpret_cast<uint32_t*>(p.out)[(row * kHeadDim + d) / 2] = pack_bf16x2(ms.a0 * inv, ms.a1 * inv);
+      if (d == 0 && p.lse) p.lse[row] = ms.M + fast_log2(ms.W) * kLn2;
     }
   }
   // Leave the counter at zero for the next call (the next launch sees it).
@@ -629,25 +751,43 @@ __global__ __launch_bounds__(256) void zero_kernel(int32_t* __restrict__ x, size
 
 }  // namespace
 
-bool decode_supports_group(int group) { return group == 1 || group == 2 || group == 4; }
+bool decode_supports_group(int group) { return group == 1 || group == 2 || group == 4 || group == 8; }
 
-template <int F>
+int decode_tokens_per_slot(int group, int max_q_len) {
+  if (!decode_supports_group(group) || max_q_len < 1) return 0;
+  for (int mt = 1; mt <= 8; mt *= 2)
+    if (max_q_len <= mt) return group * mt <= 32 ? mt : 0;
+  return 0;
+}
+
+template <int F, int M>
 const void* decode_entry(int group) {
   switch (group) {
-    case 1: return reinterpret_cast<const void*>(&decode_kernel<1, F>);
-    case 2: return reinterpret_cast<const void*>(&decode_kernel<2, F>);
-    case 4: return reinterpret_cast<const void*>(&decode_kernel<4, F>);
+    case 1: return reinterpret_cast<const void*>(&decode_kernel<1, F, M>);
+    case 2: return reinterpret_cast<const void*>(&decode_kernel<2, F, M>);
+    case 4: return reinterpret_cast<const void*>(&decode_kernel<4, F, M>);
+    case 8:
+      if constexpr (M <= 4) return reinterpret_cast<const void*>(&decode_kernel<8, F, M>);
+      return nullptr;
   }
   return nullptr;
 }
 
-hipError_t launch_decode(const DecodeParams& p, int group, int format, unsigned grid, hipStream_t s) {
+hipError_t launch_decode(const DecodeParams& p, int group, int format, int tokens, unsigned grid, hipStream_t s) {
   const void* fn = nullptr;
-  switch (format) {
-    case kFmtBF16: fn = decode_entry<kFmtBF16>(group); break;
-    case kFmtFP8: fn = decode_entry<kFmtFP8>(group); break;
-    case kFmtQ8: fn = decode_entry<kFmtQ8>(group); break;
-    case kFmtQ4: fn = decode_entry<kFmtQ4>(group); break;
+  if (tokens == 1) {
+    switch (format) {
+      case kFmtBF16: fn = decode_entry<kFmtBF16, 1>(group); break;
+      case kFmtFP8: fn = decode_entry<kFmtFP8, 1>(group); break;
+      case kFmtQ8: fn = decode_entry<kFmtQ8, 1>(group); break;
+      case kFmtQ4: fn = decode_entry<kFmtQ4, 1>(group); break;
+    }
+  } else if (format == kFmtBF16) {
+    switch (tokens) {
+      case 2: fn = decode_entry<kFmtBF16, 2>(group); break;
+      case 4: fn = decode_entry<kFmtBF16, 4>(group); break;
+      case 8: fn = decode_entry<kFmtBF16, 8>(group); break;
+    }
   }
   if (!fn) return hipErrorInvalidValue;
   DecodeParams arg = p;

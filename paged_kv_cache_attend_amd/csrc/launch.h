@@ -59,6 +59,7 @@ struct DecodeParams {
   int32_t total_q;
   int32_t part_pages;         // 16-token pages per partition
   int32_t num_parts;
+  int32_t causal;             // several tokens per slot: token t of m sees keys [0, n - m + t]
 };
 
 // Chunk path (several new rows per slot): bf16 MFMA for S = QK^T and O = PV.
@@ -119,10 +120,14 @@ struct ValidateParams {
   int32_t total_q;
 };
 
-// Decode kernels exist for these query-per-KV head group sizes.
+// Decode kernels exist for these query-per-KV head group sizes, and for up
+// to 8 new tokens per slot (bf16 pages) while tokens x group <= 32.
 bool decode_supports_group(int group);
+// Tokens per slot the decode kernel is built for that cover max_q_len
+// (1, 2, 4 or 8), or 0 when the decode path does not apply.
+int decode_tokens_per_slot(int group, int max_q_len);
 constexpr int kDecodeThreads = 64 * kDecodeWaves;
-hipError_t launch_decode(const DecodeParams& p, int group, int format, unsigned grid, hipStream_t s);
+hipError_t launch_decode(const DecodeParams& p, int group, int format, int tokens, unsigned grid, hipStream_t s);
 hipError_t launch_zero_i32(int32_t* x, size_t n, hipStream_t s);
 
 constexpr int kChunkRows = 128;  // query rows per chunk workgroup

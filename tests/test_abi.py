@@ -355,7 +355,7 @@ def test_prefix_workspace_size(lib):
                 _groups(num_groups=-1), _groups(min_prefix_len=-16)):
         assert size(s, bad) == 0
     assert lib.pa_prefix_workspace_size(ctypes.byref(s), None) == 0
-    assert size(_shape(num_q_heads=64), _groups()) == 0       # 8 query heads per KV head
+    assert size(_shape(num_q_heads=128), _groups()) == 0      # 16 query heads per KV head
     assert size(_shape(total_q=8, max_q_len=2), _groups()) == 0
 
 
@@ -378,7 +378,7 @@ def test_attend_prefix_host_errors(lib):
     assert call(scale=math.nan) == pk.Status.ERR_BAD_SHAPE
     assert call(groups=_groups(reserved=1)) == pk.Status.ERR_BAD_SHAPE
     assert call(groups=_groups(max_prefix_len=24)) == pk.Status.ERR_BAD_SHAPE
-    assert call(shape=_shape(num_q_heads=64)) == pk.Status.ERR_UNSUPPORTED
+    assert call(shape=_shape(num_q_heads=128)) == pk.Status.ERR_UNSUPPORTED
     assert call(shape=_shape(total_q=8, max_q_len=2)) == pk.Status.ERR_UNSUPPORTED
     empty = _shape(num_seqs=0, total_q=0)
     assert call(shape=empty, groups=_groups(num_groups=0, max_members=0), ws=None, ws_bytes=0) == pk.Status.OK

@@ -314,10 +314,29 @@ def test_speculative_verification(num_tokens):
     compare(p, run_gpu(p), run_oracle(p), label=f"spec verify m={num_tokens}")
 
 
-def test_chunk_path_handles_group_sizes_without_decode_kernel():
-    # 8 query heads per KV head with one row each takes the MFMA path
+def test_decode_with_eight_query_heads_per_kv_head():
+    # G = 8: eight hi and eight lo columns fill the decode kernel's tile
     p = _case([37, 100, 1000], hq=64, hkv=8, seed=43)
-    compare(p, run_gpu(p), run_oracle(p), label="G=8 decode via chunk path")
+    assert pk.plan(pk.make_shape(p.num_seqs, p.total_q, 64, 8, p.max_blocks_per_seq, 1, p.max_ctx_len,
+                                 p.num_blocks))[0] >= 0
+    compare(p, run_gpu(p), run_oracle(p), label="G=8 decode")
+
+
+@pytest.mark.parametrize("hq,hkv", [(8, 8), (4, 2), (8, 2), (32, 8), (16, 2)])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("ps", [0, 16, 4096])
+def test_multi_token_decode(hq, hkv, causal, ps):
+    # several new tokens per slot on the page-streaming decode path (tokens
+    # x group <= 32): ragged lengths, token counts below the slot maximum,
+    # a zombie, a slot without new tokens, the last page partly filled
+    G = hq // hkv
+    mmax = max(1, min(8, 32 // G))
+    ctx = [37, 100, 1000, 17, 2303, 0, 64, 500]
+    ql = [min(mmax, x) for x in (1, 3, mmax, 2, mmax, 1, 0, max(1, mmax - 1))]
+    p = _case(ctx, ql, hq=hq, hkv=hkv, seed=hq * 7 + hkv + mmax, causal=causal)
+    say(f"multi-token decode {hq}/{hkv} m<={mmax} causal={causal} ps={ps}")
+    compare(p, run_gpu(p, partition_size=ps), run_oracle(p),
+            label=f"multi-token {hq}/{hkv} m<={mmax} causal={causal} ps={ps}")
 
 
 # ---------------------------------------------------------------------------
