@@ -44,6 +44,8 @@
 //      takes the sum of the fp32 weights.
 // Keys past the end load the last key (finite) and get -inf scores.
 
+#include <type_traits>
+
 #include "device.h"
 
 namespace pa {
@@ -153,6 +155,9 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkParams p) {
   const int ntiles = (kv_end + kTileKeys - 1) / kTileKeys;
   const int T = (ntiles + 1) / 2;       // tiles per half (both halves loop T times)
   const int my_limit = p.causal ? (n - m + tok) : (n - 1);  // last visible key of this row
+  // Tiles ending at or before this key count are visible to every row of the
+  // workgroup (under the causal mask: to the tile's first token).
+  const int open_end = p.causal ? min(kv_end, n - m + (qt * kChunkRows) / G + 1) : kv_end;
   if (m != p.max_q || n != p.max_ctx) request_ids(tile0, last_page);
 
   // Loads straight into LDS (global_load_lds_dwordx4: lane l of a wave
@@ -203,9 +208,12 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkParams p) {
   float l_run = 0.f;        // this lane's share of the row sum (fp32 weights)
   float r_run = 0.f;        // the same over the bf16-rounded weights PV uses
 
-  auto compute_tile = [&](int it, int stage) {
+  // The stage is a compile-time constant (the loop below is unrolled by the
+  // ring depth), so every LDS address is a per-lane register plus an
+  // immediate offset.
+  auto compute_tile = [&](int it, auto stage_c) {
+    constexpr int stage = decltype(stage_c)::value;
     const uint8_t* sk = s_buf[kh][stage][0];
-    const uint8_t* svv = s_buf[kh][stage][1];
     // S^T = K Q^T: A = K rows (key = col), B = Q^T (row = col).
     f32x16_t st;
 #pragma unroll
@@ -234,7 +242,9 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkParams p) {
     // 4096 bytes further with the same swizzle; key + 8 has its own address.
     const int grp16 = lane >> 4;
     const int a16 = lane & 15;
-    const uint32_t vbase = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)svv;
+    // (stage 0's V tile; the stage is the reads' immediate offset)
+    const uint32_t vbase = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)s_buf[kh][0][1];
+    constexpr int voff = stage * 2 * kTileBytes;
     u32x2_t vr[16];  // vr[4 mb + 2 ks + e]: keys 16 ks + 8 e + 4 hh + 0..3
     {
       uint32_t va[8];  // va[2 mb + e]: key 8 e + 4 hh + a / 4, 4 dims of block mb
@@ -244,54 +254,55 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkParams p) {
         for (int e = 0; e < 2; ++e)
           va[2 * mb + e] = vbase + swz(8 * e + 4 * hh + (a16 >> 2), mb * 32 + (grp16 & 1) * 16 + 4 * (a16 & 3));
       asm volatile(
-          "ds_read_b64_tr_b16 %0, %16\n\t"
-          "ds_read_b64_tr_b16 %1, %17\n\t"
-          "ds_read_b64_tr_b16 %2, %16 offset:4096\n\t"
-          "ds_read_b64_tr_b16 %3, %17 offset:4096\n\t"
-          "ds_read_b64_tr_b16 %4, %18\n\t"
-          "ds_read_b64_tr_b16 %5, %19\n\t"
-          "ds_read_b64_tr_b16 %6, %18 offset:4096\n\t"
-          "ds_read_b64_tr_b16 %7, %19 offset:4096\n\t"
-          "ds_read_b64_tr_b16 %8, %20\n\t"
-          "ds_read_b64_tr_b16 %9, %21\n\t"
-          "ds_read_b64_tr_b16 %10, %20 offset:4096\n\t"
-          "ds_read_b64_tr_b16 %11, %21 offset:4096\n\t"
-          "ds_read_b64_tr_b16 %12, %22\n\t"
-          "ds_read_b64_tr_b16 %13, %23\n\t"
-          "ds_read_b64_tr_b16 %14, %22 offset:4096\n\t"
-          "ds_read_b64_tr_b16 %15, %23 offset:4096"
+          "ds_read_b64_tr_b16 %0, %16 offset:%24\n\t"
+          "ds_read_b64_tr_b16 %1, %17 offset:%24\n\t"
+          "ds_read_b64_tr_b16 %2, %16 offset:%25\n\t"
+          "ds_read_b64_tr_b16 %3, %17 offset:%25\n\t"
+          "ds_read_b64_tr_b16 %4, %18 offset:%24\n\t"
+          "ds_read_b64_tr_b16 %5, %19 offset:%24\n\t"
+          "ds_read_b64_tr_b16 %6, %18 offset:%25\n\t"
+          "ds_read_b64_tr_b16 %7, %19 offset:%25\n\t"
+          "ds_read_b64_tr_b16 %8, %20 offset:%24\n\t"
+          "ds_read_b64_tr_b16 %9, %21 offset:%24\n\t"
+          "ds_read_b64_tr_b16 %10, %20 offset:%25\n\t"
+          "ds_read_b64_tr_b16 %11, %21 offset:%25\n\t"
+          "ds_read_b64_tr_b16 %12, %22 offset:%24\n\t"
+          "ds_read_b64_tr_b16 %13, %23 offset:%24\n\t"
+          "ds_read_b64_tr_b16 %14, %22 offset:%25\n\t"
+          "ds_read_b64_tr_b16 %15, %23 offset:%25"
           : "=&v"(vr[0]), "=&v"(vr[1]), "=&v"(vr[2]), "=&v"(vr[3]), "=&v"(vr[4]), "=&v"(vr[5]), "=&v"(vr[6]),
             "=&v"(vr[7]), "=&v"(vr[8]), "=&v"(vr[9]), "=&v"(vr[10]), "=&v"(vr[11]), "=&v"(vr[12]),
             "=&v"(vr[13]), "=&v"(vr[14]), "=&v"(vr[15])
-          : "v"(va[0]), "v"(va[1]), "v"(va[2]), "v"(va[3]), "v"(va[4]), "v"(va[5]), "v"(va[6]), "v"(va[7]));
+          : "v"(va[0]), "v"(va[1]), "v"(va[2]), "v"(va[3]), "v"(va[4]), "v"(va[5]), "v"(va[6]), "v"(va[7]),
+            "i"(voff), "i"(voff + 4096));
     }
 
     // Online softmax over this lane's 16 keys of its row (log2 domain).
-    // When every key of the tile is visible to every row (no causal mask, the
-    // tile inside the keys, a positive scale) the scores need no masking and
-    // the scale folds into the exponent's FMA.
+    // The scale folds into the exponent's FMA (and into the max, taken over
+    // the raw scores); masked keys become -inf in place.  Tiles that every
+    // row of the workgroup sees whole skip the masking.  A scale that is not positive would turn the max of the raw
+    // scores into the min of the scaled ones, so then the masking pass
+    // applies the scale itself and the FMA multiplies by 1.
     const int kbase = (tile0 + it) * kTileKeys + 4 * hh;
-    const bool open = !p.causal && (tile0 + it + 1) * kTileKeys <= kv_end && p.scale_log2 > 0.f;
-    float sv[16];
-    float mloc = -INFINITY;
-    if (open) {
+    const bool pos = p.scale_log2 > 0.f;
+    const float sc = pos ? p.scale_log2 : 1.f;
+    if ((tile0 + it + 1) * kTileKeys > open_end || !pos) {
+      if (!pos) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        sv[i] = st[i];
-        mloc = fmaxf(mloc, sv[i]);
+        for (int i = 0; i < 16; ++i) st[i] *= p.scale_log2;
       }
-      mloc *= p.scale_log2;
-    } else {
 #pragma unroll
       for (int a = 0; a < 4; ++a)
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
           const int key = kbase + 8 * a + b;
-          const float x = (it < T && key <= my_limit) ? st[4 * a + b] * p.scale_log2 : -INFINITY;
-          sv[4 * a + b] = x;
-          mloc = fmaxf(mloc, x);
+          if (key > my_limit) st[4 * a + b] = -INFINITY;
         }
     }
+    float mloc = st[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) mloc = fmaxf(mloc, st[i]);
+    mloc *= sc;
     mloc = fmaxf(mloc, other_half(mloc));
     const bool raise = mloc > m_run + kRescaleSlack;
     if (__builtin_amdgcn_ballot_w64(raise) != 0) {
@@ -309,31 +320,24 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkParams p) {
     }
     const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
     float lsum = 0.f;
-    if (open) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        sv[i] = fast_exp2(fmaf(sv[i], p.scale_log2, -m_use));
-        lsum += sv[i];
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        sv[i] = fast_exp2(sv[i] - m_use);
-        lsum += sv[i];
-      }
+    for (int i = 0; i < 16; ++i) {
+      st[i] = fast_exp2(fmaf(st[i], sc, -m_use));
+      lsum += st[i];
     }
     l_run += lsum;
     // P^T operand for key steps 0 and 1: keys 16ks + 4hh + 0..3, 16ks + 8 + 4hh + 0..3.
+    // The sum of the rounded weights is a dot product of each packed pair
+    // with (1, 1): exact products, fp32 sums.
     u32x4_t pf[2];
     float rsum = 0.f;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      pf[ks][0] = pack_bf16x2(sv[8 * ks + 0], sv[8 * ks + 1]);
-      pf[ks][1] = pack_bf16x2(sv[8 * ks + 2], sv[8 * ks + 3]);
-      pf[ks][2] = pack_bf16x2(sv[8 * ks + 4], sv[8 * ks + 5]);
-      pf[ks][3] = pack_bf16x2(sv[8 * ks + 6], sv[8 * ks + 7]);
 #pragma unroll
-      for (int w = 0; w < 4; ++w) rsum += bf16_lo(pf[ks][w]) + bf16_hi(pf[ks][w]);
+      for (int w = 0; w < 4; ++w) {
+        pf[ks][w] = pack_bf16x2(st[8 * ks + 2 * w], st[8 * ks + 2 * w + 1]);
+        rsum = bf16x2_sum_into(pf[ks][w], rsum);
+      }
     }
     r_run += rsum;
     // The transposed reads must have landed (the operands pass through this
@@ -382,14 +386,25 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkParams p) {
     for (int j = 0; j < 16; ++j) q_row0 += i + j < seq ? x[j] : 0;
   }
   load_q();
-  for (int it = 0; it < T; ++it) {
+  auto step = [&](int it, auto stage_c) {
+    constexpr int stage = decltype(stage_c)::value;
     // this wave's loads of tile it are the oldest but those of it + 1,
     // it + 2 (4 instructions each); the query rows were loaded before the
     // loop and are older still.
     __builtin_amdgcn_s_waitcnt(0x0F78);  // vmcnt(8), other counters unconstrained
     __syncthreads();
-    load_tile(it + 3, (it + 3) & (kStages - 1));
-    compute_tile(it, it & (kStages - 1));
+    load_tile(it + 3, (stage + 3) & (kStages - 1));
+    compute_tile(it, stage_c);
+  };
+  static_assert(kStages == 4, "the loop below is unrolled by the ring depth");
+  for (int it = 0; it < T; it += 4) {
+    step(it, std::integral_constant<int, 0>{});
+    if (it + 1 >= T) break;
+    step(it + 1, std::integral_constant<int, 1>{});
+    if (it + 2 >= T) break;
+    step(it + 2, std::integral_constant<int, 2>{});
+    if (it + 3 >= T) break;
+    step(it + 3, std::integral_constant<int, 3>{});
   }
   // The loads past the last tile must land before the tile area is reused,
   // and every wave must be done computing.

@@ -60,6 +60,13 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// acc + lo + hi of a packed bf16 pair, in one VALU operation (a dot product
+// with (1, 1): the products are exact, the sum is fp32).
+__device__ __forceinline__ float bf16x2_sum_into(uint32_t u, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, u), __builtin_bit_cast(bf16x2_t, 0x3f803f80u),
+                                         acc, false);
+}
+
 // Sum over the whole 64-lane wave (result in every lane).
 __device__ __forceinline__ int wave_sum_i32(int x) {
   for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
