@@ -66,9 +66,25 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(const u32x4_t& u) { return __built
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 
-// Byte offset of dims d .. of key row `key` in a swizzled K or V tile: the
-// 16-byte chunk index is XORed with the key's low four bits.
-__device__ __forceinline__ int swz(int key, int d) { return key * kRowBytes + ((((d >> 3) ^ key) & 15) << 4) + (d & 7) * 2; }
+// The swizzle of a K or V tile: the 16-byte chunk c of key row `key` sits at
+// chunk position c ^ key_swz(key), where key_swz permutes the key's low four
+// bits k3 k2 k1 k0 into (k1 ^ k3) k0 k1 k2.  Two read patterns must be free of
+// LDS bank conflicts, whether the LDS serves 128 or 256 bytes per cycle:
+//  * the K fragment reads: 8 or 16 lanes read one chunk of as many
+//    consecutive keys: key_swz is a permutation of 16 keys that is also one
+//    of any 8 aligned keys in its low three bits;
+//  * the transposing V reads: 16 lanes read chunks 2j, 2j + 1 of four
+//    consecutive keys 4i .. 4i + 3 (32 lanes: chunks 4j .. 4j + 3): bits 2-1
+//    and bits 3-2 of key_swz each take all four values over those keys, so
+//    the positions cover 8 (16) distinct chunks mod 8 (16).
+// (XORing with the key itself put keys 4i and 4i + 1 of the V reads on the
+// same banks.)
+__device__ __forceinline__ int key_swz(int key) {
+  const int k0 = key & 1, k1 = (key >> 1) & 1, k2 = (key >> 2) & 1, k3 = (key >> 3) & 1;
+  return ((k1 ^ k3) << 3) | (k0 << 2) | (k1 << 1) | k2;
+}
+// Byte offset of dims d .. of key row `key` in a swizzled K or V tile.
+__device__ __forceinline__ int swz(int key, int d) { return key * kRowBytes + (((d >> 3) ^ key_swz(key)) << 4) + (d & 7) * 2; }
 
 __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkParams p) {
   // [key half][stage][K tile | V tile], both row-major with swizzled 16-byte
@@ -184,7 +200,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkParams p) {
       const int r = 8 * wh + 4 * j + (lane >> 4);  // LDS row of this lane
       const int key = min(t * kTileKeys + r, kv_end - 1);
       const int32_t id = (key >> 4) & 1 ? id1 : id0;
-      const int c = (lane & 15) ^ (r & 15);        // global chunk for this slot
+      const int c = (lane & 15) ^ key_swz(r);      // global chunk for this slot
       const size_t off = cache_offset(id, g, key & 15, c * 8, p.num_kv_heads);
       const int lds_off = (8 * wh + 4 * j) * kRowBytes;  // wave-uniform
       __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(p.k + off),
@@ -224,7 +240,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkParams p) {
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
       const int c = hh * 8 + s;
-      kf[s] = *reinterpret_cast<const u32x4_t*>(sk + col * kRowBytes + ((c ^ (col & 15)) << 4));
+      kf[s] = *reinterpret_cast<const u32x4_t*>(sk + col * kRowBytes + ((c ^ key_swz(col)) << 4));
     }
     __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the products
 #pragma unroll
