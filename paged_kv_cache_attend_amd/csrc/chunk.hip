@@ -66,23 +66,6 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(const u32x4_t& u) { return __built
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 
-// The swizzle of a K or V tile: the 16-byte chunk c of key row `key` sits at
-// chunk position c ^ key_swz(key), where key_swz permutes the key's low four
-// bits k3 k2 k1 k0 into (k1 ^ k3) k0 k1 k2.  Two read patterns must be free of
-// LDS bank conflicts, whether the LDS serves 128 or 256 bytes per cycle:
-//  * the K fragment reads: 8 or 16 lanes read one chunk of as many
-//    consecutive keys: key_swz is a permutation of 16 keys that is also one
-//    of any 8 aligned keys in its low three bits;
-//  * the transposing V reads: 16 lanes read chunks 2j, 2j + 1 of four
-//    consecutive keys 4i .. 4i + 3 (32 lanes: chunks 4j .. 4j + 3): bits 2-1
-//    and bits 3-2 of key_swz each take all four values over those keys, so
-//    the positions cover 8 (16) distinct chunks mod 8 (16).
-// (XORing with the key itself put keys 4i and 4i + 1 of the V reads on the
-// same banks.)
-__device__ __forceinline__ int key_swz(int key) {
-  const int k0 = key & 1, k1 = (key >> 1) & 1, k2 = (key >> 2) & 1, k3 = (key >> 3) & 1;
-  return ((k1 ^ k3) << 3) | (k0 << 2) | (k1 << 1) | k2;
-}
 // Byte offset of dims d .. of key row `key` in a swizzled K or V tile.
 __device__ __forceinline__ int swz(int key, int d) { return key * kRowBytes + (((d >> 3) ^ key_swz(key)) << 4) + (d & 7) * 2; }
 

@@ -45,9 +45,8 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(const u32x4_t& u) { return __built
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 
-// Byte offset of dims d .. of key row `key` in a swizzled K or V tile: the
-// 16-byte chunk index is XORed with the key's low four bits.
-__device__ __forceinline__ int swz(int key, int d) { return key * kRowBytes + ((((d >> 3) ^ key) & 15) << 4) + (d & 7) * 2; }
+// Byte offset of dims d .. of key row `key` in a swizzled K or V tile.
+__device__ __forceinline__ int swz(int key, int d) { return key * kRowBytes + (((d >> 3) ^ key_swz(key)) << 4) + (d & 7) * 2; }
 
 // Set-up workgroup: slot_plen[r] = the prefix length of r's group in whole
 // pages, for a group's first max_members slots (the rows this kernel
@@ -144,7 +143,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_kernel(PrefixParams p) {
       const int row = 4 * j + (lane >> 4);           // LDS row of this lane
       const int key = min(key0 + t * kTileKeys + row, kv_end - 1);
       const int32_t id = (key >> 4) == (key0 >> 4) + 2 * t ? id0 : id1;
-      const int c = (lane & 15) ^ (row & 15);        // global chunk for this slot
+      const int c = (lane & 15) ^ key_swz(row);      // global chunk for this slot
       const size_t off = cache_offset(id, g, key & 15, c * 8, p.num_kv_heads);
       __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(p.k + off),
                                        (void __attribute__((address_space(3)))*)(sk + 4 * j * kRowBytes), 16, 0, 0);
@@ -205,7 +204,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefix_kernel(PrefixParams p) {
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
       const int c = hh * 8 + s;
-      kf[s] = *reinterpret_cast<const u32x4_t*>(sk + col * kRowBytes + ((c ^ (col & 15)) << 4));
+      kf[s] = *reinterpret_cast<const u32x4_t*>(sk + col * kRowBytes + ((c ^ key_swz(col)) << 4));
     }
     f32x16_t st;
 #pragma unroll
