@@ -74,9 +74,9 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str, kernel: str):
-    """(fetch, write) HBM bytes per launch from the committed counter summary,
-    or None if it is missing or was taken on other sources."""
+def traffic_entry(workload: str, kernel: str):
+    """The committed counter summary of one kernel on one workload, or None
+    if it is missing or was taken on other sources."""
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)
@@ -84,7 +84,13 @@ def measured_traffic(workload: str, kernel: str):
         return None
     if rec.get("source_hash") != kernel_source_hash():
         return None
-    ent = rec.get("workloads", {}).get(workload, {}).get(kernel)
+    return rec.get("workloads", {}).get(workload, {}).get(kernel) or None
+
+
+def measured_traffic(workload: str, kernel: str):
+    """(fetch, write) HBM bytes per launch from the committed counter summary,
+    or None if it is missing or was taken on other sources."""
+    ent = traffic_entry(workload, kernel)
     if not ent:
         return None
     return ent["fetch_bytes_per_launch"], ent["write_bytes_per_launch"]
@@ -396,6 +402,14 @@ def chunk_secondary(dev, steps, launch="graph", mfma_tflops=None):
             "frac": warm_tf / BF16_PEAK_TFLOPS, "algorithmic_flops_per_launch": flops,
             "avg_launch_us": warm_ms * 1e3, "kernel": "chunk_kernel (warm: inputs resident in the Infinity Cache)",
             "traffic": None}
+    ent = traffic_entry("chunked_denoise", "chunk_kernel")
+    if ent:
+        roof["traffic"] = ent["fetch_bytes_per_launch"] + ent["write_bytes_per_launch"]
+        roof["traffic_fetch"] = ent["fetch_bytes_per_launch"]
+        roof["traffic_write"] = ent["write_bytes_per_launch"]
+        if ent.get("mfma_flop_per_launch"):
+            # SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 of the profiled dispatches
+            roof["counted_mfma_flop_per_launch"] = ent["mfma_flop_per_launch"]
     if mfma_tflops:
         roof["measured_peak_tflops"] = mfma_tflops
         roof["frac_of_measured_peak"] = warm_tf / mfma_tflops
