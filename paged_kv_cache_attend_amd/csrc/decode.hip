@@ -1,9 +1,12 @@
-// decode.hip -- paged decode attention, one new token per slot, split-KV with
-// the log-sum-exp merge fused into the same launch.
+// decode.hip -- paged decode attention, one to eight new tokens per slot,
+// split-KV with the log-sum-exp merge fused into the same launch.
 //
 // What it computes: for each active slot and query head, softmax attention of
-// the one new query row over the slot's n cached keys, gathered through the
+// each new query row over the slot's n cached keys, gathered through the
 // block table (inference-optimisation chapter, section 8.3.1, Fig. 8-10).
+// A slot usually brings one new token; verifying several proposed tokens at
+// once (section 8.5 of the same chapter) brings up to eight, and with
+// PA_FLAG_CAUSAL new token t sees keys [0, n - m + t] (section 8.2.3).
 // Decode reads every key and value of every request once per step, so the
 // kernel is bound by HBM bandwidth (same chapter, section 8.2.1): per key and
 // KV head it moves 512 bytes (K and V, 128 bf16 each) and does 4 FLOP per
@@ -62,6 +65,9 @@
 //   and writes the result, all in the same launch.  Empty partitions and
 //   slots with no keys take part with LSE = -inf; a slot whose partials are
 //   all -inf writes nothing.
+// * Several new tokens: the (token, query head) pairs of a KV head are the
+//   columns of the score tile (see Cols below), so the pages are streamed
+//   once for all of them; each column has its own causal limit.
 // * Prefix-grouped decode (pa_attend_prefix): a grouped slot's partitions
 //   start after its group's shared prefix, and the merge also folds the
 //   prefix pass's partials of the slot's rows (written by the launch before).
