@@ -49,6 +49,8 @@ CASES = [
     ("two_row_tiles", dict(groups=[(48, [48 + 7 * i for i in range(20)])], singles=[], hq=32, hkv=8)),
     ("mha", dict(groups=[(80, [80, 90, 200])], singles=[33], hq=4, hkv=4)),
     ("gqa2", dict(groups=[(16, [17, 100]), (160, [160, 170, 400])], singles=[], hq=8, hkv=4)),
+    # eight query heads per KV head: 8 members x 8 heads = 64 rows, one full row tile
+    ("gqa8", dict(groups=[(64, [64, 100, 300, 65, 80, 64, 200, 129])], singles=[40], hq=64, hkv=8)),
     ("long_prefix", dict(groups=[(2048, [2048, 2100, 2600])], singles=[700], hq=32, hkv=8)),
     # 60 prefix pages over 20 partitions of 3 pages: a partition's second
     # tile reaches into the next partition's first page (masked).
