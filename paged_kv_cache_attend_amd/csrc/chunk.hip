@@ -18,22 +18,24 @@
 //
 // Workgroup: 8 waves over 128 packed rows of one (slot, KV head).  Wave w
 // takes the rows r with r % 4 == w % 4 (32 of them) and one half of the
-// keys (w / 4); the two halves merge through LDS at the end.  Each half walks its keys in 32-key
-// tiles (two 16-token pages):
+// keys (w / 4); the two halves merge through LDS at the end.  Each half
+// walks its keys in 32-key tiles (two 16-token pages):
 //   1. the tile's K and V rows go straight from memory into LDS
-//      (global_load_lds_dwordx4), row-major with XOR-swizzled 16-byte
-//      chunks, into a four-stage ring: three tiles are in flight while one is
-//      computed, no registers hold them and no store instructions move them.
-//      Each lane's source chunk is the one the swizzle puts at its LDS slot;
-//      page ids come from scalar loads one tile ahead.  One barrier per tile;
+//      (global_load_lds_dwordx4), row-major with each row's 16-byte chunks
+//      permuted (key_swz in device.h: no LDS bank conflicts for the reads
+//      below), into a four-stage ring: three tiles are in flight while one
+//      is computed, no registers hold them and no store instructions move
+//      them.  Each lane's source chunk is the one the permutation puts at its
+//      LDS slot; page ids come from scalar loads one tile ahead.  One barrier
+//      per tile;
 //   2. each wave computes S^T = K Q^T (32 keys x 32 rows, 8 MFMAs over the 128
 //      dims, all eight K fragments read before the first product).  In the
 //      MFMA output layout a lane holds 16 keys of ONE query row, so the row
 //      max and sum of the online softmax are mostly in-lane; the other 16
 //      keys of the row sit in lane ^ 32 (v_permlane32_swap).  The
 //      accumulators are only rescaled when the row max grows by more than
-//      2^8; tiles every row sees whole skip the masking and fold the scale
-//      into the exponent's FMA;
+//      2^8; masked keys become -inf in place, tiles that every row sees whole
+//      skip the masking, and the scale folds into the exponent's FMA;
 //   3. probabilities are rounded to bf16 and used directly, from registers, as
 //      the B operand of O^T += V^T P^T (4 x 32 dims, 2 key steps, 8 MFMAs);
 //      the V^T A operand is read from the row-major V tile with transposing
@@ -42,7 +44,8 @@
 //      weights, so it is an exact weighted mean of the V rows under the
 //      weights PV used (a single dominant key comes back exactly); the LSE
 //      takes the sum of the fp32 weights.
-// Keys past the end load the last key (finite) and get -inf scores.
+// Keys past the end load the last key (finite) and get -inf scores.  The
+// 128 x 128 bf16 output tile is staged in LDS and stored as whole rows.
 
 #include <type_traits>
 
@@ -68,7 +71,9 @@ typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 
 // Byte offset of dims d .. of key row `key` in a swizzled K or V tile.
-__device__ __forceinline__ int swz(int key, int d) { return key * kRowBytes + (((d >> 3) ^ key_swz(key)) << 4) + (d & 7) * 2; }
+__device__ __forceinline__ int swz(int key, int d) {
+  return key * kRowBytes + (((d >> 3) ^ key_swz(key)) << 4) + (d & 7) * 2;
+}
 
 __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkParams p) {
   // [key half][stage][K tile | V tile], both row-major with swizzled 16-byte
@@ -491,9 +496,8 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkParams p) {
       const u32x4_t v = *reinterpret_cast<const u32x4_t*>(otile + j * kRowBytes + ((c ^ ((j >> 2) & 15)) << 4));
       // (non-temporal: written once, not read again by this kernel; measured
       // 0.2 - 0.7 us per launch faster than an ordinary store)
-      __builtin_nontemporal_store(
-          v, reinterpret_cast<u32x4_t*>(p.out + ((size_t)(q_row0 + pj / G) * p.num_q_heads + g * G + pj % G) * kHeadDim +
-                                        c * 8));
+      const size_t orow = (size_t)(q_row0 + pj / G) * p.num_q_heads + g * G + pj % G;
+      __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(p.out + orow * kHeadDim + c * 8));
     }
   }
 }

@@ -14,11 +14,12 @@
 // plus one set-up workgroup that writes every slot's prefix length for the
 // suffix pass.  A partition is at most eight 32-key tiles, and a workgroup
 // requests all of its tiles at once, straight from memory into LDS
-// (global_load_lds_dwordx4: K and V row-major with XOR-swizzled 16-byte
-// chunks, 128 KiB), so the pass costs one memory round trip rather than one
-// per tile.  Eight waves: wave w takes rows 32 (w % 2) .. +32 of the tile
-// and the tiles w / 2, w / 2 + 4 of the partition; at the end the quarters
-// merge through LDS, each wave folding and storing one 32-dim block.
+// (global_load_lds_dwordx4: K and V row-major with each row's 16-byte
+// chunks permuted by key_swz, 128 KiB), so the pass costs one memory round
+// trip rather than one per tile.  Eight waves: wave w takes rows
+// 32 (w % 2) .. +32 of the tile and the tiles w / 2, w / 2 + 4 of the
+// partition; at the end the quarters merge through LDS, each wave folding
+// and storing one 32-dim block.
 // S^T = K Q^T and O^T += V^T P^T run on v_mfma_f32_32x32x16_bf16 with the
 // softmax mostly in-lane; the V^T operand
 // comes from the row-major V tile through transposing LDS reads
@@ -46,7 +47,9 @@ typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 
 // Byte offset of dims d .. of key row `key` in a swizzled K or V tile.
-__device__ __forceinline__ int swz(int key, int d) { return key * kRowBytes + (((d >> 3) ^ key_swz(key)) << 4) + (d & 7) * 2; }
+__device__ __forceinline__ int swz(int key, int d) {
+  return key * kRowBytes + (((d >> 3) ^ key_swz(key)) << 4) + (d & 7) * 2;
+}
 
 // Set-up workgroup: slot_plen[r] = the prefix length of r's group in whole
 // pages, for a group's first max_members slots (the rows this kernel
