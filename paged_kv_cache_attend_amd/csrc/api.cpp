@@ -156,6 +156,10 @@ pa_status make_plan(const pa_shape* s, Plan* plan, bool grouped = false) {
 
 }  // namespace
 
+#ifndef PA_PREFIX_ONE_LAUNCH
+#define PA_PREFIX_ONE_LAUNCH 1
+#endif
+
 namespace {
 
 // Kernel arguments of the decode path for a plan; `ws` holds the split-KV
@@ -617,7 +621,6 @@ pa_status pa_attend_prefix(const pa_shape* shape, const pa_prefix_groups* groups
   pr.pre_parts = pp.pre_parts;
   pr.part_pages = pp.pre_pages;
   pr.max_members = groups->max_members;
-  if (launch_prefix(pr, pp.pre_grid, s) != hipSuccess) return PA_ERR_LAUNCH;
 
   pa_kv_cache kv = {};
   kv.format = kFmtBF16;
@@ -627,8 +630,39 @@ pa_status pa_attend_prefix(const pa_shape* shape, const pa_prefix_groups* groups
   d.slot_plen = pr.slot_plen;
   d.pre_out = pr.pre_out;
   d.pre_lse = pr.pre_lse;
+
+  // One launch for the shared and the own keys where the slots' own keys are
+  // split (their merge then counts the prefix partials too): prefix items of
+  // prefix_chunk_members members each, as long as the slots' partitions (the
+  // prefix items go first, so they tend to be done first and the slots'
+  // partitions do the merging) and never more prefix partitions than the
+  // workspace holds.  The set-up workgroup (the slots' prefix lengths) runs
+  // alone before it.
+  const int G = pp.suffix.group;
+  const int mc = prefix_chunk_members(G);
+  if (PA_PREFIX_ONE_LAUNCH && pp.pre_grid > 0 && pp.suffix.decode && pp.suffix.num_parts > 1) {
+    const int max_pages = groups->max_prefix_len / kBlockSize;
+    const int pre_pages = pp.pre_pages > pp.suffix.part_pages ? pp.pre_pages : pp.suffix.part_pages;
+    const int pre_parts = ceil_div(max_pages, pre_pages);
+    const int chunks = ceil_div(groups->max_members, mc);
+    const long long items = (long long)groups->num_groups * shape->num_kv_heads * pre_parts * chunks;
+    if (pre_parts <= pp.pre_parts && items > 0 && items + pp.suffix.grid <= INT_MAX) {
+      if (launch_prefix(pr, 0, s) != hipSuccess) return PA_ERR_LAUNCH;
+      d.pre_parts = pre_parts;
+      d.pre_items = (int)items;
+      d.pre_pages = pre_pages;
+      d.pre_chunks = chunks;
+      d.max_members = groups->max_members;
+      d.group_start = groups->group_start;
+      d.prefix_len = groups->prefix_len;
+      if (launch_decode(d, G, kFmtBF16, mc, (unsigned)(items + pp.suffix.grid), s) != hipSuccess)
+        return PA_ERR_LAUNCH;
+      return PA_OK;
+    }
+  }
+  if (launch_prefix(pr, pp.pre_grid, s) != hipSuccess) return PA_ERR_LAUNCH;
   d.pre_parts = pp.pre_grid > 0 ? pp.pre_parts : 0;
-  if (launch_decode(d, pp.suffix.group, kFmtBF16, 1, pp.suffix.grid, s) != hipSuccess) return PA_ERR_LAUNCH;
+  if (launch_decode(d, G, kFmtBF16, 1, pp.suffix.grid, s) != hipSuccess) return PA_ERR_LAUNCH;
   return PA_OK;
 }
 

@@ -391,6 +391,302 @@ __device__ __forceinline__ void consume_page(WaveState<Cols<G, M>::NT>& st, Page
   }
 }
 
+// One prefix item of a prefix-grouped decode done in one launch (pre_items
+// > 0): pages [pp pre_pages, ...) of one group's shared prefix for one KV
+// head, streamed once for up to M of the group's members, whose rows are the
+// token columns (member rows are consecutive: each member brings at most one
+// row on this path).  A member sees the prefix up to its own length.  The
+// item writes its members' partials to pre_out / pre_lse (normalised, with
+// their LSE; -inf where no key is visible), counts them on each member's
+// counter like a partition of that slot, and merges the slots it arrives
+// last for.  Everything below mirrors the partition path of decode_kernel.
+template <int G, int F, int M>
+__device__ __forceinline__ void prefix_item(const DecodeParams& p, int pi, int lane, int wave,
+                                            uint8_t (*s_k)[kTileBytes], uint8_t (*s_v)[kTileBytes],
+                                            float (*s_ks)[kBlockSize * 4], float (*s_vs)[kBlockSize * 4],
+                                            uint8_t (*s_q)[kHeadDim * 2], float (*s_acc)[Cols<G, M>::C][kHeadDim],
+                                            float (*s_m)[Cols<G, M>::C], float (*s_l)[Cols<G, M>::C],
+                                            float (*s_r)[Cols<G, M>::C], int* s_lastm) {
+  using CS = Cols<G, M>;
+  constexpr int C = CS::C;
+  constexpr int NT = CS::NT;
+  const int ci = pi % p.pre_chunks;
+  int rest = pi / p.pre_chunks;
+  const int pp = rest % p.pre_parts;
+  rest /= p.pre_parts;
+  const int g = rest % p.num_kv_heads;
+  const int gi = rest / p.num_kv_heads;
+
+  // The group's bounds and prefix length, then the chunk members' lengths
+  // and the row offset of its first member.
+  int s0 = scalar_load_i32(p.group_start, gi);
+  int s1 = scalar_load_i32(p.group_start, gi + 1);
+  int plen = scalar_load_i32(p.prefix_len, gi);
+  asm volatile("" : "+s"(s0), "+s"(s1), "+s"(plen));
+  plen = max(plen, 0) & ~(kBlockSize - 1);  // whole pages, as the partitions read it
+  const int members = min(s1 - s0, p.max_members);
+  const int j0 = ci * M;
+  if (plen <= 0 || j0 >= members) return;
+  const int jn = min(M, members - j0);
+  const int sf = s0 + j0;
+  int mq[M], mn[M];
+#pragma unroll
+  for (int j = 0; j < M; ++j) {
+    mq[j] = scalar_load_i32(p.q_lens, sf + min(j, jn - 1));
+    mn[j] = scalar_load_i32(p.ctx_lens, sf + min(j, jn - 1));
+  }
+  int qsum = 0;
+  for (int i = lane; i < sf; i += 64) qsum += p.q_lens[i];
+#pragma unroll
+  for (int j = 0; j < M; ++j) asm volatile("" : "+s"(mq[j]), "+s"(mn[j]));
+  asm volatile("" : "+v"(qsum));
+  // Token t = the t-th member with a row; its length and member index.
+  int mt = 0;
+#pragma unroll
+  for (int j = 0; j < M; ++j) mt += (j < jn && mq[j] > 0) ? 1 : 0;
+  if (mt == 0) return;  // no rows: nothing to write, nothing to count
+  auto token_member = [&](int t) -> int {  // member index of token t (M if none)
+    int cnt = 0, jm = M;
+#pragma unroll
+    for (int j = 0; j < M; ++j) {
+      const bool has = j < jn && mq[j] > 0;
+      if (has && cnt == t) jm = j;
+      cnt += has ? 1 : 0;
+    }
+    return jm;
+  };
+  auto member_n = [&](int jm) -> int {
+    int r = 0;
+#pragma unroll
+    for (int j = 0; j < M; ++j) r = jm == j ? mn[j] : r;
+    return r;
+  };
+
+  const int32_t* bt = p.block_table + (size_t)s0 * p.max_blocks;  // the group's shared pages
+  // (the last partition runs to the group's prefix end, as in the prefix pass)
+  const int pstart = pp * p.pre_pages;
+  const int pend = pp == p.pre_parts - 1 ? plen / kBlockSize : min(pstart + p.pre_pages, plen / kBlockSize);
+  const bool has_work = pstart < pend;
+  const int last_page = pend - 1;
+  auto page_id = [&](int page) -> int32_t { return scalar_load_i32(bt, min(page, last_page)); };
+  const int h0 = g * G;
+  const size_t rows = (size_t)p.total_q * p.num_q_heads;
+
+  Page<F> ring[kRing];
+  const int page0 = pstart + wave;
+  const int cnt = (has_work && page0 < pend) ? (pend - page0 + kWaves - 1) / kWaves : 0;
+  int32_t next_id = 0;
+  int q_row;
+  if (has_work) {
+    issue_page<F>(ring[0], p, page_id(page0), g, lane);
+    __builtin_amdgcn_sched_barrier(0);
+    q_row = __builtin_amdgcn_readfirstlane(wave_sum_i32(qsum));
+    constexpr int kQChunks = (C * 16 + kDecodeThreads - 1) / kDecodeThreads;
+    u32x4_t qchunk[kQChunks];
+#pragma unroll
+    for (int j = 0; j < kQChunks; ++j) {
+      const int idx = threadIdx.x + j * kDecodeThreads;
+      const int c = min(idx >> 4, C - 1), qc = idx & 15;
+      const int tok = min(c / G, mt - 1);
+      qchunk[j] = reinterpret_cast<const u32x4_t*>(p.q)[((size_t)(q_row + tok) * p.num_q_heads + h0 + c % G) * 16 + qc];
+    }
+    issue_order_barrier();
+#pragma unroll
+    for (int r = 1; r < kRing; ++r) issue_page<F>(ring[r], p, page_id(page0 + r * kWaves), g, lane);
+    next_id = page_id(page0 + kRing * kWaves);
+#pragma unroll
+    for (int j = 0; j < kQChunks; ++j) {
+      const int idx = threadIdx.x + j * kDecodeThreads;
+      const int c = idx >> 4, qc = idx & 15;
+      if (c < C) *reinterpret_cast<u32x4_t*>(&s_q[c][(qc ^ (c & 15)) << 4]) = qchunk[j];
+    }
+    __syncthreads();
+  } else {
+    q_row = __builtin_amdgcn_readfirstlane(wave_sum_i32(qsum));
+  }
+
+  const int pr = lane >> 4;
+  const int pc = lane & 15;
+  int col[NT];
+  bool col_live[NT];
+  int lim[NT];
+#pragma unroll
+  for (int ct = 0; ct < NT; ++ct) {
+    const int n16 = ct * 16 + pc;
+    col[ct] = CS::HL ? (n16 & (C - 1)) : n16;
+    const bool in_tile = CS::HL ? n16 < 2 * C : n16 < C;
+    const int tok = col[ct] / G;
+    const int nt = member_n(token_member(tok));
+    col_live[ct] = in_tile && tok < mt && nt > 0;
+    lim[ct] = min(plen, nt) - 1;
+  }
+
+  if (has_work) {
+    WaveState<NT> st;
+#pragma unroll
+    for (int ct = 0; ct < NT; ++ct) {
+      st.m_ref[ct] = -INFINITY;
+      st.l_lane[ct] = 0.f;
+      st.r_lane[ct] = 0.f;
+#pragma unroll
+      for (int bb = 0; bb < 8; ++bb) st.o[ct][bb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      const int c = min(col[ct], C - 1);
+#pragma unroll
+      for (int sg = 0; sg < 4; ++sg) {
+        const u32x4_t x = *reinterpret_cast<const u32x4_t*>(&s_q[c][((4 * sg + pr) ^ (c & 15)) << 4]);
+        st.qb[ct][sg] = col_live[ct] ? x : u32x4_t{0u, 0u, 0u, 0u};
+      }
+    }
+    uint8_t* sk = s_k[wave];
+    uint8_t* sv = s_v[wave];
+    float* sks = s_ks[wave];
+    float* svs = s_vs[wave];
+#define PA_CONSUME(RING, K)                                                                            \
+  consume_page<G, F, M>(st, RING, sk, sv, sks, svs, kBlockSize, p.scale_log2, lane,                    \
+                        (page0 + kWaves * (K)) * kBlockSize, lim)
+#define PA_REISSUE(RING, K)                                          \
+  {                                                                  \
+    issue_page<F>(RING, p, next_id, g, lane);                        \
+    next_id = page_id(page0 + kWaves * ((K) + 1));                   \
+  }
+    int k = 0;
+    for (; k + 2 * kRing - 1 < cnt; k += kRing) {
+#pragma unroll
+      for (int r = 0; r < kRing; ++r) {
+        PA_CONSUME(ring[r], k + r);
+        PA_REISSUE(ring[r], k + r + kRing);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < kRing; ++r) {
+      if (k + r < cnt) {
+        PA_CONSUME(ring[r], k + r);
+        if (k + r + kRing < cnt) PA_REISSUE(ring[r], k + r + kRing);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < kRing - 1; ++r)
+      if (k + kRing + r < cnt) PA_CONSUME(ring[r], k + kRing + r);
+#undef PA_CONSUME
+#undef PA_REISSUE
+#pragma unroll
+    for (int ct = 0; ct < NT; ++ct) {
+      float l_sum = st.l_lane[ct] + other16(st.l_lane[ct]);
+      l_sum += other_half(l_sum);
+      float r_sum = st.r_lane[ct] + other16(st.r_lane[ct]);
+      r_sum += other_half(r_sum);
+      f32x4_t o_tot[8];
+#pragma unroll
+      for (int bb = 0; bb < 8; ++bb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          o_tot[bb][i] = CS::HL ? st.o[ct][bb][i] + __shfl_xor(st.o[ct][bb][i], C, 64) : st.o[ct][bb][i];
+      const int c = ct * 16 + pc;
+      if (c < C) {
+        if (pr == 0) {
+          s_m[wave][c] = st.m_ref[ct];
+          s_l[wave][c] = l_sum;
+          s_r[wave][c] = CS::HL ? l_sum : r_sum;
+        }
+#pragma unroll
+        for (int bb = 0; bb < 8; ++bb) *reinterpret_cast<f32x4_t*>(&s_acc[wave][c][16 * bb + 4 * pr]) = o_tot[bb];
+      }
+    }
+    __syncthreads();
+  }
+
+  // Each thread: J (column, dim pair) outputs, as in the partition epilogue.
+  constexpr int J = CS::J;
+  float my_o0[J], my_o1[J], my_lse[J];
+  int my_c[J], my_d[J];
+  bool my_out[J];
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int i = threadIdx.x + j * kDecodeThreads;
+    my_c[j] = min(i >> 6, C - 1);
+    my_d[j] = (i & 63) * 2;
+    const int tok = my_c[j] / G;
+    my_out[j] = i < C * 64 && tok < mt && member_n(token_member(tok)) > 0;
+    my_o0[j] = 0.f;
+    my_o1[j] = 0.f;
+    my_lse[j] = -INFINITY;
+    if (has_work && my_out[j]) {
+      const int c = my_c[j], d = my_d[j];
+      float Mx = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) Mx = fmaxf(Mx, s_m[w][c]);
+      if (Mx != -INFINITY) {
+        float L = 0.f, R = 0.f, a0 = 0.f, a1 = 0.f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+          const float sc = fast_exp2(s_m[w][c] - Mx);
+          L = fmaf(sc, s_l[w][c], L);
+          R = fmaf(sc, s_r[w][c], R);
+          const float2 v = *reinterpret_cast<const float2*>(&s_acc[w][c][d]);
+          a0 = fmaf(sc, v.x, a0);
+          a1 = fmaf(sc, v.y, a1);
+        }
+        const float inv = 1.f / R;
+        my_o0[j] = a0 * inv;
+        my_o1[j] = a1 * inv;
+        my_lse[j] = (Mx + fast_log2(L)) * kLn2;
+      }
+    }
+  }
+  auto row_of = [&](int j) -> size_t {
+    return (size_t)(q_row + my_c[j] / G) * p.num_q_heads + h0 + my_c[j] % G;
+  };
+  // Publish, count and merge with the ordering of the partition path (see
+  // there): device-scope stores, their acknowledgement, a barrier, then each
+  // member's counter; the merger's loads are device-scope.
+  float* pre_out = const_cast<float*>(p.pre_out);
+  float* pre_lse = const_cast<float*>(p.pre_lse);
+  uint64_t* pre_out64 = reinterpret_cast<uint64_t*>(pre_out);
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    if (!my_out[j]) continue;
+    const size_t prow = (size_t)pp * rows + row_of(j);
+    if (my_lse[j] != -INFINITY) {
+      const uint64_t bits = (uint64_t)__float_as_uint(my_o0[j]) | ((uint64_t)__float_as_uint(my_o1[j]) << 32);
+      __hip_atomic_store(pre_out64 + (prow * kHeadDim + my_d[j]) / 2, bits, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (my_d[j] == 0) __hip_atomic_store(pre_lse + prow, my_lse[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  wait_vm_stores();
+  __syncthreads();
+  if ((int)threadIdx.x < mt) {
+    const int jm = token_member((int)threadIdx.x);
+    int last = 0;
+    if (member_n(jm) > 0) {
+      int32_t* counter = p.counters + (size_t)(sf + jm) * p.num_kv_heads + g;
+      last = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+             p.num_parts + p.pre_parts - 1;
+    }
+    s_lastm[threadIdx.x] = last;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    if (!my_out[j] || !s_lastm[my_c[j] / G]) continue;
+    const size_t row = row_of(j);
+    const int d = my_d[j];
+    MergeState ms;
+    merge_partials(ms, p.part_lse + row, p.part_out + row * kHeadDim + d, p.num_parts, p.pre_lse + row,
+                   p.pre_out + row * kHeadDim + d, p.pre_parts, rows);
+    if (ms.M != -INFINITY) {
+      const float inv = 1.f / ms.W;
+      reinterpret_cast<uint32_t*>(p.out)[(row * kHeadDim + d) / 2] = pack_bf16x2(ms.a0 * inv, ms.a1 * inv);
+      if (d == 0 && p.lse) p.lse[row] = ms.M + fast_log2(ms.W) * kLn2;
+    }
+  }
+  if ((int)threadIdx.x < mt && s_lastm[threadIdx.x]) {
+    const int jm = token_member((int)threadIdx.x);
+    __hip_atomic_store(p.counters + (size_t)(sf + jm) * p.num_kv_heads + g, 0, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
 #ifndef PA_DECODE_MIN_WGS
 #define PA_DECODE_MIN_WGS kDecodeWGsPerCU
 #endif
@@ -412,15 +708,26 @@ __global__ __launch_bounds__(kDecodeThreads, (Cols<G, M>::NT > 1 ? 1 : PA_DECODE
   __shared__ float s_l[kWaves][C];
   __shared__ float s_r[kWaves][C];
   __shared__ int s_last;
+  __shared__ int s_lastm[M];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   // The kernel arguments the start needs, fetched together (the compiler
   // would otherwise fetch some of them one round trip later).
   asm volatile("" ::"s"(p.q_lens), "s"(p.ctx_lens), "s"(p.block_table), "s"(p.slot_plen), "s"(p.pre_parts), "s"(p.num_parts),
+               "s"(p.pre_items),
                "s"(p.num_seqs), "s"(p.part_pages), "s"(p.max_blocks), "s"(gridDim.x));
 
-  const int wg = xcd_remap(blockIdx.x, gridDim.x);
+  // One launch of prefix-grouped decode: the first pre_items workgroups are
+  // prefix items (dispatched first); the rest are the slots' partitions.
+  if ((int)blockIdx.x < p.pre_items) {
+    if constexpr (F == kFmtBF16 && M == prefix_chunk_members(G)) {
+      prefix_item<G, F, M>(p, xcd_remap(blockIdx.x, p.pre_items), lane, wave, s_k, s_v, s_ks, s_vs, s_q, s_acc, s_m,
+                           s_l, s_r, s_lastm);
+    }
+    return;
+  }
+  const int wg = xcd_remap(blockIdx.x - p.pre_items, gridDim.x - p.pre_items);
   const int P = p.num_parts;
   const int part = wg % P;
   const int rest = wg / P;
@@ -454,7 +761,7 @@ __global__ __launch_bounds__(kDecodeThreads, (Cols<G, M>::NT > 1 ? 1 : PA_DECODE
   asm volatile("" : "+v"(qsum));
   if (m <= 0) return;  // no row: nothing to write, no partial to count
   const int npages = (n + kBlockSize - 1) / kBlockSize;
-  const int npre = (M == 1 && plen > 0 && n > 0) ? p.pre_parts : 0;
+  const int npre = (plen > 0 && n > 0) ? p.pre_parts : 0;
   const int pstart = plen / kBlockSize + part * p.part_pages;
   const int pend = part == P - 1 ? npages : min(npages, pstart + p.part_pages);
   const bool has_work = n > 0 && pstart < pend;
@@ -664,7 +971,7 @@ __global__ __launch_bounds__(kDecodeThreads, (Cols<G, M>::NT > 1 ? 1 : PA_DECODE
     return (size_t)(q_row + my_c[j] / G) * p.num_q_heads + h0 + my_c[j] % G;
   };
 
-  if (P == 1) {
+  if (P == 1 && p.pre_items == 0) {
 #pragma unroll
     for (int j = 0; j < J; ++j) {
       if (!my_out[j]) continue;
@@ -724,7 +1031,8 @@ __global__ __launch_bounds__(kDecodeThreads, (Cols<G, M>::NT > 1 ? 1 : PA_DECODE
   __syncthreads();
   int32_t* counter = p.counters + (size_t)seq * p.num_kv_heads + g;
   if (threadIdx.x == 0)
-    s_last = (__hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == P - 1);
+    s_last = (__hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+              P - 1 + (p.pre_items > 0 ? npre : 0));
   __syncthreads();
   if (!s_last) return;
 

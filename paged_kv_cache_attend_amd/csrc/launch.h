@@ -60,6 +60,18 @@ struct DecodeParams {
   int32_t part_pages;         // 16-token pages per partition
   int32_t num_parts;
   int32_t causal;             // several tokens per slot: token t of m sees keys [0, n - m + t]
+  // Prefix-grouped decode in one launch: the first pre_items workgroups each
+  // stream a run of pre_pages shared pages of one group and KV head once for
+  // up to M of its members (the members' rows as the token columns) and
+  // write pre_out / pre_lse; the rest are the members' own-key partitions.
+  // A slot with a prefix then merges once all num_parts + pre_parts
+  // partials of it have arrived.  0 pre_items: the prefix pass ran before.
+  int32_t pre_items;
+  int32_t pre_pages;          // pages per prefix partition
+  int32_t pre_chunks;         // member chunks (of M members) per group
+  int32_t max_members;        // members of a group that share its prefix
+  const int32_t* group_start; // [num_groups + 1]: a group's slots are [group_start[i], group_start[i + 1])
+  const int32_t* prefix_len;  // [num_groups]: shared tokens (read as whole pages)
 };
 
 // Chunk path (several new rows per slot): bf16 MFMA for S = QK^T and O = PV.
@@ -127,6 +139,10 @@ bool decode_supports_group(int group);
 // (1, 2, 4 or 8), or 0 when the decode path does not apply.
 int decode_tokens_per_slot(int group, int max_q_len);
 constexpr int kDecodeThreads = 64 * kDecodeWaves;
+// Members per prefix item in a one-launch prefix-grouped decode: as many as
+// fill the 16 columns of one score tile with their query heads (8 with one
+// head per KV head, where the tile takes each column twice, hi and lo).
+constexpr int prefix_chunk_members(int group) { return group == 1 ? 8 : 16 / group; }
 hipError_t launch_decode(const DecodeParams& p, int group, int format, int tokens, unsigned grid, hipStream_t s);
 hipError_t launch_zero_i32(int32_t* x, size_t n, hipStream_t s);
 

@@ -53,26 +53,103 @@ def _kernels(asm: str):
         yield name, [l.strip() for l in asm[i:j].split("\n")]
 
 
+_BRANCH = re.compile(r"^s_(c?branch\w*)\s+(\.LBB\w+)")
+
+
+def _blocks(body):
+    """Basic blocks of a function body: (first line, last line) per block and
+    the successor edges (fall-through and branch targets)."""
+    starts = {0}
+    for n, l in enumerate(body):
+        if re.match(r"^\.LBB\w+:", l):
+            starts.add(n)
+        if _BRANCH.match(l) or l.startswith("s_endpgm"):
+            starts.add(n + 1)
+    starts = sorted(x for x in starts if x < len(body))
+    ends = [b - 1 for b in starts[1:]] + [len(body) - 1]
+    label_block = {}
+    for i, b in enumerate(starts):
+        m = re.match(r"^(\.LBB\w+):", body[b])
+        if m:
+            label_block[m.group(1)] = i
+    succ = []
+    for i, (b, e) in enumerate(zip(starts, ends)):
+        out = []
+        last = body[e]
+        m = _BRANCH.match(last)
+        if m:
+            out.append(label_block[m.group(2)])
+        if not (last.startswith("s_endpgm") or (m and m.group(1) == "branch")) and i + 1 < len(starts):
+            out.append(i + 1)
+        succ.append(out)
+    return starts, ends, succ
+
+
+def _dominated_loads(body, line):
+    """Vector-memory loads after `line` in its block and in every block that
+    block dominates: code that only runs after `line` has run."""
+    starts, ends, succ = _blocks(body)
+    nb = len(starts)
+    preds = [[] for _ in range(nb)]
+    for i, out in enumerate(succ):
+        for j in out:
+            preds[j].append(i)
+    # iterative dominators over the blocks reachable from the entry
+    reach, todo = {0}, [0]
+    while todo:
+        for j in succ[todo.pop()]:
+            if j not in reach:
+                reach.add(j)
+                todo.append(j)
+    dom = {i: set(reach) for i in reach}
+    dom[0] = {0}
+    changed = True
+    while changed:
+        changed = False
+        for i in sorted(reach):
+            if i == 0:
+                continue
+            ps = [dom[j] for j in preds[i] if j in reach]
+            new = (set.intersection(*ps) if ps else set()) | {i}
+            if new != dom[i]:
+                dom[i], changed = new, True
+    home = max(i for i, b in enumerate(starts) if b <= line)
+    loads = []
+    for i in sorted(reach):
+        if home not in dom[i]:
+            continue
+        lo = line + 1 if i == home else starts[i]
+        loads += [body[n] for n in range(lo, ends[i] + 1)
+                  if body[n].startswith("global_load") or body[n].startswith("buffer_load")]
+    return loads
+
+
 def test_every_decode_instance_publishes_before_counting_and_merges_coherently(decode_asm):
     count = 0
     for name, body in _kernels(decode_asm):
         count += 1
         atomics = [n for n, l in enumerate(body) if l.startswith("global_atomic_add")]
-        assert len(atomics) == 1, (name, "expected one counter atomic")
-        a = atomics[0]
-        # the partial stores just before the counter
-        stores = [n for n in range(max(0, a - 120), a) if body[n].startswith("global_store")]
-        assert stores, (name, "no partial store before the counter")
-        for n in stores:
-            assert "sc1" in body[n], (name, body[n])
-        last = stores[-1]
-        between = body[last + 1:a]
-        w = [k for k, l in enumerate(between) if l.startswith("s_waitcnt") and "vmcnt(0)" in l]
-        assert w, (name, "no vmcnt(0) between the partial stores and the counter")
-        assert any(l.startswith("s_barrier") for l in between[w[0]:]), (name, "no barrier after the wait")
-        # every load after the counter (the merge) reads coherently
-        loads = [l for l in body[a + 1:] if l.startswith("global_load")]
-        assert loads, (name, "no merge loads after the counter")
-        bad = [l for l in loads if "sc1" not in l]
-        assert not bad, (name, bad[:3])
+        # one counter per path: the slots' partitions, and in the instances
+        # that also run prefix items, theirs
+        assert 1 <= len(atomics) <= 2, (name, "expected one counter atomic per path")
+        for a in atomics:
+            # the partial stores just before the counter
+            stores = [n for n in range(max(0, a - 150), a) if body[n].startswith("global_store")]
+            assert stores, (name, "no partial store before the counter")
+            for n in stores:
+                assert "sc1" in body[n], (name, body[n])
+            last = stores[-1]
+            between = body[last + 1:a]
+            w = [k for k, l in enumerate(between) if l.startswith("s_waitcnt") and "vmcnt(0)" in l]
+            assert w, (name, "no vmcnt(0) between the partial stores and the counter")
+            assert any(l.startswith("s_barrier") for l in between[w[0]:]), (name, "no barrier after the wait")
+            # every load that only runs after the counter (the merge: after
+            # the barrier that publishes the counter's answer through LDS)
+            # reads coherently
+            bar = [n for n in range(a + 1, min(a + 60, len(body))) if body[n].startswith("s_barrier")]
+            assert bar, (name, "no barrier after the counter")
+            loads = _dominated_loads(body, bar[0])
+            assert loads, (name, "no merge loads after the counter")
+            bad = [l for l in loads if "sc1" not in l]
+            assert not bad, (name, bad[:3])
     assert count >= 12  # 3 group sizes x 4 page formats
