@@ -159,6 +159,9 @@ pa_status make_plan(const pa_shape* s, Plan* plan, bool grouped = false) {
 #ifndef PA_PREFIX_ONE_LAUNCH
 #define PA_PREFIX_ONE_LAUNCH 1
 #endif
+#ifndef PA_PREFIX_ITEM_PAGES
+#define PA_PREFIX_ITEM_PAGES 0  // pages per prefix item (0: the prefix pass's partitions)
+#endif
 
 namespace {
 
@@ -633,21 +636,27 @@ pa_status pa_attend_prefix(const pa_shape* shape, const pa_prefix_groups* groups
 
   // One launch for the shared and the own keys where the slots' own keys are
   // split (their merge then counts the prefix partials too): prefix items of
-  // prefix_chunk_members members each, as long as the slots' partitions (the
-  // prefix items go first, so they tend to be done first and the slots'
-  // partitions do the merging) and never more prefix partitions than the
-  // workspace holds.  The set-up workgroup (the slots' prefix lengths) runs
-  // alone before it.
+  // kDecodeWaves x prefix_chunk_members members each over the prefix pass's
+  // partitions (the prefix items go first, so they tend to be done first and
+  // the slots' partitions do the merging).  With fewer than 64 groups the
+  // partitions find their slot's group themselves; otherwise the set-up
+  // workgroup (the slots' prefix lengths) runs alone before.
   const int G = pp.suffix.group;
   const int mc = prefix_chunk_members(G);
-  if (PA_PREFIX_ONE_LAUNCH && pp.pre_grid > 0 && pp.suffix.decode && pp.suffix.num_parts > 1) {
+  if (PA_PREFIX_ONE_LAUNCH && pp.pre_grid > 0 && pp.suffix.decode && pp.suffix.num_parts > 1 &&
+      decode_prefix_supports_group(G)) {
     const int max_pages = groups->max_prefix_len / kBlockSize;
-    const int pre_pages = pp.pre_pages > pp.suffix.part_pages ? pp.pre_pages : pp.suffix.part_pages;
+    const int pre_pages = PA_PREFIX_ITEM_PAGES > 0 ? PA_PREFIX_ITEM_PAGES : pp.pre_pages;
     const int pre_parts = ceil_div(max_pages, pre_pages);
-    const int chunks = ceil_div(groups->max_members, mc);
+    const int chunks = ceil_div(groups->max_members, kDecodeWaves * mc);
     const long long items = (long long)groups->num_groups * shape->num_kv_heads * pre_parts * chunks;
     if (pre_parts <= pp.pre_parts && items > 0 && items + pp.suffix.grid <= INT_MAX) {
-      if (launch_prefix(pr, 0, s) != hipSuccess) return PA_ERR_LAUNCH;
+      if (groups->num_groups < 64) {
+        d.slot_plen = nullptr;
+        d.num_groups = groups->num_groups;
+      } else if (launch_prefix(pr, 0, s) != hipSuccess) {
+        return PA_ERR_LAUNCH;
+      }
       d.pre_parts = pre_parts;
       d.pre_items = (int)items;
       d.pre_pages = pre_pages;
@@ -655,7 +664,7 @@ pa_status pa_attend_prefix(const pa_shape* shape, const pa_prefix_groups* groups
       d.max_members = groups->max_members;
       d.group_start = groups->group_start;
       d.prefix_len = groups->prefix_len;
-      if (launch_decode(d, G, kFmtBF16, mc, (unsigned)(items + pp.suffix.grid), s) != hipSuccess)
+      if (launch_decode_prefix(d, G, (unsigned)(items + pp.suffix.grid), s) != hipSuccess)
         return PA_ERR_LAUNCH;
       return PA_OK;
     }

@@ -243,24 +243,16 @@ struct WaveState {
   u32x4_t qb[NT][4];  // Q^T operand of step s: dims 32 s + 8 (lane / 16) .. + 8 of that column
 };
 
-// `sk` / `sv` are this wave's 4 KiB LDS tiles, `sks` / `svs` its 16 x 4
-// group scales (q8_0, q4_0).  `kbase` is the page's first key index and
-// lim[ct] the last key this lane's column of tile ct may see (several tokens
-// per slot only).
-template <int G, int F, int M>
-__device__ __forceinline__ void consume_page(WaveState<Cols<G, M>::NT>& st, Page<F>& b, uint8_t* sk, uint8_t* sv,
-                                               float* sks, float* svs, int valid, float scale_log2, int lane,
-                                               int kbase, const int* lim) {
-  using CS = Cols<G, M>;
-  constexpr int NT = CS::NT;
+// A page's K and V tiles -> the 4 KiB LDS tiles `sk` / `sv` as bf16, row t
+// keeping its 16-byte chunk c at slot c ^ t; `sks` / `svs` take its 16 x 4
+// group scales (q8_0, q4_0).  V rows past the end are zeroed: their codes
+// may decode to anything, NaN included, and a zero weight would not cancel
+// that.
+template <int F>
+__device__ __forceinline__ void stage_page(const Page<F>& b, uint8_t* sk, uint8_t* sv, float* sks, float* svs,
+                                           int valid, int lane) {
   const int pr = lane >> 4;
   const int pc = lane & 15;
-  constexpr bool kGrouped = F == kFmtQ8 || F == kFmtQ4;
-  static_assert(!kGrouped || M == 1, "grouped page formats decode one token per slot");
-
-  // K and V tiles -> LDS as bf16, row t keeping its 16-byte chunk c at slot
-  // c ^ t.  V rows past the end are zeroed: their codes may decode to
-  // anything, NaN included, and a zero weight would not cancel that.
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const int t = 4 * k + pr;
@@ -268,11 +260,25 @@ __device__ __forceinline__ void consume_page(WaveState<Cols<G, M>::NT>& st, Page
     const u32x4_t vv = chunk_to_bf16<F>(b.v[k]);
     *reinterpret_cast<u32x4_t*>(sv + t * 256 + ((pc ^ t) << 4)) = t < valid ? vv : u32x4_t{0u, 0u, 0u, 0u};
   }
-  if constexpr (kGrouped) {
+  if constexpr (F == kFmtQ8 || F == kFmtQ4) {
     sks[lane] = half_bits_to_float(b.ks);  // [token][group]
     svs[lane] = half_bits_to_float(b.vs);
   }
-  wave_lds_sync();
+}
+
+// Scores and weighted values of one staged page for this wave's columns.
+// `kbase` is the page's first key index and lim[ct] the last key this lane's
+// column of tile ct may see (several tokens per slot only).
+template <int G, int F, int M>
+__device__ __forceinline__ void score_page(WaveState<Cols<G, M>::NT>& st, const uint8_t* sk, const uint8_t* sv,
+                                           const float* sks, const float* svs, int valid, float scale_log2, int lane,
+                                           int kbase, const int* lim) {
+  using CS = Cols<G, M>;
+  constexpr int NT = CS::NT;
+  const int pr = lane >> 4;
+  const int pc = lane & 15;
+  constexpr bool kGrouped = F == kFmtQ8 || F == kFmtQ4;
+  static_assert(!kGrouped || M == 1, "grouped page formats decode one token per slot");
 
   // Scores: A = K (row = token pc, dims 32 s + 8 pr .. + 8 of step s), B = Q^T.
   // A group of 32 dims is one step, so grouped scales weight each step's
@@ -391,25 +397,47 @@ __device__ __forceinline__ void consume_page(WaveState<Cols<G, M>::NT>& st, Page
   }
 }
 
+// One page of this wave's own: staged in its LDS tiles, then scored.
+template <int G, int F, int M>
+__device__ __forceinline__ void consume_page(WaveState<Cols<G, M>::NT>& st, Page<F>& b, uint8_t* sk, uint8_t* sv,
+                                             float* sks, float* svs, int valid, float scale_log2, int lane,
+                                             int kbase, const int* lim) {
+  stage_page<F>(b, sk, sv, sks, svs, valid, lane);
+  wave_lds_sync();
+  score_page<G, F, M>(st, sk, sv, sks, svs, valid, scale_log2, lane, kbase, lim);
+}
+
 // One prefix item of a prefix-grouped decode done in one launch (pre_items
 // > 0): pages [pp pre_pages, ...) of one group's shared prefix for one KV
-// head, streamed once for up to M of the group's members, whose rows are the
-// token columns (member rows are consecutive: each member brings at most one
-// row on this path).  A member sees the prefix up to its own length.  The
-// item writes its members' partials to pre_out / pre_lse (normalised, with
-// their LSE; -inf where no key is visible), counts them on each member's
-// counter like a partition of that slot, and merges the slots it arrives
-// last for.  Everything below mirrors the partition path of decode_kernel.
+// head, read once for up to kWaves M of the group's members.  The waves take
+// turns loading the pages (wave w the w-th of every kWaves) and stage them in
+// LDS; after a barrier every wave scores all kWaves staged pages for its own
+// M members: column c of wave w is member w M + c / G, query head h0 + c % G
+// (each member brings at most one row on this path).  Each wave so ends with
+// the whole range for its members, and the waves need no merge.  Two stages
+// alternate (the second in the epilogue area, when that is large enough), so
+// one barrier per step orders both the writes and the reuse.  A member sees
+// the prefix up to its own length.  The item writes its members' partials to
+// pre_out / pre_lse (normalised, with their LSE; -inf where no key is
+// visible), counts them on each member's counter like a partition of that
+// slot, and merges the slots it arrives last for, with the ordering of the
+// partition path.
 template <int G, int F, int M>
 __device__ __forceinline__ void prefix_item(const DecodeParams& p, int pi, int lane, int wave,
                                             uint8_t (*s_k)[kTileBytes], uint8_t (*s_v)[kTileBytes],
-                                            float (*s_ks)[kBlockSize * 4], float (*s_vs)[kBlockSize * 4],
-                                            uint8_t (*s_q)[kHeadDim * 2], float (*s_acc)[Cols<G, M>::C][kHeadDim],
+                                            float (*s_acc)[Cols<G, M>::C][kHeadDim],
                                             float (*s_m)[Cols<G, M>::C], float (*s_l)[Cols<G, M>::C],
                                             float (*s_r)[Cols<G, M>::C], int* s_lastm) {
   using CS = Cols<G, M>;
   constexpr int C = CS::C;
-  constexpr int NT = CS::NT;
+  static_assert(CS::NT == 1 && F == kFmtBF16, "one bf16 column tile per wave");
+  constexpr int kMembers = kWaves * M;
+  static_assert(kMembers <= 64, "one lane per member");
+  constexpr bool kTwoStages = sizeof(float) * kWaves * C * kHeadDim >= 2 * kWaves * kTileBytes;
+  constexpr int kPRing = 2;  // pages per wave in flight; ring slot r uses stage r
+  uint8_t (*s_k2)[kTileBytes] = reinterpret_cast<uint8_t (*)[kTileBytes]>(&s_acc[0][0][0]);
+  uint8_t (*s_v2)[kTileBytes] = s_k2 + kWaves;
+
   const int ci = pi % p.pre_chunks;
   int rest = pi / p.pre_chunks;
   const int pp = rest % p.pre_parts;
@@ -417,280 +445,240 @@ __device__ __forceinline__ void prefix_item(const DecodeParams& p, int pi, int l
   const int g = rest % p.num_kv_heads;
   const int gi = rest / p.num_kv_heads;
 
-  // The group's bounds and prefix length, then the chunk members' lengths
-  // and the row offset of its first member.
+  // The group's bounds and prefix length; then, in one round trip, the
+  // members' lengths (lane j: member j of the item), the row offset of the
+  // group's slots before them and the page ids of this wave's first pages.
   int s0 = scalar_load_i32(p.group_start, gi);
   int s1 = scalar_load_i32(p.group_start, gi + 1);
   int plen = scalar_load_i32(p.prefix_len, gi);
   asm volatile("" : "+s"(s0), "+s"(s1), "+s"(plen));
   plen = max(plen, 0) & ~(kBlockSize - 1);  // whole pages, as the partitions read it
   const int members = min(s1 - s0, p.max_members);
-  const int j0 = ci * M;
+  const int j0 = ci * kMembers;
   if (plen <= 0 || j0 >= members) return;
-  const int jn = min(M, members - j0);
+  const int jn = min(kMembers, members - j0);
   const int sf = s0 + j0;
-  int mq[M], mn[M];
-#pragma unroll
-  for (int j = 0; j < M; ++j) {
-    mq[j] = scalar_load_i32(p.q_lens, sf + min(j, jn - 1));
-    mn[j] = scalar_load_i32(p.ctx_lens, sf + min(j, jn - 1));
-  }
-  int qsum = 0;
-  for (int i = lane; i < sf; i += 64) qsum += p.q_lens[i];
-#pragma unroll
-  for (int j = 0; j < M; ++j) asm volatile("" : "+s"(mq[j]), "+s"(mn[j]));
-  asm volatile("" : "+v"(qsum));
-  // Token t = the t-th member with a row; its length and member index.
-  int mt = 0;
-#pragma unroll
-  for (int j = 0; j < M; ++j) mt += (j < jn && mq[j] > 0) ? 1 : 0;
-  if (mt == 0) return;  // no rows: nothing to write, nothing to count
-  auto token_member = [&](int t) -> int {  // member index of token t (M if none)
-    int cnt = 0, jm = M;
-#pragma unroll
-    for (int j = 0; j < M; ++j) {
-      const bool has = j < jn && mq[j] > 0;
-      if (has && cnt == t) jm = j;
-      cnt += has ? 1 : 0;
-    }
-    return jm;
-  };
-  auto member_n = [&](int jm) -> int {
-    int r = 0;
-#pragma unroll
-    for (int j = 0; j < M; ++j) r = jm == j ? mn[j] : r;
-    return r;
-  };
-
   const int32_t* bt = p.block_table + (size_t)s0 * p.max_blocks;  // the group's shared pages
   // (the last partition runs to the group's prefix end, as in the prefix pass)
   const int pstart = pp * p.pre_pages;
-  const int pend = pp == p.pre_parts - 1 ? plen / kBlockSize : min(pstart + p.pre_pages, plen / kBlockSize);
+  const int pend = min(pp == p.pre_parts - 1 ? plen / kBlockSize : min(pstart + p.pre_pages, plen / kBlockSize),
+                       p.max_blocks);
   const bool has_work = pstart < pend;
   const int last_page = pend - 1;
-  auto page_id = [&](int page) -> int32_t { return scalar_load_i32(bt, min(page, last_page)); };
-  const int h0 = g * G;
-  const size_t rows = (size_t)p.total_q * p.num_q_heads;
+  // The ids of the item's first 64 pages, one per lane, read from there
+  // (v_readlane: no memory wait, which the barriers would otherwise take
+  // for every prefetched id); further pages, only where a prefix outruns
+  // the partition sizes, by scalar loads.
+  const int pid = has_work ? bt[min(pstart + lane, last_page)] : 0;
+  auto page_id = [&](int page) -> int32_t {
+    page = min(page, last_page) - pstart;
+    return page < 64 ? __builtin_amdgcn_readlane(pid, page) : scalar_load_i32(bt, page + pstart);
+  };
+  const int jl = min(lane, jn - 1);
+  const int mq = p.q_lens[sf + jl];
+  const int mn = p.ctx_lens[sf + jl];
+  int qsum = 0;
+  for (int i = lane; i < sf; i += 64) qsum += p.q_lens[i];
+  const uint64_t rowmask = __builtin_amdgcn_ballot_w64(lane < jn && mq > 0);
+  if (rowmask == 0) return;  // no rows: nothing to write, nothing to count
 
-  Page<F> ring[kRing];
-  const int page0 = pstart + wave;
-  const int cnt = (has_work && page0 < pend) ? (pend - page0 + kWaves - 1) / kWaves : 0;
-  int32_t next_id = 0;
-  int q_row;
-  if (has_work) {
-    issue_page<F>(ring[0], p, page_id(page0), g, lane);
-    __builtin_amdgcn_sched_barrier(0);
-    q_row = __builtin_amdgcn_readfirstlane(wave_sum_i32(qsum));
-    constexpr int kQChunks = (C * 16 + kDecodeThreads - 1) / kDecodeThreads;
-    u32x4_t qchunk[kQChunks];
-#pragma unroll
-    for (int j = 0; j < kQChunks; ++j) {
-      const int idx = threadIdx.x + j * kDecodeThreads;
-      const int c = min(idx >> 4, C - 1), qc = idx & 15;
-      const int tok = min(c / G, mt - 1);
-      qchunk[j] = reinterpret_cast<const u32x4_t*>(p.q)[((size_t)(q_row + tok) * p.num_q_heads + h0 + c % G) * 16 + qc];
-    }
-    issue_order_barrier();
-#pragma unroll
-    for (int r = 1; r < kRing; ++r) issue_page<F>(ring[r], p, page_id(page0 + r * kWaves), g, lane);
-    next_id = page_id(page0 + kRing * kWaves);
-#pragma unroll
-    for (int j = 0; j < kQChunks; ++j) {
-      const int idx = threadIdx.x + j * kDecodeThreads;
-      const int c = idx >> 4, qc = idx & 15;
-      if (c < C) *reinterpret_cast<u32x4_t*>(&s_q[c][(qc ^ (c & 15)) << 4]) = qchunk[j];
-    }
-    __syncthreads();
-  } else {
-    q_row = __builtin_amdgcn_readfirstlane(wave_sum_i32(qsum));
-  }
-
+  Page<F> ring[kPRing];
+  if (has_work) issue_page<F>(ring[0], p, page_id(pstart + wave), g, lane);
+  __builtin_amdgcn_sched_barrier(0);  // the first page goes out before the row-offset sum
+  const int q_row = __builtin_amdgcn_readfirstlane(wave_sum_i32(qsum));
+  // This lane's column (the lo copy maps back to the hi one), its member,
+  // whether that is live, the last key it may see and the member's row.
   const int pr = lane >> 4;
   const int pc = lane & 15;
-  int col[NT];
-  bool col_live[NT];
-  int lim[NT];
+  const int col = CS::HL ? (pc & (C - 1)) : pc;
+  const int jm = wave * M + col / G;
+  const int nm = __shfl(mn, jm, 64);
+  const bool has_row = jm < jn && ((rowmask >> jm) & 1);
+  const bool live = has_row && nm > 0;
+  const int lim[1] = {min(plen, nm) - 1};
+  const int qr = has_row ? q_row + __popcll(rowmask & ((1ull << jm) - 1)) : q_row;
+  const u32x4_t* qp = reinterpret_cast<const u32x4_t*>(p.q) + ((size_t)qr * p.num_q_heads + g * G + col % G) * 16;
+  u32x4_t qv[4];
 #pragma unroll
-  for (int ct = 0; ct < NT; ++ct) {
-    const int n16 = ct * 16 + pc;
-    col[ct] = CS::HL ? (n16 & (C - 1)) : n16;
-    const bool in_tile = CS::HL ? n16 < 2 * C : n16 < C;
-    const int tok = col[ct] / G;
-    const int nt = member_n(token_member(tok));
-    col_live[ct] = in_tile && tok < mt && nt > 0;
-    lim[ct] = min(plen, nt) - 1;
-  }
-
+  for (int sg = 0; sg < 4; ++sg) qv[sg] = qp[4 * sg + pr];
+  issue_order_barrier();
   if (has_work) {
-    WaveState<NT> st;
 #pragma unroll
-    for (int ct = 0; ct < NT; ++ct) {
-      st.m_ref[ct] = -INFINITY;
-      st.l_lane[ct] = 0.f;
-      st.r_lane[ct] = 0.f;
-#pragma unroll
-      for (int bb = 0; bb < 8; ++bb) st.o[ct][bb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      const int c = min(col[ct], C - 1);
-#pragma unroll
-      for (int sg = 0; sg < 4; ++sg) {
-        const u32x4_t x = *reinterpret_cast<const u32x4_t*>(&s_q[c][((4 * sg + pr) ^ (c & 15)) << 4]);
-        st.qb[ct][sg] = col_live[ct] ? x : u32x4_t{0u, 0u, 0u, 0u};
-      }
-    }
-    uint8_t* sk = s_k[wave];
-    uint8_t* sv = s_v[wave];
-    float* sks = s_ks[wave];
-    float* svs = s_vs[wave];
-#define PA_CONSUME(RING, K)                                                                            \
-  consume_page<G, F, M>(st, RING, sk, sv, sks, svs, kBlockSize, p.scale_log2, lane,                    \
-                        (page0 + kWaves * (K)) * kBlockSize, lim)
-#define PA_REISSUE(RING, K)                                          \
-  {                                                                  \
-    issue_page<F>(RING, p, next_id, g, lane);                        \
-    next_id = page_id(page0 + kWaves * ((K) + 1));                   \
+    for (int r = 1; r < kPRing; ++r) issue_page<F>(ring[r], p, page_id(pstart + wave + r * kWaves), g, lane);
   }
+  const bool wave_live = __builtin_amdgcn_ballot_w64(live) != 0;
+
+  WaveState<1> st;
+  st.m_ref[0] = -INFINITY;
+  st.l_lane[0] = 0.f;
+  st.r_lane[0] = 0.f;
+#pragma unroll
+  for (int bb = 0; bb < 8; ++bb) st.o[0][bb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int sg = 0; sg < 4; ++sg) st.qb[0][sg] = live ? qv[sg] : u32x4_t{0u, 0u, 0u, 0u};
+
+  // Step k: this wave's page pstart + wave + k kWaves (ring slot r = k %
+  // kPRing) -> stage r, the slot reloaded for step k + kPRing; barrier; the
+  // step's kWaves pages scored (only the last step can be short).  The main
+  // loop reissues unconditionally, as the partition path does.
+  auto step = [&](Page<F>& b, auto r_c, int k, bool reissue, bool full) {
+    constexpr bool second = kTwoStages && decltype(r_c)::value == 1;
+    uint8_t (*tk)[kTileBytes] = second ? s_k2 : s_k;
+    uint8_t (*tv)[kTileBytes] = second ? s_v2 : s_v;
+    stage_page<F>(b, tk[wave], tv[wave], nullptr, nullptr, kBlockSize, lane);
+    if (reissue) issue_page<F>(b, p, page_id(pstart + wave + (k + kPRing) * kWaves), g, lane);
+    __syncthreads();
+    if (wave_live) {
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const int page = pstart + k * kWaves + w;
+        if (full || page < pend)
+          score_page<G, F, M>(st, tk[w], tv[w], nullptr, nullptr, kBlockSize, p.scale_log2, lane, page * kBlockSize,
+                              lim);
+      }
+    }
+    if (!kTwoStages) __syncthreads();
+  };
+  if (has_work) {
+    const int nsteps = (pend - pstart + kWaves - 1) / kWaves;
+    static_assert(kPRing == 2, "the steps below are unrolled by the ring depth");
+    using R0 = std::integral_constant<int, 0>;
+    using R1 = std::integral_constant<int, 1>;
     int k = 0;
-    for (; k + 2 * kRing - 1 < cnt; k += kRing) {
-#pragma unroll
-      for (int r = 0; r < kRing; ++r) {
-        PA_CONSUME(ring[r], k + r);
-        PA_REISSUE(ring[r], k + r + kRing);
-      }
+    for (; k + 3 < nsteps; k += 2) {
+      step(ring[0], R0{}, k, true, true);
+      step(ring[1], R1{}, k + 1, true, true);
     }
-#pragma unroll
-    for (int r = 0; r < kRing; ++r) {
-      if (k + r < cnt) {
-        PA_CONSUME(ring[r], k + r);
-        if (k + r + kRing < cnt) PA_REISSUE(ring[r], k + r + kRing);
-      }
-    }
-#pragma unroll
-    for (int r = 0; r < kRing - 1; ++r)
-      if (k + kRing + r < cnt) PA_CONSUME(ring[r], k + kRing + r);
-#undef PA_CONSUME
-#undef PA_REISSUE
-#pragma unroll
-    for (int ct = 0; ct < NT; ++ct) {
-      float l_sum = st.l_lane[ct] + other16(st.l_lane[ct]);
+    // At most 3 steps left: k, k + 1 in the ring (those that exist), k + 2
+    // to be issued.
+    if (k < nsteps) step(ring[0], R0{}, k, k + 2 < nsteps, false);
+    if (k + 1 < nsteps) step(ring[1], R1{}, k + 1, false, false);
+    if (k + 2 < nsteps) step(ring[0], R0{}, k + 2, false, false);
+    if (kTwoStages) __syncthreads();  // the second stage is the area written next
+
+    // This wave's columns -> LDS (a column's sum is spread over lanes pc +
+    // 16 j; the lo copy, lane ^ C, is added when the tile holds one).
+    if (wave_live) {
+      float l_sum = st.l_lane[0] + other16(st.l_lane[0]);
       l_sum += other_half(l_sum);
-      float r_sum = st.r_lane[ct] + other16(st.r_lane[ct]);
+      float r_sum = st.r_lane[0] + other16(st.r_lane[0]);
       r_sum += other_half(r_sum);
       f32x4_t o_tot[8];
 #pragma unroll
       for (int bb = 0; bb < 8; ++bb)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          o_tot[bb][i] = CS::HL ? st.o[ct][bb][i] + __shfl_xor(st.o[ct][bb][i], C, 64) : st.o[ct][bb][i];
-      const int c = ct * 16 + pc;
-      if (c < C) {
+          o_tot[bb][i] = CS::HL ? st.o[0][bb][i] + __shfl_xor(st.o[0][bb][i], C, 64) : st.o[0][bb][i];
+      if (pc < C) {
         if (pr == 0) {
-          s_m[wave][c] = st.m_ref[ct];
-          s_l[wave][c] = l_sum;
-          s_r[wave][c] = CS::HL ? l_sum : r_sum;
+          s_m[wave][pc] = st.m_ref[0];
+          s_l[wave][pc] = l_sum;
+          s_r[wave][pc] = CS::HL ? l_sum : r_sum;
         }
 #pragma unroll
-        for (int bb = 0; bb < 8; ++bb) *reinterpret_cast<f32x4_t*>(&s_acc[wave][c][16 * bb + 4 * pr]) = o_tot[bb];
+        for (int bb = 0; bb < 8; ++bb) *reinterpret_cast<f32x4_t*>(&s_acc[wave][pc][16 * bb + 4 * pr]) = o_tot[bb];
       }
     }
     __syncthreads();
   }
 
-  // Each thread: J (column, dim pair) outputs, as in the partition epilogue.
-  constexpr int J = CS::J;
-  float my_o0[J], my_o1[J], my_lse[J];
-  int my_c[J], my_d[J];
-  bool my_out[J];
-#pragma unroll
-  for (int j = 0; j < J; ++j) {
-    const int i = threadIdx.x + j * kDecodeThreads;
-    my_c[j] = min(i >> 6, C - 1);
-    my_d[j] = (i & 63) * 2;
-    const int tok = my_c[j] / G;
-    my_out[j] = i < C * 64 && tok < mt && member_n(token_member(tok)) > 0;
-    my_o0[j] = 0.f;
-    my_o1[j] = 0.f;
-    my_lse[j] = -INFINITY;
-    if (has_work && my_out[j]) {
-      const int c = my_c[j], d = my_d[j];
-      float Mx = -INFINITY;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) Mx = fmaxf(Mx, s_m[w][c]);
-      if (Mx != -INFINITY) {
-        float L = 0.f, R = 0.f, a0 = 0.f, a1 = 0.f;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
-          const float sc = fast_exp2(s_m[w][c] - Mx);
-          L = fmaf(sc, s_l[w][c], L);
-          R = fmaf(sc, s_r[w][c], R);
-          const float2 v = *reinterpret_cast<const float2*>(&s_acc[w][c][d]);
-          a0 = fmaf(sc, v.x, a0);
-          a1 = fmaf(sc, v.y, a1);
-        }
-        const float inv = 1.f / R;
-        my_o0[j] = a0 * inv;
-        my_o1[j] = a1 * inv;
-        my_lse[j] = (Mx + fast_log2(L)) * kLn2;
-      }
-    }
-  }
-  auto row_of = [&](int j) -> size_t {
-    return (size_t)(q_row + my_c[j] / G) * p.num_q_heads + h0 + my_c[j] % G;
-  };
   // Publish, count and merge with the ordering of the partition path (see
   // there): device-scope stores, their acknowledgement, a barrier, then each
-  // member's counter; the merger's loads are device-scope.
-  float* pre_out = const_cast<float*>(p.pre_out);
+  // member's counter; the merger's loads are device-scope.  Both the
+  // publication and the merges take 16 lanes per column of the item, 8 dims
+  // each (column wc = wave wc / C's column wc % C), so that a wave covers 4
+  // columns at once.
+  const size_t rows = (size_t)p.total_q * p.num_q_heads;
+  constexpr int kTasks = kWaves * C * 16;
+  static_assert(kTasks % kDecodeThreads == 0, "whole rounds of (column, 8 dims) tasks");
+  auto row_of = [&](int c, int jc) -> size_t {
+    return (size_t)(q_row + __popcll(rowmask & ((1ull << jc) - 1))) * p.num_q_heads + g * G + c % G;
+  };
+  uint64_t* pre_out64 = reinterpret_cast<uint64_t*>(const_cast<float*>(p.pre_out));
   float* pre_lse = const_cast<float*>(p.pre_lse);
-  uint64_t* pre_out64 = reinterpret_cast<uint64_t*>(pre_out);
+  // (All LDS reads first, then the stores under their conditions: the
+  // rounds' reads overlap instead of waiting behind each branch.)
+  constexpr int kRounds = kTasks / kDecodeThreads;
+  float pm[kRounds], pl[kRounds], prr[kRounds];
+  f32x4_t pv0[kRounds], pv1[kRounds];
+  bool pub[kRounds];
 #pragma unroll
-  for (int j = 0; j < J; ++j) {
-    if (!my_out[j]) continue;
-    const size_t prow = (size_t)pp * rows + row_of(j);
-    if (my_lse[j] != -INFINITY) {
-      const uint64_t bits = (uint64_t)__float_as_uint(my_o0[j]) | ((uint64_t)__float_as_uint(my_o1[j]) << 32);
-      __hip_atomic_store(pre_out64 + (prow * kHeadDim + my_d[j]) / 2, bits, __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_AGENT);
+  for (int k = 0; k < kRounds; ++k) {
+    const int t = k * kDecodeThreads + (int)threadIdx.x;
+    const int wc = t >> 4, d8 = (t & 15) * 8;
+    const int w = wc / C, c = wc % C, jc = w * M + c / G;
+    const int njc = __shfl(mn, jc & 63, 64);
+    pub[k] = jc < jn && ((rowmask >> jc) & 1) && njc > 0;
+    pm[k] = has_work ? s_m[w][c] : -INFINITY;
+    pl[k] = s_l[w][c];
+    prr[k] = s_r[w][c];
+    pv0[k] = *reinterpret_cast<const f32x4_t*>(&s_acc[w][c][d8]);
+    pv1[k] = *reinterpret_cast<const f32x4_t*>(&s_acc[w][c][d8 + 4]);
+  }
+#pragma unroll
+  for (int k = 0; k < kRounds; ++k) {
+    if (!pub[k]) continue;
+    const int t = k * kDecodeThreads + (int)threadIdx.x;
+    const int wc = t >> 4, d8 = (t & 15) * 8;
+    const int c = wc % C, jc = (wc / C) * M + c / G;
+    const size_t prow = (size_t)pp * rows + row_of(c, jc);
+    float lse = -INFINITY;
+    if (pm[k] != -INFINITY) {
+      const float inv = 1.f / prr[k];
+      const float o[8] = {pv0[k][0], pv0[k][1], pv0[k][2], pv0[k][3], pv1[k][0], pv1[k][1], pv1[k][2], pv1[k][3]};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint64_t bits =
+            (uint64_t)__float_as_uint(o[2 * q] * inv) | ((uint64_t)__float_as_uint(o[2 * q + 1] * inv) << 32);
+        __hip_atomic_store(pre_out64 + (prow * kHeadDim + d8) / 2 + q, bits, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+      }
+      lse = (pm[k] + fast_log2(pl[k])) * kLn2;
     }
-    if (my_d[j] == 0) __hip_atomic_store(pre_lse + prow, my_lse[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (d8 == 0) __hip_atomic_store(pre_lse + prow, lse, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   wait_vm_stores();
   __syncthreads();
-  if ((int)threadIdx.x < mt) {
-    const int jm = token_member((int)threadIdx.x);
+  if ((int)threadIdx.x < jn) {  // wave 0, lane = member
     int last = 0;
-    if (member_n(jm) > 0) {
-      int32_t* counter = p.counters + (size_t)(sf + jm) * p.num_kv_heads + g;
+    if (((rowmask >> lane) & 1) && mn > 0) {
+      int32_t* counter = p.counters + (size_t)(sf + lane) * p.num_kv_heads + g;
       last = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
              p.num_parts + p.pre_parts - 1;
     }
-    s_lastm[threadIdx.x] = last;
+    s_lastm[lane] = last;
   }
   __syncthreads();
-#pragma unroll
-  for (int j = 0; j < J; ++j) {
-    if (!my_out[j] || !s_lastm[my_c[j] / G]) continue;
-    const size_t row = row_of(j);
-    const int d = my_d[j];
-    MergeState ms;
-    merge_partials(ms, p.part_lse + row, p.part_out + row * kHeadDim + d, p.num_parts, p.pre_lse + row,
-                   p.pre_out + row * kHeadDim + d, p.pre_parts, rows);
+#pragma unroll 1
+  for (int t = threadIdx.x; t < kTasks; t += kDecodeThreads) {
+    const int wc = t >> 4, d8 = (t & 15) * 8;
+    const int c = wc % C, jc = (wc / C) * M + c / G;
+    const int njc = __shfl(mn, jc & 63, 64);
+    if (!(jc < jn && ((rowmask >> jc) & 1) && njc > 0 && s_lastm[jc])) continue;
+    const size_t row = row_of(c, jc);
+    MergeState8 ms;
+    merge_partials8(ms, p.part_lse + row, p.part_out + row * kHeadDim + d8, p.num_parts, p.pre_lse + row,
+                    p.pre_out + row * kHeadDim + d8, p.pre_parts, rows);
     if (ms.M != -INFINITY) {
       const float inv = 1.f / ms.W;
-      reinterpret_cast<uint32_t*>(p.out)[(row * kHeadDim + d) / 2] = pack_bf16x2(ms.a0 * inv, ms.a1 * inv);
-      if (d == 0 && p.lse) p.lse[row] = ms.M + fast_log2(ms.W) * kLn2;
+      u32x4_t o;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) o[j] = pack_bf16x2(ms.a[2 * j] * inv, ms.a[2 * j + 1] * inv);
+      *reinterpret_cast<u32x4_t*>(p.out + row * kHeadDim + d8) = o;
+      if (d8 == 0 && p.lse) p.lse[row] = ms.M + fast_log2(ms.W) * kLn2;
     }
   }
-  if ((int)threadIdx.x < mt && s_lastm[threadIdx.x]) {
-    const int jm = token_member((int)threadIdx.x);
-    __hip_atomic_store(p.counters + (size_t)(sf + jm) * p.num_kv_heads + g, 0, __ATOMIC_RELAXED,
+  if ((int)threadIdx.x < jn && s_lastm[lane])
+    __hip_atomic_store(p.counters + (size_t)(sf + lane) * p.num_kv_heads + g, 0, __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
-  }
 }
 
 #ifndef PA_DECODE_MIN_WGS
 #define PA_DECODE_MIN_WGS kDecodeWGsPerCU
 #endif
-template <int G, int F, int M>
+// kPre: the instance of a one-launch prefix-grouped decode, whose first
+// pre_items workgroups are prefix items (one token per slot).
+template <int G, int F, int M, bool kPre = false>
 __global__ __launch_bounds__(kDecodeThreads, (Cols<G, M>::NT > 1 ? 1 : PA_DECODE_MIN_WGS)) void decode_kernel(
     DecodeParams p) {
   static_assert(G == 1 || G == 2 || G == 4 || G == 8, "group size");
@@ -708,24 +696,31 @@ __global__ __launch_bounds__(kDecodeThreads, (Cols<G, M>::NT > 1 ? 1 : PA_DECODE
   __shared__ float s_l[kWaves][C];
   __shared__ float s_r[kWaves][C];
   __shared__ int s_last;
-  __shared__ int s_lastm[M];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   // The kernel arguments the start needs, fetched together (the compiler
   // would otherwise fetch some of them one round trip later).
   asm volatile("" ::"s"(p.q_lens), "s"(p.ctx_lens), "s"(p.block_table), "s"(p.slot_plen), "s"(p.pre_parts), "s"(p.num_parts),
-               "s"(p.pre_items),
+               "s"(p.pre_items), "s"(p.num_groups), "s"(p.group_start), "s"(p.max_members),
                "s"(p.num_seqs), "s"(p.part_pages), "s"(p.max_blocks), "s"(gridDim.x));
 
   // One launch of prefix-grouped decode: the first pre_items workgroups are
   // prefix items (dispatched first); the rest are the slots' partitions.
-  if ((int)blockIdx.x < p.pre_items) {
-    if constexpr (F == kFmtBF16 && M == prefix_chunk_members(G)) {
-      prefix_item<G, F, M>(p, xcd_remap(blockIdx.x, p.pre_items), lane, wave, s_k, s_v, s_ks, s_vs, s_q, s_acc, s_m,
-                           s_l, s_r, s_lastm);
+  if constexpr (kPre) {
+    static_assert(F == kFmtBF16 && M == 1, "prefix items: bf16 pages, one token per slot");
+    if ((int)blockIdx.x < p.pre_items) {
+      constexpr int PM = prefix_chunk_members(G);
+      constexpr int PC = Cols<G, PM>::C;
+      __shared__ __attribute__((aligned(16))) float s_pacc[kWaves][PC][kHeadDim];
+      __shared__ float s_pm[kWaves][PC];
+      __shared__ float s_pl[kWaves][PC];
+      __shared__ float s_pr[kWaves][PC];
+      __shared__ int s_lastm[kWaves * PM];
+      prefix_item<G, F, PM>(p, xcd_remap(blockIdx.x, p.pre_items), lane, wave, s_k, s_v, s_pacc, s_pm, s_pl, s_pr,
+                            s_lastm);
+      return;
     }
-    return;
   }
   const int wg = xcd_remap(blockIdx.x - p.pre_items, gridDim.x - p.pre_items);
   const int P = p.num_parts;
@@ -747,7 +742,11 @@ __global__ __launch_bounds__(kDecodeThreads, (Cols<G, M>::NT > 1 ? 1 : PA_DECODE
   // Prefix-grouped decode: this slot's keys start after its shared prefix,
   // whose partials the prefix pass has written; the last partition runs to
   // the slot's end whatever the prefix length.
-  const int plen = p.slot_plen ? scalar_load_i32(p.slot_plen, seq) : 0;
+  int plen = p.slot_plen ? scalar_load_i32(p.slot_plen, seq) : 0;
+  // (One launch with fewer than 64 groups: the slot's group is the last one
+  // starting at or before it, found by the lanes among group_start.)
+  int gsv = 0x7fffffff;
+  if (p.num_groups > 0 && lane <= p.num_groups) gsv = p.group_start[lane];
   int32_t sid[kRing + 1];
 #pragma unroll
   for (int k = 0; k <= kRing; ++k) sid[k] = scalar_load_i32(bt, min(spage0 + k * kWaves, p.max_blocks - 1));
@@ -758,8 +757,13 @@ __global__ __launch_bounds__(kDecodeThreads, (Cols<G, M>::NT > 1 ? 1 : PA_DECODE
   // wave sum of the row offset waits until the first page is requested.)
 #pragma unroll
   for (int k = 0; k <= kRing; ++k) asm volatile("" : "+s"(sid[k]));
-  asm volatile("" : "+v"(qsum));
+  asm volatile("" : "+v"(qsum), "+v"(gsv));
   if (m <= 0) return;  // no row: nothing to write, no partial to count
+  if (p.num_groups > 0) {
+    const int gsi = __popcll(__builtin_amdgcn_ballot_w64(gsv <= seq)) - 1;
+    if (gsi >= 0 && gsi < p.num_groups && seq - __builtin_amdgcn_readlane(gsv, gsi) < p.max_members)
+      plen = max(scalar_load_i32(p.prefix_len, gsi), 0) & ~(kBlockSize - 1);
+  }
   const int npages = (n + kBlockSize - 1) / kBlockSize;
   const int npre = (plen > 0 && n > 0) ? p.pre_parts : 0;
   const int pstart = plen / kBlockSize + part * p.part_pages;
@@ -1102,6 +1106,19 @@ hipError_t launch_decode(const DecodeParams& p, int group, int format, int token
       case 4: fn = decode_entry<kFmtBF16, 4>(group); break;
       case 8: fn = decode_entry<kFmtBF16, 8>(group); break;
     }
+  }
+  if (!fn) return hipErrorInvalidValue;
+  DecodeParams arg = p;
+  void* args[] = {&arg};
+  return hipLaunchKernel(fn, dim3(grid), dim3(kDecodeThreads), args, 0, s);
+}
+
+hipError_t launch_decode_prefix(const DecodeParams& p, int group, unsigned grid, hipStream_t s) {
+  const void* fn = nullptr;
+  switch (group) {
+    case 1: fn = reinterpret_cast<const void*>(&decode_kernel<1, kFmtBF16, 1, true>); break;
+    case 2: fn = reinterpret_cast<const void*>(&decode_kernel<2, kFmtBF16, 1, true>); break;
+    case 4: fn = reinterpret_cast<const void*>(&decode_kernel<4, kFmtBF16, 1, true>); break;
   }
   if (!fn) return hipErrorInvalidValue;
   DecodeParams arg = p;

@@ -236,6 +236,51 @@ __device__ __forceinline__ void merge_batches(MergeState& s, const float* lse_a,
   }
 }
 
+// The same for eight adjacent dims of a row (four 8-byte device-coherent
+// loads per partial), in batches of 8 partials (40 loads in flight).
+struct MergeState8 {
+  float M = -INFINITY;
+  float W = 0.f;
+  float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+};
+
+__device__ __forceinline__ void merge_partials8(MergeState8& s, const float* lse_a, const float* out_a, int na,
+                                                const float* lse_b, const float* out_b, int nb, size_t rows) {
+  constexpr int kBatch = 8;
+  const int n = na + nb;
+  const size_t ostride = rows * 128 / 2;
+  for (int q0 = 0; q0 < n; q0 += kBatch) {
+    float lv[kBatch];
+    uint64_t ov[kBatch][4];
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const int q = min(q0 + i, n - 1);
+      const bool a = q < na;
+      const int k = a ? q : q - na;
+      const float* lp = (a ? lse_a : lse_b) + (size_t)k * rows;
+      const uint64_t* op = reinterpret_cast<const uint64_t*>(a ? out_a : out_b) + (size_t)k * ostride;
+      lv[i] = __hip_atomic_load(lp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) ov[i][j] = __hip_atomic_load(op + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const float l = lv[i];
+      if (q0 + i >= n || l == -INFINITY) continue;
+      const float M2 = fmaxf(s.M, l);
+      const float sc = fast_exp2((s.M - M2) * 1.4426950408889634f);  // 0 when M = -inf
+      const float w = fast_exp2((l - M2) * 1.4426950408889634f);
+      s.W = fmaf(s.W, sc, w);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        s.a[2 * j] = fmaf(s.a[2 * j], sc, w * __uint_as_float((uint32_t)ov[i][j]));
+        s.a[2 * j + 1] = fmaf(s.a[2 * j + 1], sc, w * __uint_as_float((uint32_t)(ov[i][j] >> 32)));
+      }
+      s.M = M2;
+    }
+  }
+}
+
 __device__ __forceinline__ void merge_partials(MergeState& s, const float* lse_a, const float* out_a, int na,
                                                const float* lse_b, const float* out_b, int nb, size_t rows) {
   const int n = na + nb;

@@ -68,10 +68,13 @@ struct DecodeParams {
   // partials of it have arrived.  0 pre_items: the prefix pass ran before.
   int32_t pre_items;
   int32_t pre_pages;          // pages per prefix partition
-  int32_t pre_chunks;         // member chunks (of M members) per group
+  int32_t pre_chunks;         // member chunks (of kDecodeWaves M members) per group
   int32_t max_members;        // members of a group that share its prefix
   const int32_t* group_start; // [num_groups + 1]: a group's slots are [group_start[i], group_start[i + 1])
   const int32_t* prefix_len;  // [num_groups]: shared tokens (read as whole pages)
+  // With slot_plen null, the slots' partitions look their group up among
+  // the num_groups (< 64) groups themselves; 0: no lookup.
+  int32_t num_groups;
 };
 
 // Chunk path (several new rows per slot): bf16 MFMA for S = QK^T and O = PV.
@@ -139,11 +142,18 @@ bool decode_supports_group(int group);
 // (1, 2, 4 or 8), or 0 when the decode path does not apply.
 int decode_tokens_per_slot(int group, int max_q_len);
 constexpr int kDecodeThreads = 64 * kDecodeWaves;
-// Members per prefix item in a one-launch prefix-grouped decode: as many as
-// fill the 16 columns of one score tile with their query heads (8 with one
-// head per KV head, where the tile takes each column twice, hi and lo).
+// Members per wave of a prefix item in a one-launch prefix-grouped decode:
+// as many as fill the 16 columns of one score tile with their query heads (8
+// with one head per KV head, where the tile takes each column twice, hi and
+// lo).  An item covers kDecodeWaves times as many.
 constexpr int prefix_chunk_members(int group) { return group == 1 ? 8 : 16 / group; }
 hipError_t launch_decode(const DecodeParams& p, int group, int format, int tokens, unsigned grid, hipStream_t s);
+// The one-launch prefix-grouped decode (bf16 pages, one token per slot):
+// pre_items prefix items, then the slots' partitions.  Built for 1, 2 and 4
+// query heads per KV head (with 8, the prefix items' LDS would leave one
+// workgroup per CU).
+constexpr bool decode_prefix_supports_group(int group) { return group == 1 || group == 2 || group == 4; }
+hipError_t launch_decode_prefix(const DecodeParams& p, int group, unsigned grid, hipStream_t s);
 hipError_t launch_zero_i32(int32_t* x, size_t n, hipStream_t s);
 
 constexpr int kChunkRows = 128;  // query rows per chunk workgroup

@@ -146,7 +146,7 @@ def test_every_decode_instance_publishes_before_counting_and_merges_coherently(d
             # every load that only runs after the counter (the merge: after
             # the barrier that publishes the counter's answer through LDS)
             # reads coherently
-            bar = [n for n in range(a + 1, min(a + 60, len(body))) if body[n].startswith("s_barrier")]
+            bar = [n for n in range(a + 1, min(a + 400, len(body))) if body[n].startswith("s_barrier")]
             assert bar, (name, "no barrier after the counter")
             loads = _dominated_loads(body, bar[0])
             assert loads, (name, "no merge loads after the counter")

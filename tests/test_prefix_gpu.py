@@ -58,6 +58,13 @@ CASES = [
     # 512 prefix pages need 32 partitions of 16 (eight tiles each): the
     # suffix merge folds its own partials and the prefix's in two batches.
     ("very_long_prefix", dict(groups=[(8192, [8192, 8200, 8500])], singles=[], hq=32, hkv=8)),
+    # 63 groups: the slots find their group themselves; 70: the set-up
+    # workgroup writes the slots' prefix lengths first.
+    ("63_groups", dict(groups=[(16, [20, 50 + i]) for i in range(63)], singles=[30], hq=32, hkv=8)),
+    ("70_groups", dict(groups=[(32, [40 + i, 90, 33]) for i in range(70)], singles=[20], hq=32, hkv=8)),
+    # 40 members at four query heads per KV head: three prefix items of 16,
+    # 16 and 8 members per (partition, KV head).
+    ("40_members", dict(groups=[(160, [161 + 3 * i for i in range(40)])], singles=[], hq=32, hkv=8)),
 ]
 
 
