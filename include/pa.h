@@ -216,10 +216,11 @@ pa_status pa_validate(const pa_shape* shape, const int32_t* block_table,
  * (section 8.3.2, Figs. 8-13 / 8-14: one copy of the common context serves
  * several requests).  pa_attend_prefix computes exactly what pa_attend
  * computes, but reads each group's shared pages once per KV head for all of
- * the group's query rows: a first pass attends the group's rows -- (member,
- * query head) pairs -- to the shared pages on the matrix cores; the decode
- * pass then attends each member to its own remaining keys and merges both
- * by log-sum-exp.
+ * the group's query rows -- (member, query head) pairs -- on the matrix
+ * cores, attends each member to its own remaining keys, and merges both by
+ * log-sum-exp.  Where the members' own keys are split (and 1, 2 or 4 query
+ * heads share a KV head) both parts run in one launch; otherwise a prefix
+ * pass runs first.
  *
  * Groups are runs of consecutive slots [group_start[k], group_start[k+1]).
  * Group k's prefix is its first L = prefix_len[k] keys, read as the
@@ -228,8 +229,8 @@ pa_status pa_validate(const pa_shape* shape, const int32_t* block_table,
  * group_start[k]'s first L/16 entries, and ctx_lens[r] >= L for members with
  * new tokens.  Slots outside every group, and slots past a group's first
  * max_members, have no prefix (their keys are all read by the decode pass;
- * the result is the same).  Decode only (max_q_len == 1, 1, 2 or 4 query
- * heads per KV head): other shapes return PA_ERR_UNSUPPORTED. */
+ * the result is the same).  Decode only (max_q_len == 1, 1, 2, 4 or 8
+ * query heads per KV head): other shapes return PA_ERR_UNSUPPORTED. */
 typedef struct pa_prefix_groups {
   int32_t num_groups;
   int32_t max_members;         /* prefix rows per group: a group's first max_members slots */

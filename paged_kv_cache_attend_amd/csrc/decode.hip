@@ -70,7 +70,10 @@
 //   once for all of them; each column has its own causal limit.
 // * Prefix-grouped decode (pa_attend_prefix): a grouped slot's partitions
 //   start after its group's shared prefix, and the merge also folds the
-//   prefix pass's partials of the slot's rows (written by the launch before).
+//   prefix partials of the slot's rows: written by the launch before, or,
+//   in the instance with prefix items, by the same launch's first
+//   workgroups, which read each shared page once for up to 4 x 16/G members
+//   (see prefix_item).
 
 #include "device.h"
 
