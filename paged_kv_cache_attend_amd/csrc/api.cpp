@@ -633,6 +633,9 @@ pa_status pa_attend_prefix(const pa_shape* shape, const pa_prefix_groups* groups
   d.slot_plen = pr.slot_plen;
   d.pre_out = pr.pre_out;
   d.pre_lse = pr.pre_lse;
+  // Where every grouped slot has the same prefix, the partitions request
+  // their first page ids for it before knowing their own.
+  d.guess_plen = groups->min_prefix_len == groups->max_prefix_len ? groups->max_prefix_len : 0;
 
   // One launch for the shared and the own keys where the slots' own keys are
   // split (their merge then counts the prefix partials too): prefix items of

@@ -448,40 +448,48 @@ __device__ __forceinline__ void prefix_item(const DecodeParams& p, int pi, int l
   const int g = rest % p.num_kv_heads;
   const int gi = rest / p.num_kv_heads;
 
-  // The group's bounds and prefix length; then, in one round trip, the
-  // members' lengths (lane j: member j of the item), the row offset of the
-  // group's slots before them and the page ids of this wave's first pages.
+  // One round trip before the first page request when the group's first
+  // slot is gi * max_members (full, consecutive groups): with the group's
+  // bounds and prefix length come, for that guess, the ids of the item's
+  // first 64 pages (one per lane, read with v_readlane: no memory wait, which
+  // the step barriers would otherwise take for every prefetched id; further
+  // pages, only where a prefix outruns the partitions, by scalar loads), the
+  // members' lengths (lane j: member j of the item) and the row offset of
+  // the slots before them.  A wrong guess costs one more round trip.
+  const int pstart = pp * p.pre_pages;
+  const int j0 = ci * kMembers;
+  auto load_lanes = [&](int s0_, int& pid_, int& mq_, int& mn_, int& qs_) {
+    const int32_t* bt_ = p.block_table + (size_t)s0_ * p.max_blocks;
+    pid_ = bt_[min(pstart + lane, p.max_blocks - 1)];
+    const int sl = min(s0_ + j0 + lane, p.num_seqs - 1);
+    mq_ = p.q_lens[sl];
+    mn_ = p.ctx_lens[sl];
+    qs_ = 0;
+    for (int i = lane; i < s0_ + j0; i += 64) qs_ += p.q_lens[i];
+  };
+  const int s0g = min(gi * p.max_members, max(p.num_seqs - 1, 0));
   int s0 = scalar_load_i32(p.group_start, gi);
   int s1 = scalar_load_i32(p.group_start, gi + 1);
   int plen = scalar_load_i32(p.prefix_len, gi);
-  asm volatile("" : "+s"(s0), "+s"(s1), "+s"(plen));
+  int pid, mq, mn, qsum;
+  load_lanes(s0g, pid, mq, mn, qsum);
+  asm volatile("" : "+s"(s0), "+s"(s1), "+s"(plen), "+v"(pid), "+v"(mq), "+v"(mn), "+v"(qsum));
   plen = max(plen, 0) & ~(kBlockSize - 1);  // whole pages, as the partitions read it
   const int members = min(s1 - s0, p.max_members);
-  const int j0 = ci * kMembers;
   if (plen <= 0 || j0 >= members) return;
+  if (s0 != s0g) load_lanes(s0, pid, mq, mn, qsum);
   const int jn = min(kMembers, members - j0);
   const int sf = s0 + j0;
   const int32_t* bt = p.block_table + (size_t)s0 * p.max_blocks;  // the group's shared pages
   // (the last partition runs to the group's prefix end, as in the prefix pass)
-  const int pstart = pp * p.pre_pages;
   const int pend = min(pp == p.pre_parts - 1 ? plen / kBlockSize : min(pstart + p.pre_pages, plen / kBlockSize),
                        p.max_blocks);
   const bool has_work = pstart < pend;
   const int last_page = pend - 1;
-  // The ids of the item's first 64 pages, one per lane, read from there
-  // (v_readlane: no memory wait, which the barriers would otherwise take
-  // for every prefetched id); further pages, only where a prefix outruns
-  // the partition sizes, by scalar loads.
-  const int pid = has_work ? bt[min(pstart + lane, last_page)] : 0;
   auto page_id = [&](int page) -> int32_t {
     page = min(page, last_page) - pstart;
     return page < 64 ? __builtin_amdgcn_readlane(pid, page) : scalar_load_i32(bt, page + pstart);
   };
-  const int jl = min(lane, jn - 1);
-  const int mq = p.q_lens[sf + jl];
-  const int mn = p.ctx_lens[sf + jl];
-  int qsum = 0;
-  for (int i = lane; i < sf; i += 64) qsum += p.q_lens[i];
   const uint64_t rowmask = __builtin_amdgcn_ballot_w64(lane < jn && mq > 0);
   if (rowmask == 0) return;  // no rows: nothing to write, nothing to count
 
@@ -597,7 +605,6 @@ __device__ __forceinline__ void prefix_item(const DecodeParams& p, int pi, int l
   auto row_of = [&](int c, int jc) -> size_t {
     return (size_t)(q_row + __popcll(rowmask & ((1ull << jc) - 1))) * p.num_q_heads + g * G + c % G;
   };
-  uint64_t* pre_out64 = reinterpret_cast<uint64_t*>(const_cast<float*>(p.pre_out));
   float* pre_lse = const_cast<float*>(p.pre_lse);
   // (All LDS reads first, then the stores under their conditions: the
   // rounds' reads overlap instead of waiting behind each branch.)
@@ -628,14 +635,9 @@ __device__ __forceinline__ void prefix_item(const DecodeParams& p, int pi, int l
     float lse = -INFINITY;
     if (pm[k] != -INFINITY) {
       const float inv = 1.f / prr[k];
-      const float o[8] = {pv0[k][0], pv0[k][1], pv0[k][2], pv0[k][3], pv1[k][0], pv1[k][1], pv1[k][2], pv1[k][3]};
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const uint64_t bits =
-            (uint64_t)__float_as_uint(o[2 * q] * inv) | ((uint64_t)__float_as_uint(o[2 * q + 1] * inv) << 32);
-        __hip_atomic_store(pre_out64 + (prow * kHeadDim + d8) / 2 + q, bits, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-      }
+      float* dst = const_cast<float*>(p.pre_out) + prow * kHeadDim + d8;
+      store_coherent_x4(dst, pv0[k] * inv);
+      store_coherent_x4(dst + 4, pv1[k] * inv);
       lse = (pm[k] + fast_log2(pl[k])) * kLn2;
     }
     if (d8 == 0) __hip_atomic_store(pre_lse + prow, lse, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -705,7 +707,8 @@ __global__ __launch_bounds__(kDecodeThreads, (Cols<G, M>::NT > 1 ? 1 : PA_DECODE
   // The kernel arguments the start needs, fetched together (the compiler
   // would otherwise fetch some of them one round trip later).
   asm volatile("" ::"s"(p.q_lens), "s"(p.ctx_lens), "s"(p.block_table), "s"(p.slot_plen), "s"(p.pre_parts), "s"(p.num_parts),
-               "s"(p.pre_items), "s"(p.num_groups), "s"(p.group_start), "s"(p.max_members),
+               "s"(p.pre_items), "s"(p.num_groups), "s"(p.group_start), "s"(p.max_members), "s"(p.guess_plen),
+               "s"(p.prefix_len),
                "s"(p.num_seqs), "s"(p.part_pages), "s"(p.max_blocks), "s"(gridDim.x));
 
   // One launch of prefix-grouped decode: the first pre_items workgroups are
@@ -735,11 +738,12 @@ __global__ __launch_bounds__(kDecodeThreads, (Cols<G, M>::NT > 1 ? 1 : PA_DECODE
   // Everything the start needs comes in one round trip, issued before the
   // first branch: the lengths, the prefix length, the slot's row offset (a
   // vector load and a wave sum) and the page ids of this wave's first pages
-  // as they are when the slot has no prefix (checked below, reloaded
-  // otherwise).  Lengths and page ids are wave-uniform scalar loads, which do
-  // not share the (in-order) vector load counter with the page stream.
+  // as they are when the slot's prefix is guess_plen keys (0 without
+  // prefix-grouped decode; checked below, reloaded otherwise).  Lengths and
+  // page ids are wave-uniform scalar loads, which do not share the (in-order)
+  // vector load counter with the page stream.
   const int32_t* bt = p.block_table + (size_t)seq * p.max_blocks;
-  const int spage0 = part * p.part_pages + wave;  // first page without a prefix
+  const int spage0 = p.guess_plen / kBlockSize + part * p.part_pages + wave;  // first page for that guess
   const int m = scalar_load_i32(p.q_lens, seq);
   const int n = scalar_load_i32(p.ctx_lens, seq);
   // Prefix-grouped decode: this slot's keys start after its shared prefix,
@@ -747,9 +751,11 @@ __global__ __launch_bounds__(kDecodeThreads, (Cols<G, M>::NT > 1 ? 1 : PA_DECODE
   // the slot's end whatever the prefix length.
   int plen = p.slot_plen ? scalar_load_i32(p.slot_plen, seq) : 0;
   // (One launch with fewer than 64 groups: the slot's group is the last one
-  // starting at or before it, found by the lanes among group_start.)
-  int gsv = 0x7fffffff;
+  // starting at or before it, found by the lanes among group_start, and its
+  // prefix length is that group's lane of prefix_len.)
+  int gsv = 0x7fffffff, plv = 0;
   if (p.num_groups > 0 && lane <= p.num_groups) gsv = p.group_start[lane];
+  if (p.num_groups > 0 && lane < p.num_groups) plv = p.prefix_len[lane];
   int32_t sid[kRing + 1];
 #pragma unroll
   for (int k = 0; k <= kRing; ++k) sid[k] = scalar_load_i32(bt, min(spage0 + k * kWaves, p.max_blocks - 1));
@@ -760,12 +766,12 @@ __global__ __launch_bounds__(kDecodeThreads, (Cols<G, M>::NT > 1 ? 1 : PA_DECODE
   // wave sum of the row offset waits until the first page is requested.)
 #pragma unroll
   for (int k = 0; k <= kRing; ++k) asm volatile("" : "+s"(sid[k]));
-  asm volatile("" : "+v"(qsum), "+v"(gsv));
+  asm volatile("" : "+v"(qsum), "+v"(gsv), "+v"(plv));
   if (m <= 0) return;  // no row: nothing to write, no partial to count
   if (p.num_groups > 0) {
     const int gsi = __popcll(__builtin_amdgcn_ballot_w64(gsv <= seq)) - 1;
     if (gsi >= 0 && gsi < p.num_groups && seq - __builtin_amdgcn_readlane(gsv, gsi) < p.max_members)
-      plen = max(scalar_load_i32(p.prefix_len, gsi), 0) & ~(kBlockSize - 1);
+      plen = max(__builtin_amdgcn_readlane(plv, gsi), 0) & ~(kBlockSize - 1);
   }
   const int npages = (n + kBlockSize - 1) / kBlockSize;
   const int npre = (plen > 0 && n > 0) ? p.pre_parts : 0;
@@ -779,7 +785,7 @@ __global__ __launch_bounds__(kDecodeThreads, (Cols<G, M>::NT > 1 ? 1 : PA_DECODE
   // the early load when it is that page.
   auto first_id = [&](int k) -> int32_t {
     const int page = pstart + wave + k * kWaves;
-    return (plen == 0 && page <= last_page) ? sid[k] : page_id(page);
+    return (plen == p.guess_plen && page <= last_page) ? sid[k] : page_id(page);
   };
 
   const int h0 = g * G;

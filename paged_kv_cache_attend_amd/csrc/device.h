@@ -137,6 +137,17 @@ __device__ __forceinline__ void issue_order_barrier() { asm volatile("" ::: "mem
 // unconstrained (expcnt 7, lgkmcnt 15 in the gfx9 encoding).
 __device__ __forceinline__ void wait_vm_stores() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// Device-coherent store of 16 bytes: written through to the point of
+// coherence that every XCD reads (the sc1 bit), as the relaxed agent-scope
+// atomic stores of up to 8 bytes are, in one instruction instead of two
+// (HIP has no 16-byte atomic store).  The compiler does not count this store
+// in its waits, so the caller waits for it with wait_vm_stores() before
+// announcing the data; the s_nop keeps the data registers from being
+// overwritten in the cycle after the store reads them.
+__device__ __forceinline__ void store_coherent_x4(float* dst, const f32x4_t& v) {
+  asm volatile("global_store_dwordx4 %0, %1, off sc1\n\ts_nop 1" ::"v"(dst), "v"(v) : "memory");
+}
+
 // Load of data read once per pass (cached K/V pages): a non-temporal load,
 // which does not keep the lines in the caches and streams measurably faster
 // from HBM than an ordinary load for scattered 4 KiB tiles.

@@ -75,6 +75,7 @@ struct DecodeParams {
   // With slot_plen null, the slots' partitions look their group up among
   // the num_groups (< 64) groups themselves; 0: no lookup.
   int32_t num_groups;
+  int32_t guess_plen;         // prefix length (whole pages) the first page-id requests assume
 };
 
 // Chunk path (several new rows per slot): bf16 MFMA for S = QK^T and O = PV.

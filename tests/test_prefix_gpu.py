@@ -89,6 +89,18 @@ def test_prefix_min_prefix_hint_and_repeats():
     compare(p, a, run_oracle(p), label="hint")
 
 
+def test_prefix_guessed_prefix_length_mismatch():
+    # With min_prefix_len == max_prefix_len the partitions request their
+    # first page ids for that prefix length before knowing their own; slots
+    # outside the group and a member past max_members have none and reload.
+    p, gs, pl = inputs.make_grouped_problem("pre_guess", 59, [(64, [70, 300, 65, 100])], [40, 90], 32, 8)
+    ref = run_oracle(p)
+    for ps in (0, 32):
+        say(f"attend_prefix guessed prefix length, partition_size={ps}")
+        got = run_prefix(p, gs, pl, partition_size=ps, min_prefix_len=64, max_members=3)
+        compare(p, got, ref, label=f"guess ps={ps}")
+
+
 def test_prefix_members_past_max_members_are_decoded_whole():
     # Slots past a group's first max_members get no prefix: the decode pass
     # attends them to all their keys, and the result is still exact.
