@@ -274,6 +274,7 @@ struct PrefixPlan {
   int row_tiles = 0;
   int pre_parts = 1;
   int pre_pages = 1;
+  int suffix_pages = 0;  // pages of the longest suffix (the slots' own keys)
   unsigned pre_grid = 0;
   size_t plen_offset = 0, pre_lse_offset = 0, pre_out_offset = 0, ws_bytes = 0;
 };
@@ -296,6 +297,7 @@ pa_status make_prefix_plan(const pa_shape* s, const pa_prefix_groups* gr, Prefix
   if (suf.max_ctx_len < kBlockSize) suf.max_ctx_len = kBlockSize;
   st = make_plan(&suf, &pp.suffix);
   if (st != PA_OK) return st;
+  pp.suffix_pages = ceil_div(suf.max_ctx_len, kBlockSize);
   const size_t rows = (size_t)s->total_q * s->num_q_heads;
   pp.row_tiles = ceil_div(gr->max_members * G, 64);
   const int max_pages = gr->max_prefix_len / kBlockSize;
@@ -638,22 +640,52 @@ pa_status pa_attend_prefix(const pa_shape* shape, const pa_prefix_groups* groups
   d.guess_plen = groups->min_prefix_len == groups->max_prefix_len ? groups->max_prefix_len : 0;
 
   // One launch for the shared and the own keys where the slots' own keys are
-  // split (their merge then counts the prefix partials too): prefix items of
-  // kDecodeWaves x prefix_chunk_members members each over the prefix pass's
-  // partitions (the prefix items go first, so they tend to be done first and
-  // the slots' partitions do the merging).  With fewer than 64 groups the
-  // partitions find their slot's group themselves; otherwise the set-up
-  // workgroup (the slots' prefix lengths) runs alone before.
+  // split (the workspace then has the counters, and the slots' merge counts
+  // the prefix partials too): prefix items of kDecodeWaves x
+  // prefix_chunk_members members each, placed first in the grid.  A prefix
+  // item that arrives last for its members has to merge all of their rows
+  // (up to 64) alone, so the plan keeps the prefix items ahead of the slots'
+  // partitions: where the whole grid fits one workgroup per CU, it takes the
+  // most slot partitions (up to the workspace's) for which prefix items of at
+  // most half as many pages still fit beside them (a prefix page costs an
+  // item about twice what a page costs a slot's partition: every wave scores
+  // it), and as many prefix partitions as the remaining CUs hold (up to the
+  // workspace's).  Otherwise the prefix pass's partitions and the slots' own
+  // plan.  With fewer than 64 groups the partitions find their slot's group
+  // themselves; otherwise the set-up workgroup (the slots' prefix lengths)
+  // runs alone before.
   const int G = pp.suffix.group;
   const int mc = prefix_chunk_members(G);
   if (PA_PREFIX_ONE_LAUNCH && pp.pre_grid > 0 && pp.suffix.decode && pp.suffix.num_parts > 1 &&
       decode_prefix_supports_group(G)) {
     const int max_pages = groups->max_prefix_len / kBlockSize;
-    const int pre_pages = PA_PREFIX_ITEM_PAGES > 0 ? PA_PREFIX_ITEM_PAGES : pp.pre_pages;
-    const int pre_parts = ceil_div(max_pages, pre_pages);
     const int chunks = ceil_div(groups->max_members, kDecodeWaves * mc);
-    const long long items = (long long)groups->num_groups * shape->num_kv_heads * pre_parts * chunks;
-    if (pre_parts <= pp.pre_parts && items > 0 && items + pp.suffix.grid <= INT_MAX) {
+    const long long units = (long long)groups->num_groups * shape->num_kv_heads * chunks;
+    const long long pairs = (long long)shape->num_seqs * shape->num_kv_heads;
+    const int suffix_pages = pp.suffix_pages;
+    int pre_pages = PA_PREFIX_ITEM_PAGES > 0 ? PA_PREFIX_ITEM_PAGES : pp.pre_pages;
+    int sparts = pp.suffix.num_parts;
+    if (PA_PREFIX_ITEM_PAGES == 0 && units > 0) {
+      const int s_lo = shape->partition_size > 0 ? sparts : 1;
+      for (int ps = sparts; ps >= s_lo; --ps) {
+        const long long left = (long long)kNumCUs - pairs * ps;
+        if (left < units) continue;
+        const long long fit = left / units;
+        const int parts = (int)(fit < pp.pre_parts ? fit : pp.pre_parts);
+        const int pages = ceil_div(max_pages, parts);
+        if (2 * pages <= ceil_div(suffix_pages, ps)) {
+          sparts = ps;
+          pre_pages = pages;
+          break;
+        }
+      }
+    }
+    const int pre_parts = ceil_div(max_pages, pre_pages);
+    const long long items = units * pre_parts;
+    const long long sgrid = pairs * sparts;
+    if (pre_parts <= pp.pre_parts && items > 0 && items + sgrid <= INT_MAX) {
+      d.num_parts = sparts;
+      d.part_pages = sparts == pp.suffix.num_parts ? pp.suffix.part_pages : ceil_div(suffix_pages, sparts);
       if (groups->num_groups < 64) {
         d.slot_plen = nullptr;
         d.num_groups = groups->num_groups;
@@ -667,7 +699,7 @@ pa_status pa_attend_prefix(const pa_shape* shape, const pa_prefix_groups* groups
       d.max_members = groups->max_members;
       d.group_start = groups->group_start;
       d.prefix_len = groups->prefix_len;
-      if (launch_decode_prefix(d, G, (unsigned)(items + pp.suffix.grid), s) != hipSuccess)
+      if (launch_decode_prefix(d, G, (unsigned)(items + sgrid), s) != hipSuccess)
         return PA_ERR_LAUNCH;
       return PA_OK;
     }
