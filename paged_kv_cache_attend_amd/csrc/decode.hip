@@ -410,6 +410,12 @@ __device__ __forceinline__ void consume_page(WaveState<Cols<G, M>::NT>& st, Page
   score_page<G, F, M>(st, sk, sv, sks, svs, valid, scale_log2, lane, kbase, lim);
 }
 
+// Partitions of `parts` (of part_pages pages, the last running to the end)
+// that hold any of a slot's `pages` own pages.
+__device__ __forceinline__ int partitions_with_keys(int pages, int parts, int part_pages) {
+  return min(parts, (max(pages, 0) + part_pages - 1) / part_pages);
+}
+
 // One prefix item of a prefix-grouped decode done in one launch (pre_items
 // > 0): pages [pp pre_pages, ...) of one group's shared prefix for one KV
 // head, read once for up to kWaves M of the group's members.  The waves take
@@ -642,6 +648,10 @@ __device__ __forceinline__ void prefix_item(const DecodeParams& p, int pi, int l
     }
     if (d8 == 0) __hip_atomic_store(pre_lse + prow, lse, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
+  // Lane j: member j's own partitions that hold keys, counted and merged
+  // besides the prefix partitions (as the member's partitions count them).
+  const int mps = partitions_with_keys((mn + kBlockSize - 1) / kBlockSize - plen / kBlockSize, p.num_parts,
+                                       p.part_pages);
   wait_vm_stores();
   __syncthreads();
   if ((int)threadIdx.x < jn) {  // wave 0, lane = member
@@ -649,7 +659,7 @@ __device__ __forceinline__ void prefix_item(const DecodeParams& p, int pi, int l
     if (((rowmask >> lane) & 1) && mn > 0) {
       int32_t* counter = p.counters + (size_t)(sf + lane) * p.num_kv_heads + g;
       last = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-             p.num_parts + p.pre_parts - 1;
+             mps + p.pre_parts - 1;
     }
     s_lastm[lane] = last;
   }
@@ -659,10 +669,11 @@ __device__ __forceinline__ void prefix_item(const DecodeParams& p, int pi, int l
     const int wc = t >> 4, d8 = (t & 15) * 8;
     const int c = wc % C, jc = (wc / C) * M + c / G;
     const int njc = __shfl(mn, jc & 63, 64);
+    const int pjc = __shfl(mps, jc & 63, 64);
     if (!(jc < jn && ((rowmask >> jc) & 1) && njc > 0 && s_lastm[jc])) continue;
     const size_t row = row_of(c, jc);
     MergeState8 ms;
-    merge_partials8(ms, p.part_lse + row, p.part_out + row * kHeadDim + d8, p.num_parts, p.pre_lse + row,
+    merge_partials8(ms, p.part_lse + row, p.part_out + row * kHeadDim + d8, pjc, p.pre_lse + row,
                     p.pre_out + row * kHeadDim + d8, p.pre_parts, rows);
     if (ms.M != -INFINITY) {
       const float inv = 1.f / ms.W;
@@ -775,6 +786,15 @@ __global__ __launch_bounds__(kDecodeThreads, (Cols<G, M>::NT > 1 ? 1 : PA_DECODE
   }
   const int npages = (n + kBlockSize - 1) / kBlockSize;
   const int npre = (plen > 0 && n > 0) ? p.pre_parts : 0;
+  // The slot's partitions that hold keys (the last runs to the slot's end):
+  // the others have nothing to add and neither publish nor count, so a short
+  // slot of a batch split for its longest costs one round trip per empty
+  // partition, and a slot with one such partition writes its result itself.
+  // (A prefix pass's partials from the launch before still need a merger:
+  // partition 0, even without keys of its own.)
+  const int ps = partitions_with_keys(npages - plen / kBlockSize, P, p.part_pages);
+  const int Ps = (npre > 0 && p.pre_items == 0) ? max(ps, 1) : ps;
+  if (part >= Ps) return;
   const int pstart = plen / kBlockSize + part * p.part_pages;
   const int pend = part == P - 1 ? npages : min(npages, pstart + p.part_pages);
   const bool has_work = n > 0 && pstart < pend;
@@ -984,7 +1004,7 @@ __global__ __launch_bounds__(kDecodeThreads, (Cols<G, M>::NT > 1 ? 1 : PA_DECODE
     return (size_t)(q_row + my_c[j] / G) * p.num_q_heads + h0 + my_c[j] % G;
   };
 
-  if (P == 1 && p.pre_items == 0) {
+  if (Ps == 1 && (p.pre_items == 0 || npre == 0)) {
 #pragma unroll
     for (int j = 0; j < J; ++j) {
       if (!my_out[j]) continue;
@@ -1045,11 +1065,11 @@ __global__ __launch_bounds__(kDecodeThreads, (Cols<G, M>::NT > 1 ? 1 : PA_DECODE
   int32_t* counter = p.counters + (size_t)seq * p.num_kv_heads + g;
   if (threadIdx.x == 0)
     s_last = (__hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-              P - 1 + (p.pre_items > 0 ? npre : 0));
+              Ps - 1 + (p.pre_items > 0 ? npre : 0));
   __syncthreads();
   if (!s_last) return;
 
-  // Merge by log-sum-exp weights: this slot's P partials and, with a shared
+  // Merge by log-sum-exp weights: this slot's Ps partials and, with a shared
   // prefix, the prefix pass's npre, their loads issued in batches before any
   // is used; a partial with LSE = -inf (empty) gets weight 0 without its
   // output being read.
@@ -1059,7 +1079,7 @@ __global__ __launch_bounds__(kDecodeThreads, (Cols<G, M>::NT > 1 ? 1 : PA_DECODE
     const size_t row = row_of(j);
     const int d = my_d[j];
     MergeState ms;
-    merge_partials(ms, p.part_lse + row, p.part_out + row * kHeadDim + d, P, p.pre_lse + row,
+    merge_partials(ms, p.part_lse + row, p.part_out + row * kHeadDim + d, Ps, p.pre_lse + row,
                    p.pre_out + row * kHeadDim + d, npre, rows);
     if (ms.M != -INFINITY) {
       const float inv = 1.f / ms.W;
