@@ -718,9 +718,9 @@ __global__ __launch_bounds__(kDecodeThreads, (Cols<G, M>::NT > 1 ? 1 : PA_DECODE
   // The kernel arguments the start needs, fetched together (the compiler
   // would otherwise fetch some of them one round trip later).
   asm volatile("" ::"s"(p.q_lens), "s"(p.ctx_lens), "s"(p.block_table), "s"(p.slot_plen), "s"(p.pre_parts), "s"(p.num_parts),
-               "s"(p.pre_items), "s"(p.num_groups), "s"(p.group_start), "s"(p.max_members), "s"(p.guess_plen),
-               "s"(p.prefix_len),
-               "s"(p.num_seqs), "s"(p.part_pages), "s"(p.max_blocks), "s"(gridDim.x));
+               "s"(p.pre_items), "s"(p.num_seqs), "s"(p.part_pages), "s"(p.max_blocks), "s"(gridDim.x));
+  if constexpr (kPre)
+    asm volatile("" ::"s"(p.num_groups), "s"(p.group_start), "s"(p.max_members), "s"(p.guess_plen), "s"(p.prefix_len));
 
   // One launch of prefix-grouped decode: the first pre_items workgroups are
   // prefix items (dispatched first); the rest are the slots' partitions.
@@ -749,12 +749,13 @@ __global__ __launch_bounds__(kDecodeThreads, (Cols<G, M>::NT > 1 ? 1 : PA_DECODE
   // Everything the start needs comes in one round trip, issued before the
   // first branch: the lengths, the prefix length, the slot's row offset (a
   // vector load and a wave sum) and the page ids of this wave's first pages
-  // as they are when the slot's prefix is guess_plen keys (0 without
-  // prefix-grouped decode; checked below, reloaded otherwise).  Lengths and
-  // page ids are wave-uniform scalar loads, which do not share the (in-order)
-  // vector load counter with the page stream.
+  // as they are when the slot has no prefix (with prefix items: when its
+  // prefix is guess_plen keys; checked below, reloaded otherwise).  Lengths
+  // and page ids are wave-uniform scalar loads, which do not share the
+  // (in-order) vector load counter with the page stream.
   const int32_t* bt = p.block_table + (size_t)seq * p.max_blocks;
-  const int spage0 = p.guess_plen / kBlockSize + part * p.part_pages + wave;  // first page for that guess
+  const int guess = kPre ? p.guess_plen : 0;
+  const int spage0 = guess / kBlockSize + part * p.part_pages + wave;  // first page for that guess
   const int m = scalar_load_i32(p.q_lens, seq);
   const int n = scalar_load_i32(p.ctx_lens, seq);
   // Prefix-grouped decode: this slot's keys start after its shared prefix,
@@ -765,8 +766,10 @@ __global__ __launch_bounds__(kDecodeThreads, (Cols<G, M>::NT > 1 ? 1 : PA_DECODE
   // starting at or before it, found by the lanes among group_start, and its
   // prefix length is that group's lane of prefix_len.)
   int gsv = 0x7fffffff, plv = 0;
-  if (p.num_groups > 0 && lane <= p.num_groups) gsv = p.group_start[lane];
-  if (p.num_groups > 0 && lane < p.num_groups) plv = p.prefix_len[lane];
+  if constexpr (kPre) {
+    if (p.num_groups > 0 && lane <= p.num_groups) gsv = p.group_start[lane];
+    if (p.num_groups > 0 && lane < p.num_groups) plv = p.prefix_len[lane];
+  }
   int32_t sid[kRing + 1];
 #pragma unroll
   for (int k = 0; k <= kRing; ++k) sid[k] = scalar_load_i32(bt, min(spage0 + k * kWaves, p.max_blocks - 1));
@@ -777,9 +780,10 @@ __global__ __launch_bounds__(kDecodeThreads, (Cols<G, M>::NT > 1 ? 1 : PA_DECODE
   // wave sum of the row offset waits until the first page is requested.)
 #pragma unroll
   for (int k = 0; k <= kRing; ++k) asm volatile("" : "+s"(sid[k]));
-  asm volatile("" : "+v"(qsum), "+v"(gsv), "+v"(plv));
+  asm volatile("" : "+v"(qsum));
+  if constexpr (kPre) asm volatile("" : "+v"(gsv), "+v"(plv));
   if (m <= 0) return;  // no row: nothing to write, no partial to count
-  if (p.num_groups > 0) {
+  if (kPre && p.num_groups > 0) {
     const int gsi = __popcll(__builtin_amdgcn_ballot_w64(gsv <= seq)) - 1;
     if (gsi >= 0 && gsi < p.num_groups && seq - __builtin_amdgcn_readlane(gsv, gsi) < p.max_members)
       plen = max(__builtin_amdgcn_readlane(plv, gsi), 0) & ~(kBlockSize - 1);
@@ -805,7 +809,7 @@ __global__ __launch_bounds__(kDecodeThreads, (Cols<G, M>::NT > 1 ? 1 : PA_DECODE
   // the early load when it is that page.
   auto first_id = [&](int k) -> int32_t {
     const int page = pstart + wave + k * kWaves;
-    return (plen == p.guess_plen && page <= last_page) ? sid[k] : page_id(page);
+    return (plen == guess && page <= last_page) ? sid[k] : page_id(page);
   };
 
   const int h0 = g * G;
