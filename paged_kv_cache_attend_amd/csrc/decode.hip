@@ -1083,7 +1083,7 @@ __global__ __launch_bounds__(kDecodeThreads, (Cols<G, M>::NT > 1 ? 1 : PA_DECODE
     const size_t row = row_of(j);
     const int d = my_d[j];
     MergeState ms;
-    merge_partials(ms, p.part_lse + row, p.part_out + row * kHeadDim + d, Ps, p.pre_lse + row,
+    merge_partials<J == 1>(ms, p.part_lse + row, p.part_out + row * kHeadDim + d, Ps, p.pre_lse + row,
                    p.pre_out + row * kHeadDim + d, npre, rows);
     if (ms.M != -INFINITY) {
       const float inv = 1.f / ms.W;

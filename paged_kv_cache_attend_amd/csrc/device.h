@@ -221,7 +221,7 @@ __device__ __forceinline__ void merge_fold(MergeState& s, float l, float o0, flo
 // at lse_a[i * rows] and its two dims at out_a[i * rows * 128 + 0, 1]
 // (likewise B).  Device-coherent relaxed loads (partials of this launch may
 // come from workgroups on any XCD), in batches whose loads are all issued
-// before any is used: 2, 4, 8 or 16 partials for short merges, else 28 (56 loads
+// before any is used: 2, 4, 8 (or 16) partials for short merges, else 28 (56 loads
 // in flight, within the 6-bit load counter).
 template <int kBatch>
 __device__ __forceinline__ void merge_batches(MergeState& s, const float* lse_a, const float* out_a, int na,
@@ -292,6 +292,10 @@ __device__ __forceinline__ void merge_partials8(MergeState8& s, const float* lse
   }
 }
 
+// kBatch16: also a batch of 16 for 9 - 16 partials (callers that merge one
+// (row, dim pair) per thread; with several unrolled per thread the extra
+// variant costs more scalar registers than it saves).
+template <bool kBatch16 = false>
 __device__ __forceinline__ void merge_partials(MergeState& s, const float* lse_a, const float* out_a, int na,
                                                const float* lse_b, const float* out_b, int nb, size_t rows) {
   const int n = na + nb;
@@ -302,7 +306,7 @@ __device__ __forceinline__ void merge_partials(MergeState& s, const float* lse_a
     merge_batches<4>(s, lse_a, out_a, na, lse_b, out_b, n, rows);
   else if (n <= 8)
     merge_batches<8>(s, lse_a, out_a, na, lse_b, out_b, n, rows);
-  else if (n <= 16)
+  else if (kBatch16 && n <= 16)
     merge_batches<16>(s, lse_a, out_a, na, lse_b, out_b, n, rows);
   else
     merge_batches<28>(s, lse_a, out_a, na, lse_b, out_b, n, rows);
