@@ -15,8 +15,8 @@ from paged_kv_cache_attend_amd import inputs
 DEV = torch.device("cuda:0")
 
 # Tolerances on the output and the LSE (natural log), from the accuracy
-# budget of bf16 storage with fp32 accumulation: the benchmark spec-style absolute
-# bounds, max |dout| <= 1e-2, mean |dout| <= 1e-3, max |dlse| <= 1e-3.  Below
+# budget of bf16 storage with fp32 accumulation: absolute bounds max |dout|
+# <= 1e-2, mean |dout| <= 1e-3, max |dlse| <= 1e-3.  Below
 # |o| = 4 half a bf16 ulp of the output is at most 2^-8 ~ 0.0039 and the max
 # bound is the absolute 1e-2.  From |o| = 4 on, half an ulp alone is 2^-6 =
 # 0.0156 or more, above 1e-2 before any arithmetic, so there the bound is that
