@@ -43,7 +43,10 @@
 //      complete under it.  The output is divided by the sum of those rounded
 //      weights, so it is an exact weighted mean of the V rows under the
 //      weights PV used (a single dominant key comes back exactly); the LSE
-//      takes the sum of the fp32 weights.
+//      takes the sum of the fp32 weights.  Where some row of a key half sees
+//      fewer than kFewKeys of its keys -- too few to average the rounding
+//      down -- the rounding's remainders go through a product of their own
+//      as well, and the divisor is the fp32 sum.
 // Keys past the end load the last key (finite) and get -inf scores.  The
 // 128 x 128 bf16 output tile is staged in LDS and stored as whole rows.
 
@@ -61,6 +64,11 @@ constexpr int kRowBytes = kHeadDim * 2;           // 256: one key row of K or V
 constexpr int kTileBytes = kTileKeys * kRowBytes; // 8 KiB (K or V)
 constexpr int kStages = 4;                        // LDS stages per key half
 constexpr float kRescaleSlack = 8.0f;             // log2 units
+// A half whose rows see few keys cannot average the rounding of bf16
+// weights down: where some live row sees between 1 and kFewKeys - 1 of the
+// half's keys, the remainders of the weights' rounding go through a second
+// PV product (twice the PV products, on the few tiles such a half has).
+constexpr int kFewKeys = 64;
 constexpr int kMergeBytes = 72 * 1024;            // merge buffer at the start of the tile area
 
 static_assert(kChunkRows == 4 * 32, "four row groups of 32 rows");
@@ -182,6 +190,16 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkParams p) {
   const int ntiles = (kv_end + kTileKeys - 1) / kTileKeys;
   const int T = (ntiles + 1) / 2;       // tiles per half (both halves loop T times)
   const int my_limit = p.causal ? (n - m + tok) : (n - 1);  // last visible key of this row
+  bool fine;  // this half's rows: some sees 1 .. kFewKeys - 1 of its keys
+  {
+    const int t_first = (qt * kChunkRows) / G;
+    const int t_last = (min(m * G, (qt + 1) * kChunkRows) - 1) / G;
+    const int base = tile0 * kTileKeys;
+    // a row that sees v keys has min(max(v - base, 0), T * 32) of them here
+    const int v_lo = p.causal ? n - m + t_first + 1 : n;
+    const int v_hi = p.causal ? n - m + t_last + 1 : n;
+    fine = v_hi > base && min(max(v_lo - base, 1), T * kTileKeys) < kFewKeys;
+  }
   // Tiles ending at or before this key count are visible to every row of the
   // workgroup (under the causal mask: to the tile's first token).
   const int open_end = p.causal ? min(kv_end, n - m + (qt * kChunkRows) / G + 1) : kv_end;
@@ -366,13 +384,31 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkParams p) {
         rsum = bf16x2_sum_into(pf[ks][w], rsum);
       }
     }
-    r_run += rsum;
+    // (few keys: the remainders go through a product of their own below, so
+    // the fp32 weights are what PV sums, and their sum is the divisor)
+    r_run += fine ? lsum : rsum;
     // The transposed reads must have landed (the operands pass through this
     // block, so nothing reads them before it).
     asm volatile("s_waitcnt lgkmcnt(0)"
                  : "+v"(vr[0]), "+v"(vr[1]), "+v"(vr[2]), "+v"(vr[3]), "+v"(vr[4]), "+v"(vr[5]), "+v"(vr[6]),
                    "+v"(vr[7]), "+v"(vr[8]), "+v"(vr[9]), "+v"(vr[10]), "+v"(vr[11]), "+v"(vr[12]),
                    "+v"(vr[13]), "+v"(vr[14]), "+v"(vr[15]));
+    if (fine) {  // the rounding's remainders first, then the rounded weights
+      u32x4_t pl[2];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) pl[ks][w] = lo_after(st[8 * ks + 2 * w], st[8 * ks + 2 * w + 1], pf[ks][w]);
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const u32x2_t l2 = vr[4 * mb + 2 * ks];
+          const u32x2_t h2 = vr[4 * mb + 2 * ks + 1];
+          const u32x4_t vf = u32x4_t{l2[0], l2[1], h2[0], h2[1]};
+          o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vf), as_bf16x8(pl[ks]), o[mb], 0, 0, 0);
+        }
+    }
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
 #pragma unroll

@@ -54,7 +54,11 @@
 //   and they feed PV the remainder lo = w - hi(w) while lanes of columns < G
 //   feed hi(w), w cut to bf16.  hi + lo is w to 2^-15 of w, and the two
 //   output columns of a head are added once at the end: no extra matrix
-//   product.  Rows past a slot's end are zeroed in the V tile
+//   product.  Where the columns leave no room for the lo copies (several
+//   tokens per slot), the weights go in rounded to bf16 and the output is
+//   divided by the sum of the rounded weights; a partition in which some
+//   row sees fewer than kFewKeys keys also feeds the rounding's remainders
+//   through a product of their own.  Rows past a slot's end are zeroed in the V tile
 //   and get weight 0 by select, since their stored codes and scales may be
 //   anything.
 // * Epilogue: the four waves' (max, sum, acc) merge through LDS.  With one
@@ -88,6 +92,12 @@ constexpr int kWaves = kDecodeWaves;
 constexpr int kRing = PA_DECODE_RING;                  // pages per wave in the register ring
 constexpr int kTileBytes = kBlockSize * kHeadDim * 2;  // 4 KiB
 constexpr float kRescaleSlack = 8.0f;                  // log2 units
+// Where a weight enters PV as one bf16 number (no room for the lo copies),
+// a partial whose rows see few keys cannot average the rounding of its
+// weights down: with fewer than this many keys for some row, the wave also
+// feeds the rounding's remainders through a second product (the cost is
+// twice the PV products on the few pages such a partial has).
+constexpr int kFewKeys = 64;
 
 // One page of one KV head as loaded: per lane, the codes of chunks
 // c = lane + 64 k (k < 4) -- token c / 16, dims 8 (c % 16) .. +8 -- of the K
@@ -210,17 +220,6 @@ __device__ __forceinline__ s16x4_t as_s16x4(uint32_t lo, uint32_t hi) {
   return __builtin_bit_cast(s16x4_t, u32x2_t{lo, hi});
 }
 
-// Two fp32 weights as a bf16 pair.  In the lanes of columns < G: hi(w), w
-// truncated to bf16 (its top 16 bits); in the lanes of the duplicate columns:
-// w - hi(w) (exact in fp32), truncated likewise.  hi + lo is w to within 2^-15
-// of w, and both halves come from one byte permute per pair.
-__device__ __forceinline__ uint32_t hi_or_lo(float w0, float w1, uint32_t lo_mask) {
-  const float x0 = w0 - __uint_as_float(__float_as_uint(w0) & lo_mask);
-  const float x1 = w1 - __uint_as_float(__float_as_uint(w1) & lo_mask);
-  // bytes 2, 3 of x0 and 2, 3 of x1 -> (lo half, hi half) of the result
-  return __builtin_amdgcn_perm(__float_as_uint(x1), __float_as_uint(x0), 0x07060302u);
-}
-
 // Columns of the score tile.  A slot's (token, query head) pairs of one KV
 // head, token major -- column c is token c / G of query head g G + c % G --
 // for up to M tokens per slot: C = G M real columns.  When two copies fit in
@@ -275,7 +274,7 @@ __device__ __forceinline__ void stage_page(const Page<F>& b, uint8_t* sk, uint8_
 template <int G, int F, int M>
 __device__ __forceinline__ void score_page(WaveState<Cols<G, M>::NT>& st, const uint8_t* sk, const uint8_t* sv,
                                            const float* sks, const float* svs, int valid, float scale_log2, int lane,
-                                           int kbase, const int* lim) {
+                                           int kbase, const int* lim, bool fine = false) {
   using CS = Cols<G, M>;
   constexpr int NT = CS::NT;
   const int pr = lane >> 4;
@@ -390,8 +389,18 @@ __device__ __forceinline__ void score_page(WaveState<Cols<G, M>::NT>& st, const 
       } else {
         const uint32_t w01 = pack_bf16x2(pw[0], pw[1]);
         const uint32_t w23 = pack_bf16x2(pw[2], pw[3]);
-        st.r_lane[ct] += (bf16_lo(w01) + bf16_hi(w01)) + (bf16_lo(w23) + bf16_hi(w23));
+        // (few keys, see kFewKeys: the rounding's remainders go through a
+        // product of their own below, so the fp32 sum is the divisor)
+        st.r_lane[ct] += fine ? (pw[0] + pw[1]) + (pw[2] + pw[3])
+                              : (bf16_lo(w01) + bf16_hi(w01)) + (bf16_lo(w23) + bf16_hi(w23));
         pg = as_s16x4(w01, w23);
+      }
+      if (!CS::HL && fine) {  // the rounding's remainders first, then the rounded weights
+        const uint32_t hi01 = __builtin_bit_cast(u32x2_t, pg)[0], hi23 = __builtin_bit_cast(u32x2_t, pg)[1];
+        const s16x4_t pl = as_s16x4(lo_after(pw[0], pw[1], hi01), lo_after(pw[2], pw[3], hi23));
+#pragma unroll
+        for (int bb = 0; bb < 8; ++bb)
+          st.o[ct][bb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt[bb], pl, st.o[ct][bb], 0, 0, 0);
       }
 #pragma unroll
       for (int bb = 0; bb < 8; ++bb)
@@ -404,10 +413,10 @@ __device__ __forceinline__ void score_page(WaveState<Cols<G, M>::NT>& st, const 
 template <int G, int F, int M>
 __device__ __forceinline__ void consume_page(WaveState<Cols<G, M>::NT>& st, Page<F>& b, uint8_t* sk, uint8_t* sv,
                                              float* sks, float* svs, int valid, float scale_log2, int lane,
-                                             int kbase, const int* lim) {
+                                             int kbase, const int* lim, bool fine) {
   stage_page<F>(b, sk, sv, sks, svs, valid, lane);
   wave_lds_sync();
-  score_page<G, F, M>(st, sk, sv, sks, svs, valid, scale_log2, lane, kbase, lim);
+  score_page<G, F, M>(st, sk, sv, sks, svs, valid, scale_log2, lane, kbase, lim, fine);
 }
 
 // Partitions of `parts` (of part_pages pages, the last running to the end)
@@ -491,6 +500,7 @@ __device__ __forceinline__ void prefix_item(const DecodeParams& p, int pi, int l
   const int pend = min(pp == p.pre_parts - 1 ? plen / kBlockSize : min(pstart + p.pre_pages, plen / kBlockSize),
                        p.max_blocks);
   const bool has_work = pstart < pend;
+  const bool fine = !CS::HL && (pend - pstart) * kBlockSize < kFewKeys;
   const int last_page = pend - 1;
   auto page_id = [&](int page) -> int32_t {
     page = min(page, last_page) - pstart;
@@ -551,7 +561,7 @@ __device__ __forceinline__ void prefix_item(const DecodeParams& p, int pi, int l
         const int page = pstart + k * kWaves + w;
         if (full || page < pend)
           score_page<G, F, M>(st, tk[w], tv[w], nullptr, nullptr, kBlockSize, p.scale_log2, lane, page * kBlockSize,
-                              lim);
+                              lim, fine);
       }
     }
     if (!kTwoStages) __syncthreads();
@@ -802,6 +812,15 @@ __global__ __launch_bounds__(kDecodeThreads, (Cols<G, M>::NT > 1 ? 1 : PA_DECODE
   const int pstart = plen / kBlockSize + part * p.part_pages;
   const int pend = part == P - 1 ? npages : min(npages, pstart + p.part_pages);
   const bool has_work = n > 0 && pstart < pend;
+  // Few keys: some live row sees between 1 and kFewKeys - 1 of this
+  // partition's keys (token t of m sees keys up to n - m + t when causal; a
+  // row that sees v keys has min(max(v - start, 0), the partition's keys) of
+  // them here).
+  bool fine = false;
+  if constexpr (!CS::HL) {
+    const int base = pstart * kBlockSize;
+    fine = n > base && min(max((p.causal ? n - m + 1 : n) - base, 1), min(n, pend * kBlockSize) - base) < kFewKeys;
+  }
 
   const int last_page = pend - 1;
   auto page_id = [&](int page) -> int32_t { return scalar_load_i32(bt, min(page, last_page)); };
@@ -903,7 +922,7 @@ __global__ __launch_bounds__(kDecodeThreads, (Cols<G, M>::NT > 1 ? 1 : PA_DECODE
     auto valid_of = [&](int k) { return min(kBlockSize, n - (page0 + kWaves * k) * kBlockSize); };
 #define PA_CONSUME(RING, K)                                                                            \
   consume_page<G, F, M>(st, RING, sk, sv, sks, svs, valid_of(K), p.scale_log2, lane,                   \
-                        (page0 + kWaves * (K)) * kBlockSize, lim)
+                        (page0 + kWaves * (K)) * kBlockSize, lim, fine)
 #define PA_REISSUE(RING, K)                                          \
   {                                                                  \
     issue_page<F>(RING, p, next_id, g, lane);                        \

@@ -60,6 +60,27 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// The remainders w - hi of two fp32 weights after their bf16 pair hi (as
+// pack_bf16x2 rounds them), truncated to bf16: exact in fp32 before the
+// truncation, so hi + lo is w to within 2^-16 of w.
+__device__ __forceinline__ uint32_t lo_after(float w0, float w1, uint32_t hi) {
+  const float x0 = w0 - bf16_lo(hi);
+  const float x1 = w1 - bf16_hi(hi);
+  return __builtin_amdgcn_perm(__float_as_uint(x1), __float_as_uint(x0), 0x07060302u);
+}
+
+// Two fp32 weights as a bf16 pair, split for a weight fed to a matrix
+// product as hi + lo: with lo_mask 0, hi(w), w truncated to bf16 (its top 16
+// bits); with lo_mask 0xffff0000, w - hi(w) (exact in fp32), truncated
+// likewise.  hi + lo is w to within 2^-15 of w, and either half comes from
+// one byte permute per pair.
+__device__ __forceinline__ uint32_t hi_or_lo(float w0, float w1, uint32_t lo_mask) {
+  const float x0 = w0 - __uint_as_float(__float_as_uint(w0) & lo_mask);
+  const float x1 = w1 - __uint_as_float(__float_as_uint(w1) & lo_mask);
+  // bytes 2, 3 of x0 and 2, 3 of x1 -> (lo half, hi half) of the result
+  return __builtin_amdgcn_perm(__float_as_uint(x1), __float_as_uint(x0), 0x07060302u);
+}
+
 // The swizzle of the 32-key K and V tiles that the chunk and prefix kernels
 // stage in LDS (256-byte rows of 16 chunks): the 16-byte chunk c of key row
 // `key` sits at chunk position c ^ key_swz(key), where key_swz permutes the

@@ -18,8 +18,8 @@ import oracle
 import paged_kv_cache_attend_amd as pk
 from paged_kv_cache_attend_amd import inputs
 
-from gpu_util import (DEV, LSE_SENTINEL, OUT_SENTINEL, TOL_MEAN, bf16_to_f64, compare, out_bound, run_gpu,
-                      run_oracle, say)
+from gpu_util import (DEV, LSE_SENTINEL, OUT_SENTINEL, TOL_MEAN, bf16_to_f64, compare, half_ulp_bf16, out_bound,
+                      run_gpu, run_oracle, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -293,6 +293,43 @@ def test_chunk_path_many_slots(num_seqs):
     p = _case(ctx.tolist(), ql.tolist(), hq=4, hkv=2, seed=num_seqs, causal=True)
     say(f"chunk many slots: {num_seqs}")
     compare(p, run_gpu(p), run_oracle(p), label=f"chunk {num_seqs} slots")
+
+
+# Rows that see few keys: on the paths that feed PV single bf16 weights (the
+# chunk kernel, decode with several tokens per slot where the score tile has
+# no room for the lo copies), such rows cannot average the weights' rounding
+# down, so there the weights go in as hi + lo halves.  Their outputs then
+# carry the output rounding and fp32-level error only: half a bf16 ulp plus
+# 2.5e-4, where single bf16 weights leave up to ~4e-3 on top of the half ulp
+# (a CPU emulation of both on 2 - 40 keys: 3.3e-3 - 4.3e-3 against 1.5e-5).
+FEW_KEY_CASES = [
+    # decode, 8 tokens x 4 heads = 32 columns (two score tiles)
+    ("decode_m8", dict(ctx=list(range(2, 42)), ql=[min(n, 1 + n % 8) for n in range(2, 42)], hq=32, hkv=8)),
+    # decode, 2 tokens x 8 heads = 16 columns
+    ("decode_g8_m2", dict(ctx=list(range(2, 40)), ql=[1 + n % 2 for n in range(2, 40)], hq=64, hkv=8)),
+    # chunk path: a first prefill chunk (row t sees t + 1 keys), causal
+    ("chunk_first_chunk", dict(ctx=[200, 130, 64], ql=[200, 130, 64], hq=8, hkv=8)),
+    # chunk path, four heads per KV head, a tail with few keys in the second key half
+    ("chunk_g4", dict(ctx=[300, 97, 40], ql=[40, 33, 40], hq=32, hkv=8)),
+]
+
+
+@pytest.mark.parametrize("name,case", FEW_KEY_CASES, ids=[c[0] for c in FEW_KEY_CASES])
+def test_few_key_rows_within_output_rounding(name, case):
+    p = _case(case["ctx"], ql=case["ql"], hq=case["hq"], hkv=case["hkv"], seed=67, causal=True)
+    got = run_gpu(p)
+    ref = run_oracle(p)
+    compare(p, got, ref, label=name)
+    out, _, written = ref
+    o = bf16_to_f64(got[0])
+    # keys each row sees (token t of a slot's m sees n - m + t + 1)
+    vis = np.concatenate([np.arange(int(n) - int(m) + 1, int(n) + 1) for n, m in zip(p.ctx_lens, p.q_lens)])
+    few = written & (vis < 64)
+    assert few.any()
+    err = np.abs(o[few] - out[few])
+    over = err - half_ulp_bf16(out[few])
+    say(f"  {name}: {int(few.sum())} rows with < 64 keys, max |dout| beyond half an ulp {over.max():.2e}")
+    assert over.max() <= 2.5e-4, float(over.max())
 
 
 def test_chunked_prefill_page_example_full_size():
