@@ -43,10 +43,12 @@
 //      complete under it.  The output is divided by the sum of those rounded
 //      weights, so it is an exact weighted mean of the V rows under the
 //      weights PV used (a single dominant key comes back exactly); the LSE
-//      takes the sum of the fp32 weights.  Where some row of a key half sees
-//      fewer than kFewKeys of its keys -- too few to average the rounding
-//      down -- the rounding's remainders go through a product of their own
-//      as well, and the divisor is the fp32 sum.
+//      takes the sum of the fp32 weights.  A key half in which some row
+//      sees fewer than kFewKeys of the half's keys -- too few to average the
+//      rounding down -- makes a second pass over its tiles after the loop,
+//      adding the rounding's remainders (each scaled to the row's final
+//      reference max) through a product of their own; its divisor is then
+//      the fp32 sum.
 // Keys past the end load the last key (finite) and get -inf scores.  The
 // 128 x 128 bf16 output tile is staged in LDS and stored as whole rows.
 
@@ -64,12 +66,10 @@ constexpr int kRowBytes = kHeadDim * 2;           // 256: one key row of K or V
 constexpr int kTileBytes = kTileKeys * kRowBytes; // 8 KiB (K or V)
 constexpr int kStages = 4;                        // LDS stages per key half
 constexpr float kRescaleSlack = 8.0f;             // log2 units
-// A half whose rows see few keys cannot average the rounding of bf16
-// weights down: where some live row sees between 1 and kFewKeys - 1 of the
-// half's keys, the remainders of the weights' rounding go through a second
-// PV product (twice the PV products, on the few tiles such a half has).
-constexpr int kFewKeys = 64;
 constexpr int kMergeBytes = 72 * 1024;            // merge buffer at the start of the tile area
+// Rows that see fewer than this many of a key half's keys get the second,
+// remainder pass (see above).
+constexpr int kFewKeys = 64;
 
 static_assert(kChunkRows == 4 * 32, "four row groups of 32 rows");
 
@@ -190,15 +190,20 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkParams p) {
   const int ntiles = (kv_end + kTileKeys - 1) / kTileKeys;
   const int T = (ntiles + 1) / 2;       // tiles per half (both halves loop T times)
   const int my_limit = p.causal ? (n - m + tok) : (n - 1);  // last visible key of this row
-  bool fine;  // this half's rows: some sees 1 .. kFewKeys - 1 of its keys
+  // Few keys in a half: some live row sees between 1 and kFewKeys - 1 of
+  // the half's keys (a row that sees v keys has min(max(v - base, 0), T * 32)
+  // of those of the half starting at key base).  Both halves' flags, since
+  // the remainder pass's barriers are the workgroup's.
+  bool fine, fine_any;
   {
     const int t_first = (qt * kChunkRows) / G;
     const int t_last = (min(m * G, (qt + 1) * kChunkRows) - 1) / G;
-    const int base = tile0 * kTileKeys;
-    // a row that sees v keys has min(max(v - base, 0), T * 32) of them here
     const int v_lo = p.causal ? n - m + t_first + 1 : n;
     const int v_hi = p.causal ? n - m + t_last + 1 : n;
-    fine = v_hi > base && min(max(v_lo - base, 1), T * kTileKeys) < kFewKeys;
+    auto few = [&](int base) { return v_hi > base && min(max(v_lo - base, 1), T * kTileKeys) < kFewKeys; };
+    const bool f0 = few(0), f1 = few(T * kTileKeys);
+    fine = kh == 0 ? f0 : f1;
+    fine_any = f0 || f1;
   }
   // Tiles ending at or before this key count are visible to every row of the
   // workgroup (under the causal mask: to the tile's first token).
@@ -384,31 +389,13 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkParams p) {
         rsum = bf16x2_sum_into(pf[ks][w], rsum);
       }
     }
-    // (few keys: the remainders go through a product of their own below, so
-    // the fp32 weights are what PV sums, and their sum is the divisor)
-    r_run += fine ? lsum : rsum;
+    r_run += rsum;
     // The transposed reads must have landed (the operands pass through this
     // block, so nothing reads them before it).
     asm volatile("s_waitcnt lgkmcnt(0)"
                  : "+v"(vr[0]), "+v"(vr[1]), "+v"(vr[2]), "+v"(vr[3]), "+v"(vr[4]), "+v"(vr[5]), "+v"(vr[6]),
                    "+v"(vr[7]), "+v"(vr[8]), "+v"(vr[9]), "+v"(vr[10]), "+v"(vr[11]), "+v"(vr[12]),
                    "+v"(vr[13]), "+v"(vr[14]), "+v"(vr[15]));
-    if (fine) {  // the rounding's remainders first, then the rounded weights
-      u32x4_t pl[2];
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int w = 0; w < 4; ++w) pl[ks][w] = lo_after(st[8 * ks + 2 * w], st[8 * ks + 2 * w + 1], pf[ks][w]);
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const u32x2_t l2 = vr[4 * mb + 2 * ks];
-          const u32x2_t h2 = vr[4 * mb + 2 * ks + 1];
-          const u32x4_t vf = u32x4_t{l2[0], l2[1], h2[0], h2[1]};
-          o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vf), as_bf16x8(pl[ks]), o[mb], 0, 0, 0);
-        }
-    }
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
@@ -460,6 +447,91 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkParams p) {
   // and every wave must be done computing.
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   __syncthreads();
+
+  // Remainder pass (few keys in a half): the half's tiles again, one at a
+  // time through stage 0.  The scores, the masking and the lazy reference
+  // max are recomputed exactly as above, so each tile's weights w and their
+  // bf16 roundings hi are the ones PV used; the remainders w - hi, scaled by
+  // 2^(reference at the tile - final reference) as the rescales scaled that
+  // tile's share of o, go through PV as bf16.  o then sums the fp32 weights,
+  // so the divisor becomes their fp32 sum.
+  if (fine_any) {
+    const float m_fin = m_run;
+    float m2 = -INFINITY;
+    const bool pos = p.scale_log2 > 0.f;
+    const float sc = pos ? p.scale_log2 : 1.f;
+    const int grp16 = lane >> 4;
+    const int a16 = lane & 15;
+#pragma unroll 1
+    for (int it = 0; it < T; ++it) {
+      const int t = tile0 + it;
+      issue_tile(it, 0, scalar_load_i32(bt, min(2 * t, last_page)), scalar_load_i32(bt, min(2 * t + 1, last_page)));
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+      __syncthreads();
+      if (fine) {
+        const uint8_t* sk = s_buf[kh][0][0];
+        const uint8_t* svv = s_buf[kh][0][1];
+        f32x16_t st;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) st[i] = 0.f;
+        u32x4_t kf[8];
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          const int c = hh * 8 + s;
+          kf[s] = *reinterpret_cast<const u32x4_t*>(sk + col * kRowBytes + ((c ^ key_swz(col)) << 4));
+        }
+#pragma unroll
+        for (int s = 0; s < 8; ++s)
+          st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf[s]), as_bf16x8(qf[s]), st, 0, 0, 0);
+        const int kbase = t * kTileKeys + 4 * hh;
+        if ((t + 1) * kTileKeys > open_end || !pos) {
+          if (!pos) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) st[i] *= p.scale_log2;
+          }
+#pragma unroll
+          for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+              if (kbase + 8 * a + b > my_limit) st[4 * a + b] = -INFINITY;
+        }
+        float mloc = st[0];
+#pragma unroll
+        for (int i = 1; i < 16; ++i) mloc = fmaxf(mloc, st[i]);
+        mloc *= sc;
+        mloc = fmaxf(mloc, other_half(mloc));
+        if (__builtin_amdgcn_ballot_w64(mloc > m2 + kRescaleSlack) != 0) m2 = fmaxf(m2, mloc);
+        const float m_use = (m2 == -INFINITY) ? 0.f : m2;
+        const float to_fin = m_fin == -INFINITY ? 0.f : fast_exp2(m_use - m_fin);
+        u32x4_t pl[2];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            const float w0 = fast_exp2(fmaf(st[8 * ks + 2 * w], sc, -m_use));
+            const float w1 = fast_exp2(fmaf(st[8 * ks + 2 * w + 1], sc, -m_use));
+            const uint32_t hi = pack_bf16x2(w0, w1);
+            pl[ks][w] = pack_bf16x2((w0 - bf16_lo(hi)) * to_fin, (w1 - bf16_hi(hi)) * to_fin);
+          }
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) {
+            s16x4_t v2[2];
+#pragma unroll
+            for (int e = 0; e < 2; ++e)
+              v2[e] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(
+                  svv + ks * 4096 + swz(8 * e + 4 * hh + (a16 >> 2), mb * 32 + (grp16 & 1) * 16 + 4 * (a16 & 3))));
+            const u32x2_t l2 = __builtin_bit_cast(u32x2_t, v2[0]);
+            const u32x2_t h2 = __builtin_bit_cast(u32x2_t, v2[1]);
+            const u32x4_t vf = u32x4_t{l2[0], l2[1], h2[0], h2[1]};
+            o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vf), as_bf16x8(pl[ks]), o[mb], 0, 0, 0);
+          }
+      }
+      __syncthreads();  // stage 0 is loaded again next
+    }
+    if (fine) r_run = l_run;
+  }
 
   // Merge the key halves through LDS (the tile area) behind one barrier:
   // wave (rg, kh) keeps output blocks 2 kh, 2 kh + 1 (dims 64 kh .. +64) of

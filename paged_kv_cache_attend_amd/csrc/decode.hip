@@ -389,14 +389,16 @@ __device__ __forceinline__ void score_page(WaveState<Cols<G, M>::NT>& st, const 
       } else {
         const uint32_t w01 = pack_bf16x2(pw[0], pw[1]);
         const uint32_t w23 = pack_bf16x2(pw[2], pw[3]);
-        // (few keys, see kFewKeys: the rounding's remainders go through a
-        // product of their own below, so the fp32 sum is the divisor)
-        st.r_lane[ct] += fine ? (pw[0] + pw[1]) + (pw[2] + pw[3])
-                              : (bf16_lo(w01) + bf16_hi(w01)) + (bf16_lo(w23) + bf16_hi(w23));
+        st.r_lane[ct] += (bf16_lo(w01) + bf16_hi(w01)) + (bf16_lo(w23) + bf16_hi(w23));
         pg = as_s16x4(w01, w23);
       }
-      if (!CS::HL && fine) {  // the rounding's remainders first, then the rounded weights
+      if (!CS::HL && __builtin_expect(fine, 0)) {
+        // Few keys (see kFewKeys): the rounding's remainders go through a
+        // product of their own, so PV sums the fp32 weights, and their sum
+        // is the divisor.
         const uint32_t hi01 = __builtin_bit_cast(u32x2_t, pg)[0], hi23 = __builtin_bit_cast(u32x2_t, pg)[1];
+        st.r_lane[ct] += ((pw[0] + pw[1]) + (pw[2] + pw[3])) -
+                         ((bf16_lo(hi01) + bf16_hi(hi01)) + (bf16_lo(hi23) + bf16_hi(hi23)));
         const s16x4_t pl = as_s16x4(lo_after(pw[0], pw[1], hi01), lo_after(pw[2], pw[3], hi23));
 #pragma unroll
         for (int bb = 0; bb < 8; ++bb)
