@@ -38,9 +38,17 @@ COMMON = [
 ]
 
 
+# Per-source device options.  The decode kernel's leading scalar arguments
+# (the fields its start needs) are preloaded into scalar registers at wave
+# launch, so its first memory requests do not wait for the argument block.
+EXTRA = {
+    "decode.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=10"],
+}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *COMMON, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *COMMON, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd.insert(1, "-xhip")
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -708,7 +708,12 @@ __device__ __forceinline__ void prefix_item(const DecodeParams& p, int pi, int l
 // pre_items workgroups are prefix items (one token per slot).
 template <int G, int F, int M, bool kPre = false>
 __global__ __launch_bounds__(kDecodeThreads, (Cols<G, M>::NT > 1 ? 1 : PA_DECODE_MIN_WGS)) void decode_kernel(
-    DecodeParams p) {
+    const int32_t* block_table, const int32_t* q_lens, const int32_t* ctx_lens, const int32_t* slot_plen,
+    int num_seqs, int num_parts, int part_pages, int max_blocks, int pre_items, int grid, DecodeParams p) {
+  // The leading arguments repeat the fields of p that the start needs before
+  // its first memory request; they arrive preloaded in scalar registers
+  // (kernel-argument preloading), so the page-id requests need not wait for
+  // a load of the argument block.
   static_assert(G == 1 || G == 2 || G == 4 || G == 8, "group size");
   using CS = Cols<G, M>;
   constexpr int C = CS::C;
@@ -729,8 +734,8 @@ __global__ __launch_bounds__(kDecodeThreads, (Cols<G, M>::NT > 1 ? 1 : PA_DECODE
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   // The kernel arguments the start needs, fetched together (the compiler
   // would otherwise fetch some of them one round trip later).
-  asm volatile("" ::"s"(p.q_lens), "s"(p.ctx_lens), "s"(p.block_table), "s"(p.slot_plen), "s"(p.pre_parts), "s"(p.num_parts),
-               "s"(p.pre_items), "s"(p.num_seqs), "s"(p.part_pages), "s"(p.max_blocks), "s"(gridDim.x));
+  asm volatile("" ::"s"(q_lens), "s"(ctx_lens), "s"(block_table), "s"(slot_plen), "s"(num_parts),
+               "s"(pre_items), "s"(num_seqs), "s"(part_pages), "s"(max_blocks), "s"(grid));
   if constexpr (kPre)
     asm volatile("" ::"s"(p.num_groups), "s"(p.group_start), "s"(p.max_members), "s"(p.guess_plen), "s"(p.prefix_len));
 
@@ -738,7 +743,7 @@ __global__ __launch_bounds__(kDecodeThreads, (Cols<G, M>::NT > 1 ? 1 : PA_DECODE
   // prefix items (dispatched first); the rest are the slots' partitions.
   if constexpr (kPre) {
     static_assert(F == kFmtBF16 && M == 1, "prefix items: bf16 pages, one token per slot");
-    if ((int)blockIdx.x < p.pre_items) {
+    if ((int)blockIdx.x < pre_items) {
       constexpr int PM = prefix_chunk_members(G);
       constexpr int PC = Cols<G, PM>::C;
       __shared__ __attribute__((aligned(16))) float s_pacc[kWaves][PC][kHeadDim];
@@ -746,17 +751,17 @@ __global__ __launch_bounds__(kDecodeThreads, (Cols<G, M>::NT > 1 ? 1 : PA_DECODE
       __shared__ float s_pl[kWaves][PC];
       __shared__ float s_pr[kWaves][PC];
       __shared__ int s_lastm[kWaves * PM];
-      prefix_item<G, F, PM>(p, xcd_remap(blockIdx.x, p.pre_items), lane, wave, s_k, s_v, s_pacc, s_pm, s_pl, s_pr,
+      prefix_item<G, F, PM>(p, xcd_remap(blockIdx.x, pre_items), lane, wave, s_k, s_v, s_pacc, s_pm, s_pl, s_pr,
                             s_lastm);
       return;
     }
   }
-  const int wg = xcd_remap(blockIdx.x - p.pre_items, gridDim.x - p.pre_items);
-  const int P = p.num_parts;
+  const int wg = xcd_remap(blockIdx.x - pre_items, grid - pre_items);
+  const int P = num_parts;
   const int part = wg % P;
   const int rest = wg / P;
-  const int seq = rest % p.num_seqs;
-  const int g = rest / p.num_seqs;
+  const int seq = rest % num_seqs;
+  const int g = rest / num_seqs;
 
   // Everything the start needs comes in one round trip, issued before the
   // first branch: the lengths, the prefix length, the slot's row offset (a
@@ -765,15 +770,15 @@ __global__ __launch_bounds__(kDecodeThreads, (Cols<G, M>::NT > 1 ? 1 : PA_DECODE
   // prefix is guess_plen keys; checked below, reloaded otherwise).  Lengths
   // and page ids are wave-uniform scalar loads, which do not share the
   // (in-order) vector load counter with the page stream.
-  const int32_t* bt = p.block_table + (size_t)seq * p.max_blocks;
+  const int32_t* bt = block_table + (size_t)seq * max_blocks;
   const int guess = kPre ? p.guess_plen : 0;
-  const int spage0 = guess / kBlockSize + part * p.part_pages + wave;  // first page for that guess
-  const int m = scalar_load_i32(p.q_lens, seq);
-  const int n = scalar_load_i32(p.ctx_lens, seq);
+  const int spage0 = guess / kBlockSize + part * part_pages + wave;  // first page for that guess
+  const int m = scalar_load_i32(q_lens, seq);
+  const int n = scalar_load_i32(ctx_lens, seq);
   // Prefix-grouped decode: this slot's keys start after its shared prefix,
   // whose partials the prefix pass has written; the last partition runs to
   // the slot's end whatever the prefix length.
-  int plen = p.slot_plen ? scalar_load_i32(p.slot_plen, seq) : 0;
+  int plen = slot_plen ? scalar_load_i32(slot_plen, seq) : 0;
   // (One launch with fewer than 64 groups: the slot's group is the last one
   // starting at or before it, found by the lanes among group_start, and its
   // prefix length is that group's lane of prefix_len.)
@@ -784,9 +789,9 @@ __global__ __launch_bounds__(kDecodeThreads, (Cols<G, M>::NT > 1 ? 1 : PA_DECODE
   }
   int32_t sid[kRing + 1];
 #pragma unroll
-  for (int k = 0; k <= kRing; ++k) sid[k] = scalar_load_i32(bt, min(spage0 + k * kWaves, p.max_blocks - 1));
+  for (int k = 0; k <= kRing; ++k) sid[k] = scalar_load_i32(bt, min(spage0 + k * kWaves, max_blocks - 1));
   int qsum = 0;  // this lane's share of the row offset
-  for (int i = lane; i < seq; i += 64) qsum += p.q_lens[i];
+  for (int i = lane; i < seq; i += 64) qsum += q_lens[i];
   // (Keeps the loads above the branch: the compiler would otherwise sink the
   // ones only the working path uses below it, one round trip later.  The
   // wave sum of the row offset waits until the first page is requested.)
@@ -808,11 +813,11 @@ __global__ __launch_bounds__(kDecodeThreads, (Cols<G, M>::NT > 1 ? 1 : PA_DECODE
   // partition, and a slot with one such partition writes its result itself.
   // (A prefix pass's partials from the launch before still need a merger:
   // partition 0, even without keys of its own.)
-  const int ps = partitions_with_keys(npages - plen / kBlockSize, P, p.part_pages);
-  const int Ps = (npre > 0 && p.pre_items == 0) ? max(ps, 1) : ps;
+  const int ps = partitions_with_keys(npages - plen / kBlockSize, P, part_pages);
+  const int Ps = (npre > 0 && pre_items == 0) ? max(ps, 1) : ps;
   if (part >= Ps) return;
-  const int pstart = plen / kBlockSize + part * p.part_pages;
-  const int pend = part == P - 1 ? npages : min(npages, pstart + p.part_pages);
+  const int pstart = plen / kBlockSize + part * part_pages;
+  const int pend = part == P - 1 ? npages : min(npages, pstart + part_pages);
   const bool has_work = n > 0 && pstart < pend;
   // Few keys: some live row sees between 1 and kFewKeys - 1 of this
   // partition's keys (token t of m sees keys up to n - m + t when causal; a
@@ -1029,7 +1034,7 @@ __global__ __launch_bounds__(kDecodeThreads, (Cols<G, M>::NT > 1 ? 1 : PA_DECODE
     return (size_t)(q_row + my_c[j] / G) * p.num_q_heads + h0 + my_c[j] % G;
   };
 
-  if (Ps == 1 && (p.pre_items == 0 || npre == 0)) {
+  if (Ps == 1 && (pre_items == 0 || npre == 0)) {
 #pragma unroll
     for (int j = 0; j < J; ++j) {
       if (!my_out[j]) continue;
@@ -1090,7 +1095,7 @@ __global__ __launch_bounds__(kDecodeThreads, (Cols<G, M>::NT > 1 ? 1 : PA_DECODE
   int32_t* counter = p.counters + (size_t)seq * p.num_kv_heads + g;
   if (threadIdx.x == 0)
     s_last = (__hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-              Ps - 1 + (p.pre_items > 0 ? npre : 0));
+              Ps - 1 + (pre_items > 0 ? npre : 0));
   __syncthreads();
   if (!s_last) return;
 
@@ -1145,6 +1150,16 @@ const void* decode_entry(int group) {
   return nullptr;
 }
 
+// The kernel's leading scalar arguments, then the whole parameter block.
+static hipError_t launch_decode_fn(const void* fn, const DecodeParams& p, unsigned grid, hipStream_t s) {
+  DecodeParams arg = p;
+  const int32_t *bt = p.block_table, *ql = p.q_lens, *cl = p.ctx_lens, *sp = p.slot_plen;
+  int ns = p.num_seqs, np = p.num_parts, pp = p.part_pages, mb = p.max_blocks, pi = p.pre_items;
+  int gr = (int)grid;
+  void* args[] = {&bt, &ql, &cl, &sp, &ns, &np, &pp, &mb, &pi, &gr, &arg};
+  return hipLaunchKernel(fn, dim3(grid), dim3(kDecodeThreads), args, 0, s);
+}
+
 hipError_t launch_decode(const DecodeParams& p, int group, int format, int tokens, unsigned grid, hipStream_t s) {
   const void* fn = nullptr;
   if (tokens == 1) {
@@ -1162,9 +1177,7 @@ hipError_t launch_decode(const DecodeParams& p, int group, int format, int token
     }
   }
   if (!fn) return hipErrorInvalidValue;
-  DecodeParams arg = p;
-  void* args[] = {&arg};
-  return hipLaunchKernel(fn, dim3(grid), dim3(kDecodeThreads), args, 0, s);
+  return launch_decode_fn(fn, p, grid, s);
 }
 
 hipError_t launch_decode_prefix(const DecodeParams& p, int group, unsigned grid, hipStream_t s) {
@@ -1175,9 +1188,7 @@ hipError_t launch_decode_prefix(const DecodeParams& p, int group, unsigned grid,
     case 4: fn = reinterpret_cast<const void*>(&decode_kernel<4, kFmtBF16, 1, true>); break;
   }
   if (!fn) return hipErrorInvalidValue;
-  DecodeParams arg = p;
-  void* args[] = {&arg};
-  return hipLaunchKernel(fn, dim3(grid), dim3(kDecodeThreads), args, 0, s);
+  return launch_decode_fn(fn, p, grid, s);
 }
 
 hipError_t launch_zero_i32(int32_t* x, size_t n, hipStream_t s) {
