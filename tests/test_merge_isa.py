@@ -37,8 +37,9 @@ def decode_asm(tmp_path_factory):
     if not os.path.exists(B.HIPCC) and shutil.which("hipcc") is None:
         pytest.skip("hipcc not available")
     out = tmp_path_factory.mktemp("isa") / "decode.s"
-    cmd = [B.HIPCC, *[a for a in B.COMMON if a != "-fPIC"], "--cuda-device-only", "-S",
-           os.path.join(B.CSRC, "decode.hip"), "-o", str(out)]
+    # the same options as the shipped object (argument preloading included)
+    cmd = [B.HIPCC, *[a for a in B.COMMON if a != "-fPIC"], *B.EXTRA.get("decode.hip", []),
+           "--cuda-device-only", "-S", os.path.join(B.CSRC, "decode.hip"), "-o", str(out)]
     r = subprocess.run(cmd, capture_output=True, text=True)
     assert r.returncode == 0, r.stderr[-2000:]
     return out.read_text()
